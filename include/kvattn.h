@@ -1,0 +1,262 @@
+/*
+ * kvattn.h -- C ABI of a paged-KV decode-attention library for AMD MI355X (gfx950).
+ *
+ * Sources this interface follows (cited below by the tag in brackets):
+ *   [InplaceKVCache] "Physically Partitioned KVCache Format for CPU-GPU Load Balancing in
+ *                    MoE Inference" (Yu, Dong, Liao)
+ *   [CrossPool]      "CrossPool: Efficient Multi-LLM Serving for Cold MoE Models through
+ *                    KV-Cache and Weight Disaggregation"
+ *   [VAMP]           "Dynamic HBM Repartitioning for Multi-Turn MoE Serving"
+ *
+ * What it computes.  One decode step of exact attention for one new query token per
+ * sequence, o = softmax(scale * q K^T) V, over a KV cache held in fixed-size blocks
+ * ([InplaceKVCache] §4.1: every region is organised in fixed-size blocks; [CrossPool] §3.1:
+ * kernels address a logical KV space through a paged interface while physical pages are
+ * placed elsewhere).  A per-sequence block table maps logical block i to a physical block
+ * id; physical ids index the union of several caller-owned device regions, e.g. the base KV
+ * region plus HBM reclaimed from expert weights ([VAMP] §IV-C, §V-A: reclaimed pages join
+ * the free-block pool).  Each sequence's token range is cut into partitions that each emit a
+ * partial (o, lse) pair; an exact log-sum-exp merge folds them together, optionally with one
+ * more partial computed elsewhere, e.g. a CPU share of the context ([InplaceKVCache] §4.2
+ * and §5.1: the two engines cover disjoint sequence ranges over all heads and their partial
+ * outputs merge exactly by LSE rescaling, one join per step, on the GPU).
+ *
+ * Conventions shared by every call:
+ *   - Every function returns kvattn_status (0 = OK, < 0 = error) unless stated otherwise;
+ *     kvattn_last_error() returns a message for the last failure on the calling thread.
+ *   - "host" pointers are ordinary CPU memory read synchronously; "device" pointers are
+ *     HIP device memory owned by the caller.  The library never allocates device memory.
+ *   - Device work is enqueued asynchronously on the caller's HIP stream (hipStream_t passed
+ *     as void*; NULL = the null stream).  Argument validation is synchronous: a call that
+ *     returns an error has enqueued nothing.  Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - lse is the natural logarithm of the sum of exp(scaled score) over the partial's tokens.
+ *     An empty partial has lse = -INFINITY and o = 0 and carries no weight in a merge.
+ *
+ * KV block layout in a region (element type e = 4 bytes for F32, 2 for BF16; x = 16 / e
+ * elements per 16-byte chunk; bs = block_size; Hkv = num_kv_heads; Dk, Dv head dims):
+ *   GQA (latent = 0):  block = [ K part | V part ], Hkv * bs * (Dk + Dv) elements.
+ *       K(h, t, i) at element  ((h * (Dk / x) + i / x) * bs + t) * x + i % x
+ *       V(h, t, j) at element  Hkv * bs * Dk + (h * Dv + j) * bs + t
+ *     i.e. K is stored in 16-byte chunks of one token, the chunks of bs consecutive tokens
+ *     side by side; V is stored transposed (token index fastest).
+ *   MLA (latent = 1):  block = bs * Dk elements, Hkv must be 1, Dv <= Dk, Dv % x == 0.
+ *       C(t, i) at element  ((i / x) * bs + t) * x + i % x     (K(t, i) = C(t, i),
+ *       V(t, j) = C(t, j) for j < Dv: the value is the leading Dv columns of the latent).
+ *   Block id n of region r (regions numbered in the order passed to kvattn_pool_alloc, ids
+ *   consecutive across regions) starts at byte (n - first_id(r)) * block_bytes of region r.
+ *   The layout is this library's choice: the pages fix only that blocks have a fixed size.
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvattn_status;
+
+enum {
+  KVATTN_OK = 0,
+  KVATTN_E_INVAL = -1,          /* bad argument: null pointer, size, alignment, inconsistency */
+  KVATTN_E_POOL_EXHAUSTED = -2, /* not enough free blocks; pool and outputs left unchanged */
+  KVATTN_E_RANGE = -3,          /* a block id outside [0, pool blocks) */
+  KVATTN_E_STATE = -4,          /* block in the wrong state: claim of a used block, double release */
+  KVATTN_E_UNSUPPORTED = -5,    /* shape / dtype combination without a kernel */
+  KVATTN_E_HIP = -6             /* HIP runtime error while enqueueing */
+};
+
+enum { KVATTN_F32 = 0, KVATTN_BF16 = 1 };
+
+#define KVATTN_BLOCK_ABSENT (-1) /* table entry with no block on this device */
+#define KVATTN_MAX_REGIONS 8
+
+/* Error bits a decode kernel may set in *err_dev (see kvattn_decode_partial). */
+#define KVATTN_ERR_BAD_BLOCK 1   /* a table entry inside a sequence's range is not a valid id */
+#define KVATTN_ERR_BAD_SEQ 2     /* device per-sequence values disagree with the host ones */
+
+typedef struct {
+  int32_t block_size;   /* tokens per block bs; power of two in [1, 256] */
+  int32_t num_kv_heads; /* Hkv; 1 for a latent cache */
+  int32_t head_dim_k;   /* Dk: key (latent) dimension; multiple of x */
+  int32_t head_dim_v;   /* Dv: value dimension; multiple of x */
+  int32_t kv_dtype;     /* KVATTN_F32 or KVATTN_BF16 */
+  int32_t latent;       /* 0 = per-head K and V (GQA); 1 = shared latent (MLA) */
+} kvattn_layout;
+
+typedef struct {
+  void* base;         /* device address of the region, 16-byte aligned; caller-owned */
+  int64_t num_blocks; /* number of whole blocks the region holds */
+} kvattn_region;
+
+typedef struct kvattn_pool kvattn_pool; /* opaque host metadata: regions, free list, refcounts */
+
+/* Bytes of one block under `layout`, or -1 if the layout is invalid. */
+int64_t kvattn_block_bytes(const kvattn_layout* layout);
+
+/*
+ * Create a block pool over 1..KVATTN_MAX_REGIONS caller-owned device regions
+ * ([VAMP] §IV-C and §V-A: HBM reclaimed from expert weights is inserted into the free-block
+ * pool beside the base KV region; [InplaceKVCache] §4.1: fixed-size blocks are the unit).
+ * Block ids are consecutive over the regions in the order given.  The free list starts as
+ * a Fisher-Yates shuffle of all ids driven by SplitMix64 seeded with `seed`: with
+ * state = seed, for i = N-1 down to 1: j = splitmix64_next(&state) % (i + 1), swap(ids[i],
+ * ids[j]); blocks are then handed out in the order ids[0], ids[1], ...  (A released block
+ * is handed out before any block never used: the free list is a stack.)
+ * `out` receives a pool the caller frees with kvattn_pool_free.  Only host memory is used.
+ * Errors: E_INVAL (null pointers, bad layout, zero regions, misaligned or null base,
+ * a region with num_blocks < 0, more than 2^31-1 blocks in total).
+ */
+kvattn_status kvattn_pool_alloc(const kvattn_layout* layout, const kvattn_region* regions,
+                                int32_t n_regions, uint64_t seed, kvattn_pool** out);
+
+/* Release the pool's host metadata; the regions stay the caller's.  NULL is ignored. */
+void kvattn_pool_free(kvattn_pool* pool);
+
+/*
+ * Fill a block table for `batch` sequences ([CrossPool] §3.1: the virtualiser, not the
+ * kernel, chooses physical pages; when the page budget runs out the request is queued or
+ * rejected and running decodes are left alone).  All host memory.  Row b of table_out
+ * (max_blocks entries) maps logical block i of sequence b to a physical id, or to
+ * KVATTN_BLOCK_ABSENT.  Sequence b needs nb = ceil(ctx_lens[b] / bs) entries; entries
+ * from nb on are ABSENT.  Two modes:
+ *
+ * Allocate (explicit_table == NULL), sequences processed in order b = 0, 1, ...:
+ *   - entries i < first_tok[b] / bs (integer division) are ABSENT: the tokens before
+ *     first_tok[b] live elsewhere (e.g. the CPU share); NULL means 0 for every sequence.
+ *   - if share_src != NULL and share_src[b] >= 0, entries i < share_nblocks[b] are copied
+ *     from row share_src[b] (which must be < b, resident there, and i < nb of both rows)
+ *     and each shared block's reference count rises by one (prefix sharing);
+ *     a sequence cannot both share and have ABSENT entries.
+ *   - every remaining entry below nb takes the next block of the free list, refcount 1.
+ *   All or nothing: if the free list is short, returns E_POOL_EXHAUSTED, writes the
+ *   number of missing blocks to *shortfall_out (if non-NULL) and changes nothing.
+ *
+ * Explicit (explicit_table != NULL, [batch][max_blocks]): the caller chose the ids.  Each
+ *   entry must be ABSENT or an id in range (else E_RANGE); entries from nb on must be
+ *   ABSENT (else E_INVAL); every referenced id must be free (else E_STATE).  A block named
+ *   k times gets refcount k and leaves the free list; table_out receives a copy.
+ *
+ * first_tok, share_src and share_nblocks are ignored in explicit mode.
+ * Errors: E_INVAL, E_RANGE, E_STATE, E_POOL_EXHAUSTED, each leaving the pool unchanged.
+ */
+kvattn_status kvattn_block_table(kvattn_pool* pool, int32_t batch, const int32_t* ctx_lens,
+                                 const int32_t* first_tok, const int32_t* share_src,
+                                 const int32_t* share_nblocks, const int32_t* explicit_table,
+                                 int32_t max_blocks, int32_t* table_out, int64_t* shortfall_out);
+
+/*
+ * Drop one reference for every non-ABSENT entry of a [batch][max_blocks] host table; a
+ * block whose count reaches zero returns to the top of the free list (in table order).
+ * All or nothing: E_RANGE for an id out of range, E_STATE if some block would drop below
+ * zero references (e.g. a second release of the same table); then nothing changes.
+ */
+kvattn_status kvattn_block_release(kvattn_pool* pool, const int32_t* table, int32_t batch,
+                                   int32_t max_blocks);
+
+/* Free blocks left in the pool, or -1 for NULL. */
+int64_t kvattn_pool_num_free(const kvattn_pool* pool);
+
+/* Reference count of block `id`, or -1 if out of range. */
+int32_t kvattn_pool_refcount(const kvattn_pool* pool, int32_t id);
+
+/*
+ * Number of partitions of a sequence whose device-resident range is [tok_begin, ctx_len),
+ * cut into pieces of part_tokens tokens: ceil((ctx_len - tok_begin) / part_tokens), and 0
+ * for an empty range.  Partition p covers [tok_begin + p * part_tokens,
+ * min(ctx_len, tok_begin + (p + 1) * part_tokens)).  Returns -1 for invalid arguments
+ * (negative values, tok_begin > ctx_len, part_tokens <= 0).  ([InplaceKVCache] §5.1: the
+ * split is along the sequence, each engine over all heads.)
+ */
+int32_t kvattn_partition_count(int32_t ctx_len, int32_t tok_begin, int32_t part_tokens);
+
+/*
+ * One decode step's partial attention ([InplaceKVCache] §5.1 and §6.1: exact attention,
+ * online softmax with a running max and normaliser, fp32 accumulation; sequence-dimension
+ * split).  For every sequence b, KV head group and partition p of [tok_begin[b],
+ * ctx_lens[b]) (geometry as in kvattn_partition_count with part_tokens[b]) it writes
+ *     o_part[b][h][p][:] = sum_t w_t V(t) / sum_t w_t,  w_t = exp(s_t - max s),
+ *     s_t = scale * q[b][h] . K(t),      lse_part[b][h][p] = max s + ln(sum_t w_t)
+ * over the partition's tokens t, for every query head h, with KV head h / (Hq / Hkv)
+ * (consecutive query heads share a KV head; MLA: all heads share the latent).  Logical
+ * token t of sequence b lives at offset t % bs of physical block table_dev[b][t / bs].
+ *
+ *   q            device [batch][num_q_heads][Dk], element type q_dtype (must equal kv_dtype)
+ *   table_dev    device [batch][max_blocks] int32 (entries of the range must be valid ids)
+ *   ctx_lens, tok_begin (NULL = 0), part_tokens: host [batch] int32 used for validation and
+ *                grid sizing; seq_dev: device int32 [3][batch] holding the same three arrays
+ *                (row 1 all zeros if tok_begin is NULL), read by the kernels.
+ *   max_parts    partitions per sequence the o_part / lse_part arrays have room for
+ *   o_part       device fp32 [batch][num_q_heads][max_parts][Dv]
+ *   lse_part     device fp32 [batch][num_q_heads][max_parts]
+ *   nparts_dev   device int32 [batch]: receives the partition count of each sequence
+ *   err_dev      device int32 or NULL: KVATTN_ERR_* bits are OR-ed in (never cleared) if a
+ *                kernel meets an invalid block id or device lengths that disagree with the
+ *                host ones; the offending block contributes nothing / the sequence gets no
+ *                partitions, and no memory outside the arguments is touched.
+ * Entries of o_part / lse_part for p >= nparts[b] are not written.
+ * Validation (E_INVAL): null pointers, batch < 1, num_q_heads % Hkv != 0, per sequence
+ * 0 <= tok_begin <= ctx_len <= max_blocks * bs, part_tokens > 0 and part_tokens % bs == 0,
+ * partition count <= max_parts.  E_UNSUPPORTED: q_dtype != kv_dtype, or a head / dim
+ * combination without a kernel (GQA: Dk = Dv in {64, 128, 256}, Hq / Hkv <= 16;
+ * MLA: BF16, Dk = 576, Dv = 512, Hq <= 16, bs = 64).  E_HIP: launch failure.
+ */
+kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int32_t q_dtype,
+                                    int32_t batch, int32_t num_q_heads, float scale,
+                                    const int32_t* table_dev, int32_t max_blocks,
+                                    const int32_t* ctx_lens, const int32_t* tok_begin,
+                                    const int32_t* part_tokens, const int32_t* seq_dev,
+                                    int32_t max_parts, float* o_part, float* lse_part,
+                                    int32_t* nparts_dev, int32_t* err_dev, void* hip_stream);
+
+/*
+ * Exact LSE merge of each (sequence, head)'s partials ([InplaceKVCache] §4.2, §5.1, §5.2:
+ * the partial outputs and their normalisers are folded on the GPU, one join per step):
+ *     M = max_p lse_p,  lse = M + ln sum_p exp(lse_p - M),  o = sum_p exp(lse_p - lse) o_p
+ * over p < nparts_dev[b], plus, when o_ext != NULL, one external partial (o_ext[b][h],
+ * lse_ext[b][h]) computed elsewhere (e.g. the CPU share of the context).  With no partial
+ * of positive weight the result is o = 0, lse = -INFINITY.
+ *   o_part, lse_part, nparts_dev  as written by kvattn_decode_partial (device)
+ *   o_ext, lse_ext   device fp32 [batch][num_q_heads][dv] and [batch][num_q_heads], or both
+ *                    NULL
+ *   o_out            device fp32 [batch][num_q_heads][dv]
+ *   lse_out          device fp32 [batch][num_q_heads] or NULL
+ * Errors: E_INVAL (null required pointers, one of o_ext/lse_ext NULL but not the other,
+ * batch/heads/max_parts < 1, dv not in [1, 1024] or not a multiple of 4 is E_UNSUPPORTED),
+ * E_HIP.  The output may not alias the inputs.
+ */
+kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,
+                               const int32_t* nparts_dev, int32_t batch, int32_t num_q_heads,
+                               int32_t max_parts, int32_t dv, const float* o_ext,
+                               const float* lse_ext, float* o_out, float* lse_out,
+                               void* hip_stream);
+
+/*
+ * Address-resolution probe (for tests): runs the same device resolution code as the decode
+ * kernels ([CrossPool] §3.1: logical KV address -> physical page) and writes, for every
+ * sequence b and token t < ctx_lens[b] with a resident block, the region index and the byte
+ * offset (within that region) of element K(h = 0, t, 0) -- or C(t, 0) for MLA -- and -1 / -1
+ * for t >= ctx_lens[b] or an ABSENT or invalid entry.
+ *   table_dev  device [batch][max_blocks]; ctx_lens_dev device [batch]
+ *   region_out device int32 [batch][max_tokens]; offset_out device int64 [batch][max_tokens]
+ * Errors: E_INVAL (null pointers, max_tokens > max_blocks * bs), E_HIP.
+ */
+kvattn_status kvattn_resolve_offsets(const kvattn_pool* pool, const int32_t* table_dev,
+                                     int32_t batch, int32_t max_blocks,
+                                     const int32_t* ctx_lens_dev, int32_t max_tokens,
+                                     int32_t* region_out, int64_t* offset_out, void* hip_stream);
+
+/* Message of the last error on the calling thread ("" if none).  Never NULL. */
+const char* kvattn_last_error(void);
+
+/* Library version string.  Never NULL. */
+const char* kvattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVATTN_H */

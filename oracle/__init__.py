@@ -1,0 +1,49 @@
+"""Reference oracle for paged-KV decode attention with split-sequence LSE merge.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, float64 CPU definition that
+the HIP path is checked against.  Only the test suite, the smoke check in
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import it; the
+product path (``paged_kv_cache_mla_amd``) never does, and this package imports nothing
+from it.  The two share no code: the oracle re-derives the block layout, the address
+resolution, the attention and the merge from their definitions.
+
+Sources (cited by tag):
+  [InplaceKVCache] "Physically Partitioned KVCache Format for CPU-GPU Load Balancing in MoE
+                   Inference" -- §4.1 block-organised regions, §4.2 the CPU returns only its
+                   partial output and normalisers and the GPU merges, §5.1 sequence-dimension
+                   split with exact LSE merge, §6.1 exact attention with online softmax.
+  [CrossPool]      "CrossPool: Efficient Multi-LLM Serving for Cold MoE Models through
+                   KV-Cache and Weight Disaggregation" -- §3.1 paged KV interface over a
+                   logical KV address space.
+  [VAMP]           "Dynamic HBM Repartitioning for Multi-Turn MoE Serving" -- §IV-C, §V-A
+                   reclaimed pages joining the free-block pool.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
+invariants, brute force at 50 digits, a library special case) or, for the allocator model,
+by ``tests/test_alloc_oracle.py`` (published SplitMix64 outputs, exhaustive permutation
+counts).  None is "parity unpinned".
+"""
+
+from .bf16 import bf16_bits_to_f64
+from .layout import Layout, block_elems, gather_sequence, token_k_offset
+from .attention import attend, merge, partial_over_range
+from .partition import partition_count, partition_ranges
+from .decode import decode_reference, decode_partials_reference, resolve_offsets_reference
+from . import alloc
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "Layout",
+    "block_elems",
+    "gather_sequence",
+    "token_k_offset",
+    "attend",
+    "merge",
+    "partial_over_range",
+    "partition_count",
+    "partition_ranges",
+    "decode_reference",
+    "decode_partials_reference",
+    "resolve_offsets_reference",
+    "alloc",
+]
