@@ -1,0 +1,12 @@
+"""Paged-KV decode attention with split-sequence LSE merge for AMD MI355X (gfx950).
+
+The compute path is the C-ABI library ``libkvattn.so`` (hand-written HIP kernels, see
+``include/kvattn.h``); this package is its thin Python binding.  Importing the package
+loads nothing; the first call loads the library and raises if it has not been built.
+"""
+
+from .api import (BF16, F32, DecodeStep, KvattnError, Pool, block_bytes, decode_partial,
+                  merge_lse, partition_count, resolve_offsets)
+
+__all__ = ["BF16", "F32", "DecodeStep", "KvattnError", "Pool", "block_bytes", "decode_partial",
+           "merge_lse", "partition_count", "resolve_offsets"]

@@ -1,0 +1,96 @@
+"""ctypes loader for libkvattn.so (the C ABI declared in include/kvattn.h).
+
+Loading needs no GPU; it fails loudly if the library has not been built.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvattn.so")
+
+OK = 0
+E_INVAL = -1
+E_POOL_EXHAUSTED = -2
+E_RANGE = -3
+E_STATE = -4
+E_UNSUPPORTED = -5
+E_HIP = -6
+F32 = 0
+BF16 = 1
+BLOCK_ABSENT = -1
+MAX_REGIONS = 8
+ERR_BAD_BLOCK = 1
+ERR_BAD_SEQ = 2
+
+STATUS_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_POOL_EXHAUSTED: "E_POOL_EXHAUSTED",
+                E_RANGE: "E_RANGE", E_STATE: "E_STATE", E_UNSUPPORTED: "E_UNSUPPORTED",
+                E_HIP: "E_HIP"}
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("latent", ctypes.c_int32)]
+
+
+class Region(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("num_blocks", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "kvattn_block_bytes": (_I64, [ctypes.POINTER(Layout)]),
+    "kvattn_pool_alloc": (_I32, [ctypes.POINTER(Layout), ctypes.POINTER(Region), _I32,
+                                 ctypes.c_uint64, ctypes.POINTER(_P)]),
+    "kvattn_pool_free": (None, [_P]),
+    "kvattn_block_table": (_I32, [_P, _I32, _PI32, _PI32, _PI32, _PI32, _PI32, _I32, _PI32, _PI64]),
+    "kvattn_block_release": (_I32, [_P, _PI32, _I32, _I32]),
+    "kvattn_pool_num_free": (_I64, [_P]),
+    "kvattn_pool_refcount": (_I32, [_P, _I32]),
+    "kvattn_partition_count": (_I32, [_I32, _I32, _I32]),
+    "kvattn_decode_partial": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32,
+                                     _PI32, _PI32, _PI32, _P, _I32, _P, _P, _P, _P, _P]),
+    "kvattn_merge_lse": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "kvattn_resolve_offsets": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
+    "kvattn_last_error": (ctypes.c_char_p, []),
+    "kvattn_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load():
+    """Load libkvattn.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_mla_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class KvattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.kvattn_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def check(status: int, where: str):
+    if status != OK:
+        raise KvattnError(status, where)

@@ -1,0 +1,202 @@
+"""Thin Python binding over the kvattn C ABI.
+
+Only argument marshalling lives here: torch supplies device memory and the current HIP
+stream, numpy holds host tables; every step of the decode path runs in the library's
+kernels.  Functions mirror the C names without the ``kvattn_`` prefix.
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import BF16, F32, KvattnError, check
+
+__all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets",
+           "partition_count", "block_bytes", "KvattnError", "BF16", "F32"]
+
+
+def _i32p(arr):
+    if arr is None:
+        return None
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _host_i32(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _dptr(t):
+    """Device address of a torch tensor (or None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _layout(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent):
+    return _lib.Layout(block_size, num_kv_heads, head_dim_k, head_dim_v,
+                       F32 if dtype in ("f32", F32) else BF16, 1 if latent else 0)
+
+
+def block_bytes(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent=False):
+    lib = _lib.load()
+    lay = _layout(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent)
+    return int(lib.kvattn_block_bytes(ctypes.byref(lay)))
+
+
+def partition_count(ctx_len, tok_begin, part_tokens):
+    return int(_lib.load().kvattn_partition_count(ctx_len, tok_begin, part_tokens))
+
+
+class Pool:
+    """Host metadata of a block pool over caller-owned device regions.
+
+    `regions` is a list of (device address, number of blocks) pairs -- typically
+    ``(tensor.data_ptr(), n)`` of torch tensors the caller keeps alive.
+    """
+
+    def __init__(self, block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent,
+                 regions, seed=0):
+        self._lib = _lib.load()
+        self.layout = _layout(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent)
+        arr = (_lib.Region * len(regions))()
+        for i, (addr, nblk) in enumerate(regions):
+            arr[i].base = ctypes.c_void_p(int(addr))
+            arr[i].num_blocks = int(nblk)
+        out = ctypes.c_void_p()
+        check(self._lib.kvattn_pool_alloc(ctypes.byref(self.layout), arr, len(regions),
+                                          ctypes.c_uint64(seed & (2 ** 64 - 1)),
+                                          ctypes.byref(out)), "pool_alloc")
+        self.handle = out
+        self.block_size = block_size
+
+    def close(self):
+        if self.handle:
+            self._lib.kvattn_pool_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self):
+        return int(self._lib.kvattn_pool_num_free(self.handle))
+
+    def refcount(self, block_id):
+        return int(self._lib.kvattn_pool_refcount(self.handle, int(block_id)))
+
+    def block_table(self, ctx_lens, max_blocks, first_tok=None, share_src=None,
+                    share_nblocks=None, explicit=None):
+        """Returns (status, table [B, max_blocks] int32, shortfall); raises only on misuse
+        of this wrapper -- the status codes of the C call are returned as they are."""
+        ctx = _host_i32(ctx_lens)
+        bsz = int(ctx.shape[0])
+        ft, ss, sn = _host_i32(first_tok), _host_i32(share_src), _host_i32(share_nblocks)
+        ex = None if explicit is None else np.ascontiguousarray(np.asarray(explicit, np.int32))
+        out = np.full((bsz, max_blocks), -7, np.int32)
+        short = ctypes.c_int64(-1)
+        st = self._lib.kvattn_block_table(self.handle, bsz, _i32p(ctx), _i32p(ft), _i32p(ss),
+                                          _i32p(sn), _i32p(ex), int(max_blocks), _i32p(out),
+                                          ctypes.byref(short))
+        return int(st), out, int(short.value)
+
+    def release(self, table):
+        t = np.ascontiguousarray(np.asarray(table, np.int32))
+        return int(self._lib.kvattn_block_release(self.handle, _i32p(t), t.shape[0], t.shape[1]))
+
+
+def decode_partial(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, ctx_lens,
+                   tok_begin, part_tokens, seq_dev, max_parts, o_part, lse_part, nparts,
+                   err=None, stream=None):
+    lib = _lib.load()
+    ctx, beg, part = _host_i32(ctx_lens), _host_i32(tok_begin), _host_i32(part_tokens)
+    st = lib.kvattn_decode_partial(pool.handle, _dptr(q), int(q_dtype), int(ctx.shape[0]),
+                                   int(num_q_heads), ctypes.c_float(scale), _dptr(table_dev),
+                                   int(max_blocks), _i32p(ctx), _i32p(beg), _i32p(part),
+                                   _dptr(seq_dev), int(max_parts), _dptr(o_part),
+                                   _dptr(lse_part), _dptr(nparts), _dptr(err), _stream(stream))
+    check(st, "decode_partial")
+
+
+def merge_lse(o_part, lse_part, nparts, batch, num_q_heads, max_parts, dv, o_out,
+              o_ext=None, lse_ext=None, lse_out=None, stream=None):
+    lib = _lib.load()
+    st = lib.kvattn_merge_lse(_dptr(o_part), _dptr(lse_part), _dptr(nparts), int(batch),
+                              int(num_q_heads), int(max_parts), int(dv), _dptr(o_ext),
+                              _dptr(lse_ext), _dptr(o_out), _dptr(lse_out), _stream(stream))
+    check(st, "merge_lse")
+
+
+def resolve_offsets(pool, table_dev, max_blocks, ctx_lens_dev, max_tokens, region_out,
+                    offset_out, stream=None):
+    lib = _lib.load()
+    st = lib.kvattn_resolve_offsets(pool.handle, _dptr(table_dev), int(table_dev.shape[0]),
+                                    int(max_blocks), _dptr(ctx_lens_dev), int(max_tokens),
+                                    _dptr(region_out), _dptr(offset_out), _stream(stream))
+    check(st, "resolve_offsets")
+
+
+class DecodeStep:
+    """Device-resident metadata and buffers for repeated decode steps over one batch.
+
+    Holds the block table, the per-sequence [ctx_len, tok_begin, part_tokens] rows and the
+    partial / output buffers on the device; `run` enqueues decode_partial then merge_lse on
+    the current stream.
+    """
+
+    def __init__(self, pool, table, ctx_lens, part_tokens, num_q_heads, head_dim_v,
+                 tok_begin=None, device="cuda"):
+        import torch
+        self.pool = pool
+        self.ctx = _host_i32(ctx_lens)
+        self.part = _host_i32(part_tokens)
+        self.beg = _host_i32(tok_begin)
+        self.batch = int(self.ctx.shape[0])
+        self.hq = int(num_q_heads)
+        self.dv = int(head_dim_v)
+        table = np.ascontiguousarray(np.asarray(table, np.int32))
+        self.max_blocks = int(table.shape[1])
+        begs = self.beg if self.beg is not None else np.zeros_like(self.ctx)
+        counts = [partition_count(int(c), int(b), int(p)) for c, b, p in zip(self.ctx, begs, self.part)]
+        if min(counts) < 0:
+            raise ValueError("invalid partition arguments")
+        self.max_parts = max(1, max(counts))
+        self.table_dev = torch.from_numpy(table).to(device)
+        self.seq_dev = torch.from_numpy(np.stack([self.ctx, begs, self.part]).astype(np.int32)).to(device)
+        f32 = torch.float32
+        self.o_part = torch.empty((self.batch, self.hq, self.max_parts, self.dv), dtype=f32, device=device)
+        self.lse_part = torch.empty((self.batch, self.hq, self.max_parts), dtype=f32, device=device)
+        self.nparts = torch.empty(self.batch, dtype=torch.int32, device=device)
+        self.o_out = torch.empty((self.batch, self.hq, self.dv), dtype=f32, device=device)
+        self.lse_out = torch.empty((self.batch, self.hq), dtype=f32, device=device)
+        self.err = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def partial(self, q, q_dtype, scale, stream=None):
+        decode_partial(self.pool, q, q_dtype, self.hq, scale, self.table_dev, self.max_blocks,
+                       self.ctx, self.beg, self.part, self.seq_dev, self.max_parts, self.o_part,
+                       self.lse_part, self.nparts, self.err, stream)
+
+    def merge(self, o_ext=None, lse_ext=None, stream=None):
+        merge_lse(self.o_part, self.lse_part, self.nparts, self.batch, self.hq, self.max_parts,
+                  self.dv, self.o_out, o_ext, lse_ext, self.lse_out, stream)
+
+    def run(self, q, q_dtype, scale, o_ext=None, lse_ext=None, stream=None):
+        self.partial(q, q_dtype, scale, stream)
+        self.merge(o_ext, lse_ext, stream)
+        return self.o_out, self.lse_out

@@ -1,0 +1,220 @@
+// C-ABI entry points of the device path: argument validation, kernel choice, launch.
+
+#include <cmath>
+#include <cstdlib>
+#include <string>
+
+#include "device_common.h"
+#include "pool_internal.h"
+
+namespace kvattn {
+
+hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, dim3 grid, hipStream_t st);
+hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, hipStream_t st);
+hipError_t launch_mla(const DecodeArgs& a, dim3 grid, hipStream_t st);
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static RegionTable region_table(const kvattn_pool* pool) {
+  RegionTable rt{};
+  for (int r = 0; r < KVATTN_MAX_REGIONS; ++r) {
+    rt.base[r] = static_cast<const char*>(r < pool->n_regions ? pool->base[r] : pool->base[0]);
+    rt.first[r] = pool->first_id[r];
+  }
+  rt.first[KVATTN_MAX_REGIONS] = pool->first_id[KVATTN_MAX_REGIONS];
+  rt.block_bytes = pool->block_bytes;
+  rt.n = pool->n_regions;
+  rt.total = (int32_t)pool->total_blocks;
+  return rt;
+}
+
+static int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+static bool force_generic() {
+  const char* e = std::getenv("KVATTN_FORCE_GENERIC");
+  return e && e[0] == '1';
+}
+
+static kvattn_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return KVATTN_OK;
+  return set_error(KVATTN_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace kvattn
+
+using namespace kvattn;
+
+extern "C" {
+
+kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int32_t q_dtype,
+                                    int32_t batch, int32_t num_q_heads, float scale,
+                                    const int32_t* table_dev, int32_t max_blocks,
+                                    const int32_t* ctx_lens, const int32_t* tok_begin,
+                                    const int32_t* part_tokens, const int32_t* seq_dev,
+                                    int32_t max_parts, float* o_part, float* lse_part,
+                                    int32_t* nparts_dev, int32_t* err_dev, void* hip_stream) {
+  clear_error();
+  if (!pool || !q || !table_dev || !ctx_lens || !part_tokens || !seq_dev || !o_part ||
+      !lse_part || !nparts_dev)
+    return set_error(KVATTN_E_INVAL, "decode_partial: null argument");
+  if (batch < 1 || num_q_heads < 1 || max_blocks < 1 || max_parts < 1)
+    return set_error(KVATTN_E_INVAL, "decode_partial: batch, heads, max_blocks and max_parts must be >= 1");
+  if (!std::isfinite(scale)) return set_error(KVATTN_E_INVAL, "decode_partial: scale must be finite");
+  if (!aligned16(q) || !aligned16(o_part))
+    return set_error(KVATTN_E_INVAL, "decode_partial: q and o_part must be 16-byte aligned");
+  const kvattn_layout& L = pool->layout;
+  if (q_dtype != L.kv_dtype)
+    return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: q_dtype must equal the cache dtype");
+  const int hkv = L.num_kv_heads;
+  if (num_q_heads % hkv != 0)
+    return set_error(KVATTN_E_INVAL, "decode_partial: num_q_heads must be a multiple of num_kv_heads");
+  const int group = num_q_heads / hkv;
+  const int bs = L.block_size;
+
+  // kernel choice
+  enum { K_MFMA, K_GENERIC, K_MLA } kind;
+  if (L.latent) {
+    if (L.kv_dtype != KVATTN_BF16 || L.head_dim_k != 576 || L.head_dim_v != 512 || bs != 64 ||
+        num_q_heads > 16)
+      return set_error(KVATTN_E_UNSUPPORTED,
+                       "decode_partial: latent caches need bf16, Dk 576, Dv 512, block 64, <= 16 heads");
+    kind = K_MLA;
+  } else {
+    const int d = L.head_dim_k;
+    if (L.head_dim_v != d || (d != 64 && d != 128 && d != 256))
+      return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: GQA needs Dk == Dv in {64, 128, 256}");
+    if (group > 16)
+      return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: at most 16 query heads per KV head");
+    kind = (L.kv_dtype == KVATTN_BF16 && bs >= 16 && !force_generic()) ? K_MFMA : K_GENERIC;
+  }
+
+  // per-sequence checks and grid size
+  int max_np = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int len = ctx_lens[b];
+    const int beg = tok_begin ? tok_begin[b] : 0;
+    const int P = part_tokens[b];
+    if (beg < 0 || beg > len || (int64_t)len > (int64_t)max_blocks * bs)
+      return set_error(KVATTN_E_INVAL, "decode_partial: sequence " + std::to_string(b) +
+                                           " needs 0 <= tok_begin <= ctx_len <= max_blocks * block_size");
+    if (P <= 0 || P % bs != 0)
+      return set_error(KVATTN_E_INVAL, "decode_partial: part_tokens must be a positive multiple of block_size");
+    const int np = kvattn_partition_count(len, beg, P);
+    if (np > max_parts)
+      return set_error(KVATTN_E_INVAL, "decode_partial: sequence " + std::to_string(b) +
+                                           " has more partitions than max_parts");
+    if (np > max_np) max_np = np;
+  }
+  if (max_np > 0 && pool->total_blocks == 0)
+    return set_error(KVATTN_E_INVAL, "decode_partial: the pool holds no blocks");
+  const int grid_np = max_np > 0 ? max_np : 1;
+  const int64_t items = (int64_t)batch * (kind == K_MLA ? 1 : hkv) * grid_np;
+  if (items > INT32_MAX) return set_error(KVATTN_E_INVAL, "decode_partial: launch too large");
+
+  DecodeArgs a{};
+  a.rt = region_table(pool);
+  a.q = q;
+  a.table = table_dev;
+  a.seq = seq_dev;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.nparts = nparts_dev;
+  a.err = err_dev;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = hkv;
+  a.group = group;
+  a.max_blocks = max_blocks;
+  a.max_parts = max_parts;
+  a.grid_np = grid_np;
+  a.bs = bs;
+  a.bs_shift = log2_exact(bs);
+  a.scale = scale;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const dim3 grid((unsigned)items);
+  hipError_t e;
+  switch (kind) {
+    case K_MLA: e = launch_mla(a, grid, st); break;
+    case K_MFMA: e = launch_gqa_mfma(a, L.head_dim_k, grid, st); break;
+    default: e = launch_gqa_generic(a, L.head_dim_k, L.kv_dtype == KVATTN_F32, grid, st); break;
+  }
+  return hip_status(e, "decode_partial launch");
+}
+
+kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,
+                               const int32_t* nparts_dev, int32_t batch, int32_t num_q_heads,
+                               int32_t max_parts, int32_t dv, const float* o_ext,
+                               const float* lse_ext, float* o_out, float* lse_out,
+                               void* hip_stream) {
+  clear_error();
+  if (!o_part || !lse_part || !nparts_dev || !o_out)
+    return set_error(KVATTN_E_INVAL, "merge_lse: null argument");
+  if ((o_ext == nullptr) != (lse_ext == nullptr))
+    return set_error(KVATTN_E_INVAL, "merge_lse: o_ext and lse_ext must both be given or both NULL");
+  if (batch < 1 || num_q_heads < 1 || max_parts < 1)
+    return set_error(KVATTN_E_INVAL, "merge_lse: batch, heads and max_parts must be >= 1");
+  if (dv < 1 || dv > 1024 || dv % 4 != 0)
+    return set_error(KVATTN_E_UNSUPPORTED, "merge_lse: dv must be a multiple of 4 in [4, 1024]");
+  if (!aligned16(o_part) || !aligned16(o_out) || (o_ext && !aligned16(o_ext)))
+    return set_error(KVATTN_E_INVAL, "merge_lse: o_part, o_ext and o_out must be 16-byte aligned");
+  MergeArgs a{o_part, lse_part, nparts_dev, o_ext, lse_ext, o_out, lse_out,
+              batch, num_q_heads, max_parts, dv};
+  return hip_status(launch_merge(a, static_cast<hipStream_t>(hip_stream)), "merge_lse launch");
+}
+
+}  // extern "C"
+
+namespace kvattn {
+
+__global__ void resolve_offsets_kernel(RegionTable rt, const int32_t* table, int32_t batch,
+                                       int32_t max_blocks, const int32_t* ctx_lens,
+                                       int32_t max_tokens, int32_t bs_shift, int32_t* region_out,
+                                       int64_t* offset_out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)batch * max_tokens) return;
+  const int b = (int)(gid / max_tokens);
+  const int t = (int)(gid - (int64_t)b * max_tokens);
+  int32_t r_out = -1;
+  int64_t off = -1;
+  if (t < ctx_lens[b] && (t >> bs_shift) < max_blocks) {
+    const int32_t pid = table[(int64_t)b * max_blocks + (t >> bs_shift)];
+    if (valid_block(rt, pid)) {
+      const int r = region_of(rt, pid);
+      r_out = r;
+      // same address arithmetic as the decode kernels: block start + 16 bytes per token slot
+      off = (block_ptr(rt, pid) - rt.base[r]) + ((int64_t)(t & ((1 << bs_shift) - 1)) << 4);
+    }
+  }
+  region_out[gid] = r_out;
+  offset_out[gid] = off;
+}
+
+}  // namespace kvattn
+
+extern "C" kvattn_status kvattn_resolve_offsets(const kvattn_pool* pool, const int32_t* table_dev,
+                                                int32_t batch, int32_t max_blocks,
+                                                const int32_t* ctx_lens_dev, int32_t max_tokens,
+                                                int32_t* region_out, int64_t* offset_out,
+                                                void* hip_stream) {
+  clear_error();
+  if (!pool || !table_dev || !ctx_lens_dev || !region_out || !offset_out)
+    return set_error(KVATTN_E_INVAL, "resolve_offsets: null argument");
+  if (batch < 1 || max_blocks < 1 || max_tokens < 1 ||
+      (int64_t)max_tokens > (int64_t)max_blocks * pool->layout.block_size)
+    return set_error(KVATTN_E_INVAL, "resolve_offsets: bad sizes");
+  const int64_t n = (int64_t)batch * max_tokens;
+  const RegionTable rt = region_table(pool);
+  hipLaunchKernelGGL(resolve_offsets_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(hip_stream), rt, table_dev, batch, max_blocks,
+                     ctx_lens_dev, max_tokens, log2_exact(pool->layout.block_size), region_out,
+                     offset_out);
+  return hip_status(hipGetLastError(), "resolve_offsets launch");
+}

@@ -1,0 +1,33 @@
+// Host-side pool state shared by the pool bookkeeping (pool.cpp, no HIP dependency) and
+// the kernel launchers (which read the layout and the region table).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "kvattn.h"
+
+struct kvattn_pool {
+  kvattn_layout layout;
+  int64_t block_bytes = 0;
+  int32_t n_regions = 0;
+  void* base[KVATTN_MAX_REGIONS] = {};
+  int64_t first_id[KVATTN_MAX_REGIONS + 1] = {};  // first_id[n_regions] = total blocks
+  int64_t total_blocks = 0;
+  std::vector<int32_t> free_stack;  // next block handed out = back()
+  std::vector<int32_t> refcount;
+};
+
+namespace kvattn {
+
+// Thread-local last-error message; set_error returns `code` for convenient returns.
+kvattn_status set_error(kvattn_status code, const std::string& msg);
+void clear_error();
+
+// Layout checks shared by the pool and the launchers; returns an empty string when valid.
+std::string layout_problem(const kvattn_layout& l);
+
+inline int32_t elem_bytes(int32_t dtype) { return dtype == KVATTN_F32 ? 4 : 2; }
+
+}  // namespace kvattn

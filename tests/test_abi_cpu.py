@@ -1,0 +1,252 @@
+"""CPU tests of the C ABI: symbols, pool bookkeeping vs the oracle's model, validation.
+
+No call here reaches a kernel: the pool is host-only, and every decode / merge call below
+fails validation before anything is enqueued (fake device addresses are never touched).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.alloc import PoolError, PoolModel
+from oracle.layout import Layout as OLayout, block_elems
+from paged_kv_cache_mla_amd import _lib
+from paged_kv_cache_mla_amd.api import Pool, block_bytes, partition_count
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvattn.h")
+FAKE = 0x7F0000000000  # 16-byte aligned fake device address (never dereferenced)
+KIND = {"inval": _lib.E_INVAL, "exhausted": _lib.E_POOL_EXHAUSTED, "range": _lib.E_RANGE,
+        "state": _lib.E_STATE}
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return sorted(set(re.findall(r"\b(kvattn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert names == sorted(_lib._SIGNATURES)        # the binding covers exactly the header
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.kvattn_version().decode().startswith("kvattn")
+    assert lib.kvattn_last_error() is not None
+
+
+def _pool(total_or_regions, seed, bs=16, hkv=2, d=64, dtype="bf16", latent=False):
+    regions = total_or_regions if isinstance(total_or_regions, list) else [total_or_regions]
+    addrs = []
+    base = FAKE
+    for n in regions:
+        addrs.append((base, n))
+        base += 0x100000000
+    return Pool(bs, hkv, d, d, dtype, latent, addrs, seed=seed)
+
+
+def _model_call(model, fn, *args, **kw):
+    try:
+        return _lib.OK, getattr(model, fn)(*args, **kw), 0
+    except PoolError as e:
+        return KIND[e.kind], None, e.shortfall
+
+
+@pytest.mark.parametrize("seed", [0, 1, 12345, 2 ** 63 + 5])
+def test_initial_free_order_matches_oracle_shuffle(seed):
+    pool = _pool([37, 64], seed, bs=4)
+    model = PoolModel(101, seed, 4)
+    st, table, _ = pool.block_table([4 * 101], max_blocks=101)
+    assert st == _lib.OK
+    assert table[0].tolist() == oracle.alloc.shuffled_ids(101, seed)
+    assert table[0].tolist() == model.alloc([4 * 101], 101)[0].tolist()
+    assert pool.num_free == 0
+
+
+def test_pool_matches_model_over_random_operations():
+    rng = np.random.default_rng(7)
+    for trial in range(12):
+        bs = int(rng.choice([1, 4, 16, 64]))
+        total = int(rng.integers(1, 400))
+        seed = int(rng.integers(0, 2 ** 63))
+        split = int(rng.integers(0, total + 1))
+        pool = _pool([split, total - split] if split not in (0, total) else [total], seed, bs=bs)
+        model = PoolModel(total, seed, bs)
+        live = []
+        for step in range(40):
+            op = rng.random()
+            if op < 0.55 or not live:
+                bsz = int(rng.integers(1, 6))
+                mb = int(rng.integers(1, 12))
+                ctx = rng.integers(0, mb * bs + 1, size=bsz)
+                if rng.random() < 0.1:
+                    ctx[0] = mb * bs + 1                       # too long -> E_INVAL
+                first = None
+                share_src = share_n = None
+                if rng.random() < 0.3:
+                    first = [int(rng.integers(0, c + 1)) for c in ctx]
+                elif rng.random() < 0.5 and bsz > 1:
+                    share_src = [-1] + [int(rng.integers(-1, b)) for b in range(1, bsz)]
+                    share_n = [int(rng.integers(0, mb + 1)) for _ in range(bsz)]
+                st, table, short = pool.block_table(ctx, mb, first, share_src, share_n)
+                mst, mtable, mshort = _model_call(model, "alloc", ctx, mb, first, share_src, share_n)
+                assert st == mst, (trial, step, _lib.load().kvattn_last_error())
+                if st == _lib.OK:
+                    assert np.array_equal(table, mtable)
+                    live.append((ctx, table))
+                elif st == _lib.E_POOL_EXHAUSTED:
+                    assert short == mshort
+            elif op < 0.85:
+                ctx, table = live.pop(int(rng.integers(0, len(live))))
+                assert pool.release(table) == _lib.OK
+                model.release(table)
+                if rng.random() < 0.3:                          # double release
+                    assert pool.release(table) == _lib.E_STATE or not (table >= 0).any()
+            else:
+                # explicit claim of some currently free ids (plus maybe a used one)
+                free_now = list(model.free)
+                if not free_now:
+                    continue
+                k = int(rng.integers(1, min(len(free_now), 6) + 1))
+                ids = rng.choice(free_now, size=k, replace=False)
+                tab = np.full((2, k), -1, np.int32)
+                tab[0] = ids
+                tab[1, : k // 2] = ids[: k // 2]                    # shared references
+                if rng.random() < 0.3 and live:
+                    tab[0, 0] = live[0][1].reshape(-1)[live[0][1].reshape(-1) >= 0][0] \
+                        if (live[0][1] >= 0).any() else tab[0, 0]
+                ctx = [k * bs, (k // 2) * bs]
+                st, table, _ = pool.block_table(ctx, k, explicit=tab)
+                mst, mtab, _ = _model_call(model, "claim_explicit", ctx, tab)
+                assert st == mst
+                if st == _lib.OK:
+                    live.append((np.array(ctx), tab))
+            assert pool.num_free == len(model.free)
+            for pid in range(total):
+                assert pool.refcount(pid) == model.ref[pid]
+
+
+def test_exhaustion_is_all_or_nothing_and_reports_shortfall():
+    pool = _pool(10, 3, bs=16)
+    st, t1, _ = pool.block_table([16 * 6], max_blocks=8)
+    assert st == _lib.OK and pool.num_free == 4
+    st, t2, short = pool.block_table([16 * 3, 16 * 3], max_blocks=8)
+    assert st == _lib.E_POOL_EXHAUSTED and short == 2 and pool.num_free == 4
+    assert (t2 == -7).all()                                    # output untouched
+    assert pool.release(t1) == _lib.OK and pool.num_free == 10
+
+
+def test_explicit_table_errors():
+    pool = _pool(8, 0, bs=16)
+    st, _, _ = pool.block_table([32], 2, explicit=[[0, 8]])
+    assert st == _lib.E_RANGE
+    st, _, _ = pool.block_table([16], 2, explicit=[[0, 1]])       # entry past the end
+    assert st == _lib.E_INVAL
+    st, _, _ = pool.block_table([32, 16], 2, explicit=[[0, 1], [1, -1]])
+    assert st == _lib.OK and pool.refcount(1) == 2 and pool.refcount(0) == 1
+    st, _, _ = pool.block_table([16], 1, explicit=[[1]])
+    assert st == _lib.E_STATE
+    assert pool.release([[1, 1, 1]]) == _lib.E_STATE              # 3 drops, 2 refs
+    assert pool.release([[9]]) == _lib.E_RANGE
+    assert pool.release([[0, 1], [1, -1]]) == _lib.OK and pool.num_free == 8
+
+
+def test_pool_alloc_validation(lib):
+    lay = _lib.Layout(16, 2, 64, 64, _lib.BF16, 0)
+    out = ctypes.c_void_p()
+    regs = (_lib.Region * 2)()
+    regs[0].base, regs[0].num_blocks = FAKE, 4
+    regs[1].base, regs[1].num_blocks = FAKE + 8, 4                  # misaligned
+    assert lib.kvattn_pool_alloc(ctypes.byref(lay), regs, 2, 0, ctypes.byref(out)) == _lib.E_INVAL
+    regs[1].base = None
+    assert lib.kvattn_pool_alloc(ctypes.byref(lay), regs, 2, 0, ctypes.byref(out)) == _lib.E_INVAL
+    assert lib.kvattn_pool_alloc(ctypes.byref(lay), regs, 9, 0, ctypes.byref(out)) == _lib.E_INVAL
+    for bad in [_lib.Layout(12, 2, 64, 64, _lib.BF16, 0), _lib.Layout(16, 0, 64, 64, _lib.BF16, 0),
+                _lib.Layout(16, 2, 60, 64, _lib.BF16, 0), _lib.Layout(16, 2, 64, 64, 7, 0),
+                _lib.Layout(16, 2, 576, 512, _lib.BF16, 1), _lib.Layout(16, 1, 512, 576, _lib.BF16, 1)]:
+        assert lib.kvattn_block_bytes(ctypes.byref(bad)) == -1
+        assert lib.kvattn_pool_alloc(ctypes.byref(bad), regs, 1, 0, ctypes.byref(out)) == _lib.E_INVAL
+
+
+@pytest.mark.parametrize("shape", [(16, 4, 128, 128, "bf16", False), (16, 1, 64, 64, "f32", False),
+                                   (64, 1, 576, 512, "bf16", True), (16, 2, 256, 256, "bf16", False)])
+def test_block_bytes_match_oracle_layout(shape):
+    bs, hkv, dk, dv, dt, lat = shape
+    lay = OLayout(bs, hkv, dk, dv, dt, lat)
+    assert block_bytes(bs, hkv, dk, dv, dt, lat) == block_elems(lay) * lay.elem_bytes
+
+
+def test_partition_count_matches_oracle():
+    for L in range(0, 300, 7):
+        for beg in range(0, L + 2, 11):
+            for P in (-1, 0, 1, 16, 48, 512):
+                assert partition_count(L, beg, P) == oracle.partition_count(L, beg, P)
+
+
+def _decode_call(lib, pool, **over):
+    args = dict(q=FAKE, q_dtype=_lib.BF16, batch=2, hq=8, scale=0.1, table=FAKE, max_blocks=4,
+                ctx=[64, 50], beg=None, part=[32, 32], seq=FAKE, max_parts=2, o=FAKE, lse=FAKE,
+                nparts=FAKE, err=None)
+    args.update(over)
+    arr = lambda v: None if v is None else np.ascontiguousarray(np.asarray(v, np.int32))  # noqa: E731
+    ctx, beg, part = arr(args["ctx"]), arr(args["beg"]), arr(args["part"])
+    p32 = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))  # noqa: E731
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    return lib.kvattn_decode_partial(pool.handle, vp(args["q"]), args["q_dtype"], args["batch"],
+                                     args["hq"], ctypes.c_float(args["scale"]), vp(args["table"]),
+                                     args["max_blocks"], p32(ctx), p32(beg), p32(part),
+                                     vp(args["seq"]), args["max_parts"], vp(args["o"]),
+                                     vp(args["lse"]), vp(args["nparts"]), vp(args["err"]), None)
+
+
+def test_decode_partial_validation_without_gpu(lib):
+    pool = _pool(8, 0, bs=16, hkv=2, d=64)
+    assert _decode_call(lib, pool, q=None) == _lib.E_INVAL
+    assert _decode_call(lib, pool, q=FAKE + 4) == _lib.E_INVAL             # misaligned q
+    assert _decode_call(lib, pool, q_dtype=_lib.F32) == _lib.E_UNSUPPORTED
+    assert _decode_call(lib, pool, hq=7) == _lib.E_INVAL                    # not a multiple of Hkv
+    assert _decode_call(lib, pool, hq=34) == _lib.E_UNSUPPORTED             # group 17 > 16
+    assert _decode_call(lib, pool, part=[32, 24]) == _lib.E_INVAL           # not a block multiple
+    assert _decode_call(lib, pool, part=[32, 0]) == _lib.E_INVAL
+    assert _decode_call(lib, pool, ctx=[65, 50]) == _lib.E_INVAL            # > max_blocks * bs
+    assert _decode_call(lib, pool, beg=[0, 51]) == _lib.E_INVAL             # begin past the end
+    assert _decode_call(lib, pool, beg=[-1, 0]) == _lib.E_INVAL
+    assert _decode_call(lib, pool, max_parts=1) == _lib.E_INVAL             # 2 partitions needed
+    assert _decode_call(lib, pool, scale=float("nan")) == _lib.E_INVAL
+    assert _decode_call(lib, pool, batch=0) == _lib.E_INVAL
+    pool3 = _pool(8, 0, bs=16, hkv=2, d=96)
+    assert _decode_call(lib, pool3) == _lib.E_UNSUPPORTED                   # d 96 has no kernel
+    mla = _pool(8, 0, bs=32, hkv=1, d=576, latent=False)
+    assert mla.handle
+    mla_bad = Pool(32, 1, 576, 512, "bf16", True, [(FAKE, 4)])
+    assert _decode_call(lib, mla_bad, hq=16) == _lib.E_UNSUPPORTED          # latent needs bs 64
+    assert "block" in lib.kvattn_last_error().decode()
+
+
+def test_merge_validation_without_gpu(lib):
+    vp = ctypes.c_void_p
+    ok = dict(o=vp(FAKE), l=vp(FAKE), n=vp(FAKE), b=2, h=4, mp=3, dv=128, ox=None, lx=None,
+              out=vp(FAKE), lout=None)
+
+    def call(**over):
+        a = dict(ok)
+        a.update(over)
+        return lib.kvattn_merge_lse(a["o"], a["l"], a["n"], a["b"], a["h"], a["mp"], a["dv"],
+                                    a["ox"], a["lx"], a["out"], a["lout"], None)
+    assert call(o=None) == _lib.E_INVAL
+    assert call(ox=vp(FAKE)) == _lib.E_INVAL                                # lse_ext missing
+    assert call(dv=130) == _lib.E_UNSUPPORTED
+    assert call(dv=2048) == _lib.E_UNSUPPORTED
+    assert call(mp=0) == _lib.E_INVAL
+    assert call(out=vp(FAKE + 8)) == _lib.E_INVAL
+
+
+def test_partition_count_edge_values(lib):
+    assert lib.kvattn_partition_count(0, 0, 16) == 0
+    assert lib.kvattn_partition_count(1, 0, 16) == 1
+    assert lib.kvattn_partition_count(2 ** 31 - 1, 0, 1) == 2 ** 31 - 1
+    assert lib.kvattn_partition_count(10, 11, 16) == -1

@@ -1,0 +1,222 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (written here, applied element by element): bf16 caches with fp32 accumulation
+max |o_gpu - o_ref| / max |o_ref| <= 2e-3; fp32 caches max |o_gpu - o_ref| <= 1e-5; lse
+within 2e-3 (bf16) / 1e-5 (fp32).  Partition counts and address resolution are compared
+bit for bit, and relabelling physical blocks must leave the GPU output bitwise unchanged.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_case
+from tests import oracle_cases as oc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on CPU-only hosts)")
+    from paged_kv_cache_mla_amd import _lib
+    _lib.load()                      # fails loudly if the library is not built
+    torch.cuda.set_device(0)
+
+
+def _run(case, ext=None):
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    dc = DeviceCase(case)
+    o_ext = lse_ext = None
+    if ext is not None:
+        o_ext = torch.from_numpy(ext[0].astype(np.float32)).cuda()
+        lse_ext = torch.from_numpy(ext[1].astype(np.float32)).cuda()
+    o, lse = dc.run(o_ext, lse_ext)
+    torch.cuda.synchronize()
+    return dc, o.cpu().numpy(), lse.cpu().numpy()
+
+
+def _check_partials(case, dc, seqs=None):
+    parts = oc.device_partials(case, seqs)
+    nparts = dc.step.nparts.cpu().numpy()
+    o_part = dc.step.o_part.cpu().numpy()
+    l_part = dc.step.lse_part.cpu().numpy()
+    for idx, b in enumerate(range(case.batch) if seqs is None else seqs):
+        beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
+        assert nparts[b] == oracle.partition_count(int(case.ctx_lens[b]), beg, int(case.part_tokens[b]))
+        po, pl = parts[idx]
+        n = po.shape[0]
+        if n == 0:
+            continue
+        ref_scale = float(np.max(np.abs(po))) if case.dtype == "bf16" else 1.0
+        err = float(np.max(np.abs(o_part[b, :, :n, :].transpose(1, 0, 2) - po))) / ref_scale
+        assert err <= oc.out_tol(case), (b, err)
+        assert float(np.max(np.abs(l_part[b, :, :n].T - pl))) <= oc.lse_tol(case)
+
+
+SMALL = ["tiny_fp32", "gqa_32k", "split_128k", "prefix_shared", "mla_16k"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workload_matches_oracle(name):
+    case = make_case(name, "small")
+    _say(f"[parity] {name} small B={case.batch} L={case.ctx_lens.tolist()}")
+    ext = oc.external_partial(case) if case.ext_regions is not None else None
+    dc, o, lse = _run(case, ext)
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    _say(f"[parity] {name}: out error {err:.3e} (tol {oc.out_tol(case)})")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc)
+
+
+@pytest.mark.parametrize("name", ["gqa_32k", "prefix_shared", "split_128k"])
+def test_generic_kernel_matches_oracle(name, monkeypatch):
+    monkeypatch.setenv("KVATTN_FORCE_GENERIC", "1")
+    case = make_case(name, "small")
+    ext = oc.external_partial(case) if case.ext_regions is not None else None
+    _, o, lse = _run(case, ext)
+    o_ref, lse_ref = oc.full_reference(case)
+    assert oc.out_error(case, o, o_ref) <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+
+
+@pytest.mark.parametrize("name", ["gqa_32k", "mla_16k", "prefix_shared"])
+def test_deterministic_bitwise(name):
+    case = make_case(name, "small")
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    dc = DeviceCase(case)
+    o1, l1 = (t.clone() for t in dc.run())
+    o2, l2 = dc.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _relabelled(case, seed):
+    """Same logical content, every physical block moved to a new random slot (across
+    regions), tables rewritten accordingly."""
+    import copy
+    rng = np.random.default_rng(seed)
+    total = sum(case.region_blocks)
+    new_of_old = rng.permutation(total)
+    per = case.elems_per_block()
+    flat = np.concatenate(case.regions)
+    moved = np.empty_like(flat)
+    for old in range(total):
+        new = new_of_old[old]
+        moved[new * per:(new + 1) * per] = flat[old * per:(old + 1) * per]
+    c2 = copy.copy(case)
+    bounds = np.cumsum([0] + list(case.region_blocks))
+    c2.regions = [moved[bounds[r] * per:bounds[r + 1] * per] for r in range(len(case.region_blocks))]
+    t = case.table.copy()
+    t[t >= 0] = new_of_old[t[t >= 0]]
+    c2.table = t
+    return c2
+
+
+@pytest.mark.parametrize("name", ["gqa_32k", "prefix_shared", "mla_16k", "tiny_fp32"])
+def test_physical_relabelling_is_bitwise_invisible(name):
+    case = make_case(name, "small")
+    _, o1, l1 = _run(case)
+    _, o2, l2 = _run(_relabelled(case, 11))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["prefix_shared", "mla_16k", "split_128k", "tiny_fp32"])
+def test_resolution_offsets_bitwise(name):
+    from paged_kv_cache_mla_amd.api import resolve_offsets
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    case = make_case(name, "small")
+    dc = DeviceCase(case)
+    max_tokens = case.max_blocks * case.block_size
+    reg = torch.empty((case.batch, max_tokens), dtype=torch.int32, device="cuda")
+    off = torch.empty((case.batch, max_tokens), dtype=torch.int64, device="cuda")
+    ctx_dev = torch.from_numpy(case.ctx_lens).cuda()
+    resolve_offsets(dc.pool, dc.step.table_dev, case.max_blocks, ctx_dev, max_tokens, reg, off)
+    torch.cuda.synchronize()
+    want_r, want_o = oracle.resolve_offsets_reference(oc.layout_of(case), case.region_blocks,
+                                                      case.table, case.ctx_lens, max_tokens)
+    assert np.array_equal(reg.cpu().numpy(), want_r)
+    assert np.array_equal(off.cpu().numpy(), want_o)
+
+
+def test_one_token_context_returns_value_exactly():
+    case = make_case("gqa_32k", "small")
+    case.ctx_lens = np.array([1, 16, 17, 600], np.int32)
+    nb = [1, 1, 2, 38]
+    t = case.table.copy()
+    for b in range(case.batch):
+        t[b, nb[b]:] = -1
+    case.table = t
+    dc, o, lse = _run(case)
+    lay = oc.layout_of(case)
+    k, v = oracle.gather_sequence(lay, case.regions, case.region_blocks, case.table[0], 0, 1)
+    g = case.num_q_heads // case.num_kv_heads
+    for h in range(case.num_q_heads):
+        assert np.array_equal(o[0, h].astype(np.float64), v[0, h // g])      # bit-exact value
+    o_ref, _ = oc.full_reference(case)
+    assert oc.out_error(case, o, o_ref) <= oc.out_tol(case)
+
+
+def test_empty_device_range_returns_external_partial():
+    case = make_case("split_128k", "small")
+    case.tok_begin = case.ctx_lens.copy()             # the whole context lives elsewhere
+    rng = np.random.default_rng(3)
+    o_ext = rng.standard_normal((case.batch, case.num_q_heads, case.head_dim_v)).astype(np.float32)
+    l_ext = rng.standard_normal((case.batch, case.num_q_heads)).astype(np.float32)
+    dc, o, lse = _run(case, (o_ext, l_ext))
+    assert (dc.step.nparts.cpu().numpy() == 0).all()
+    assert np.allclose(o, o_ext, rtol=0, atol=1e-6) and np.allclose(lse, l_ext, rtol=0, atol=1e-6)
+
+
+def test_invalid_block_id_is_flagged_not_read():
+    from paged_kv_cache_mla_amd import _lib
+    case = make_case("gqa_32k", "small")
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    dc = DeviceCase(case)
+    bad = dc.table.copy()
+    bad[0, 3] = sum(case.region_blocks) + 5           # out of range inside sequence 0's span
+    dc.step.table_dev.copy_(torch.from_numpy(bad))
+    dc.run()
+    torch.cuda.synchronize()
+    assert int(dc.step.err.item()) & _lib.ERR_BAD_BLOCK
+
+
+# ---------------------------------------------------------------- full sizes, sampled
+FULL = [("gqa_32k", {}, [0, 7, 15]), ("mla_16k", {}, [0, 31]),
+        ("split_128k", {"r": 0.25}, [1]), ("split_128k", {"r": 0.5}, [2]),
+        ("split_128k", {"r": 0.75}, [3]), ("prefix_shared", {}, [0, 9, 63])]
+
+
+@pytest.mark.parametrize("name,kw,seqs", FULL, ids=[f"{n}-{k.get('r', '')}" for n, k, _ in FULL])
+def test_full_size_sampled_sequences(name, kw, seqs):
+    _say(f"[full] generating {name} {kw}")
+    case = make_case(name, "full", **kw)
+    ext = oc.external_partial(case, seqs) if case.ext_regions is not None else None
+    _say(f"[full] running {name} B={case.batch} device tokens={case.device_tokens()}")
+    dc, o, lse = _run(case, ext)
+    assert int(dc.step.err.item()) == 0
+    nparts = dc.step.nparts.cpu().numpy()
+    for b in range(case.batch):
+        beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
+        assert nparts[b] == oracle.partition_count(int(case.ctx_lens[b]), beg, int(case.part_tokens[b]))
+    o_ref, lse_ref = oc.full_reference(case, seqs)
+    err = oc.out_error(case, o[seqs], o_ref[seqs])
+    _say(f"[full] {name} {kw} sampled seqs {seqs}: out error {err:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse[seqs] - lse_ref[seqs]))) <= oc.lse_tol(case)
+    # every output finite and every lse finite
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
