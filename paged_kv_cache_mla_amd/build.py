@@ -4,7 +4,9 @@
 
 Every .hip / .cpp file under csrc/ is compiled to an object in parallel and linked into
 paged_kv_cache_mla_amd/libkvattn.so.  Device code is compiled with packed-fp32 instructions
-disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).
+disabled (-Xclang -target-feature -Xclang -packed-fp32-ops) and MFMA accumulators kept in
+ordinary VGPRs (-mllvm -amdgpu-mfma-vgpr-form=1, device pass only), which avoids copies between register files
+around the online-softmax rescale.
 """
 
 import concurrent.futures
@@ -24,7 +26,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]
 
 
 def _compile(src: str) -> str:

@@ -10,14 +10,14 @@
 //  * gqa_decode_mfma_kernel (bf16, block size >= 16): one wave per work item.  Each 16-token
 //    tile is a dense contraction on the matrix cores: S^T[16 tok x 16 heads] = K Q^T with
 //    v_mfma_f32_16x16x32_bf16 (query heads of the group in the N columns, padded to 16),
-//    then O^T[D x 16 heads] += V^T P^T with v_mfma_f32_16x16x16_bf16.  The block layout makes
-//    both operands plain 16-byte / 8-byte per-lane loads straight from HBM: K is stored in
-//    16-byte chunks with the chunks of consecutive tokens side by side (one k-step of one tile
-//    is 1 KiB contiguous), V is stored transposed (one 16-dim slice of a tile is 512 B
+//    then, per pair of tiles, O^T[D x 16 heads] += V^T P^T, also 16x16x32.  The block layout
+//    makes both operands plain 16-byte / 8-byte per-lane loads straight from HBM: K is stored
+//    in 16-byte chunks with the chunks of consecutive tokens side by side (one k-step of one
+//    tile is 1 KiB contiguous), V is stored transposed (one 16-dim slice of a tile is 512 B
 //    contiguous).  The MFMA output layout of S^T (lane = head column, 4 consecutive tokens per
 //    lane) is exactly the B-operand layout the PV product needs, so no data moves between
-//    lanes except two shuffles for the per-head max.  Tiles are prefetched NBUF deep in
-//    registers.
+//    lanes except two lane swaps for the per-head max.  The next pair of tiles is prefetched
+//    into registers while the current pair is computed.
 //  * gqa_decode_generic_kernel (fp32 or bf16, any block size): a plain VALU version, one token
 //    per lane, used for fp32 caches and as an independent cross-check of the MFMA kernel.
 
@@ -28,10 +28,23 @@ namespace kvattn {
 static constexpr float kNegInf = -__builtin_huge_valf();
 static constexpr float kLn2 = 0.693147180559945309f;
 
-template <int D, int NBUF>
+// Growth of a head's running max (log2 domain) tolerated before the accumulators are
+// rescaled: the unnormalised weights then stay below 2^8, well inside fp32 / bf16 range, and
+// the rescale (a pass over every accumulator) happens only a few times per partition.
+static constexpr float kRescaleSlack = 8.f;
+
+// Tiles are consumed in pairs.  For a pair (A, B) the PV product is one
+// v_mfma_f32_16x16x32_bf16 per 16-dim output tile with k-slot (g4, i) = token 4*g4 + i of A
+// for i < 4 and of B for i >= 4: the A operand is then just the two tiles' 8-byte V^T slices
+// side by side, and the B operand the two tiles' score-layout weights side by side.  The
+// weights enter as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)), two MFMAs per
+// output tile, so P V is accurate to ~2^-16 relative rather than bf16's 2^-9.
+template <int D, int BSL, int PAIRS>
 __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
-  constexpr int KS = D / 32;  // k-steps of the QK product (32 dims each)
-  constexpr int VT = D / 16;  // 16-dim output tiles of the PV product
+  constexpr int BS = 1 << BSL;
+  constexpr int KS = D / 32;       // k-steps of the QK product (32 dims each)
+  constexpr int VT = D / 16;       // 16-dim output tiles of the PV product
+  constexpr int RING = 2 * PAIRS;  // tiles held in registers
   const int lane = threadIdx.x;
   const int n = lane & 15;  // MFMA row / column index
   const int g4 = lane >> 4; // lane group: k-slot of the operands, row group of the output
@@ -55,6 +68,14 @@ __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
   const int t_lo = lo >> 4;
   const int ntiles = ((hi + 15) >> 4) - t_lo;
 
+  // Block ids of the partition (at most 128 blocks; the launcher checks), two per lane:
+  // pid0 lane i = block wbase + i, pid1 lane i = block wbase + 64 + i.
+  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  const int blk_last = ((t_lo + ntiles - 1) << 4) >> BSL;
+  const int wbase = (t_lo << 4) >> BSL;
+  const int pid0 = trow[min(wbase + lane, blk_last)];
+  const int pid1 = trow[min(wbase + 64 + lane, blk_last)];
+
   // B operand of the QK product: Q^T, lane (n, g4) holds head n, dims 8*(g4+4j) .. +7.
   bf16x8 qop[KS];
   {
@@ -69,88 +90,118 @@ __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  const int64_t kchunk0 = (int64_t)kvh * (D / 8);
-  const int64_t vrow0 = (int64_t)kvh * D;
-  const int64_t kpart_bytes = (int64_t)a.hkv * a.bs * D * 2;
-  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  // Per-lane byte offsets inside a block (tile start folded into the uniform base):
+  //   K chunk kvh*D/8 + g4 + 4j of token slot n:  koff + j * 4*BS*16
+  //   V^T row kvh*D + n + 16t, token slots 4*g4..: voff + t * 16*BS*2
+  const uint32_t koff = (uint32_t)((((kvh * (D / 8) + g4) << BSL) + n) * 16);
+  const uint32_t voff = (uint32_t)((((kvh * D + n) << BSL) + 4 * g4) * 2);
+  const int64_t kpart_bytes = (int64_t)a.hkv * BS * D * 2;
 
-  uint4 kb[NBUF][KS];
-  uint2 vb[NBUF][VT];
-  bool vld[NBUF];
+  u32x4 kb[RING][KS];
+  u32x2 vb[RING][VT];
+  bool vld[RING];
 
-  auto issue = [&](int slot, int tile_rel) {
-    const int tok0 = (t_lo + tile_rel) << 4;
-    const int blk = tok0 >> a.bs_shift;
-    const int sub = tok0 & (a.bs - 1);
-    const int32_t pid = trow[blk];
-    vld[slot] = valid_block(a.rt, pid);
-    const char* base = block_ptr(a.rt, pid);
+  auto issue = [&](int slot, int rel) {
+    const int tok0 = (t_lo + rel) << 4;
+    const int blk = tok0 >> BSL;
+    const int sub = tok0 & (BS - 1);
+    const int rb = blk - wbase;
+    const int32_t pa = __builtin_amdgcn_readlane(pid0, rb & 63);
+    const int32_t pb = __builtin_amdgcn_readlane(pid1, rb & 63);
+    const int32_t pid = rb < 64 ? pa : pb;
+    const bool ok = valid_block(a.rt, pid);
+    vld[slot] = ok;
+    gchar* base = block_addr(a.rt, ok ? pid : 0);
+    gchar* kbase = base + sub * 16;
+    gchar* vbase = base + kpart_bytes + sub * 2;
 #pragma unroll
     for (int j = 0; j < KS; ++j)
-      kb[slot][j] = *reinterpret_cast<const uint4*>(
-          base + ((((kchunk0 + g4 + 4 * j) << a.bs_shift) + sub + n) << 4));
+      kb[slot][j] = *reinterpret_cast<gu32x4*>(kbase + koff + j * (4 * BS * 16));
 #pragma unroll
     for (int t = 0; t < VT; ++t)
-      vb[slot][t] = *reinterpret_cast<const uint2*>(
-          base + kpart_bytes + ((((vrow0 + 16 * t + n) << a.bs_shift) + sub + 4 * g4) << 1));
+      vb[slot][t] = *reinterpret_cast<gu32x2*>(vbase + voff + t * (16 * BS * 2));
   };
 
   f32x4 acc[VT];
 #pragma unroll
   for (int t = 0; t < VT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf;  // running max of this lane's head, log2 domain
-  float lsum = 0.f;   // this lane's share of the running normaliser
+  float m = kNegInf;  // reference max of this lane's head (log2 domain)
+  float lsum = 0.f;   // this lane's share of the normaliser
   bool bad = false;
+  const float scale_log2 = a.scale_log2;
 
+  // scores of one tile, masked: lane (n, g4), register i = token 16*tile + 4*g4 + i, head n
+  auto scores = [&](int slot, int rel, float* sv) {
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < NBUF - 1; ++s) issue(s, min(s, ntiles - 1));
+    for (int j = 0; j < KS; ++j)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[slot][j]), qop[j], sacc, 0, 0, 0);
+    const int tb = ((t_lo + rel) << 4) + 4 * g4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tb + i;
+      const bool ok = vld[slot] & (t >= lo) & (t < hi);  // bitwise: no short-circuit branches
+      sv[i] = ok ? sacc[i] * scale_log2 : kNegInf;
+    }
+    bad |= !vld[slot] & (rel < ntiles);
+  };
 
-  for (int it = 0; it < ntiles; it += NBUF) {
+  // prologue: the first PAIRS - 1 pairs
 #pragma unroll
-    for (int s = 0; s < NBUF; ++s) {
-      issue((s + NBUF - 1) % NBUF, min(it + s + NBUF - 1, ntiles - 1));
-      if (it + s < ntiles) {
-        const int tile = t_lo + it + s;
-        bad |= !vld[s];
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < RING - 2; ++s) issue(s, min(s, ntiles - 1));
+
+  // Tiles past the end of the partition are computed fully masked (zero weight, max
+  // unchanged), so the loop body has no branches around memory operations.
+  for (int it = 0; it < ntiles; it += RING) {
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[s][j]), qop[j], sacc, 0, 0, 0);
-        // lane (n, g4), register i: token 16*tile + 4*g4 + i, head n
-        const int tb = (tile << 4) + 4 * g4;
-        float sv[4];
-        float mx = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tb + i;
-          const bool ok = vld[s] && t >= lo && t < hi;
-          sv[i] = ok ? sacc[i] * a.scale_log2 : kNegInf;
-          mx = fmaxf(mx, sv[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int ps = 0; ps < PAIRS; ++ps) {
+      const int sa = 2 * ps, sb = 2 * ps + 1;
+      const int ra = it + 2 * ps, rb = ra + 1;
+      // refill the pair slot consumed last round with the pair RING - 2 tiles ahead
+      const int fs = (sa + RING - 2) % RING;
+      issue(fs, min(ra + RING - 2, ntiles - 1));
+      issue(fs + 1, min(ra + RING - 1, ntiles - 1));
+      float sva[4], svb[4];
+      scores(sa, ra, sva);
+      scores(sb, rb, svb);
+      const float mx = rows_max(fmaxf(fmaxf(fmaxf(sva[0], sva[1]), fmaxf(sva[2], sva[3])),
+                                      fmaxf(fmaxf(svb[0], svb[1]), fmaxf(svb[2], svb[3]))));
+      if (__any(mx > m + kRescaleSlack)) {
         const float mnew = fmaxf(m, mx);
-        const float mref = mnew == kNegInf ? 0.f : mnew;
-        const float alpha = exp2f(m - mref);
-        const uint32_t p01 = pack_bf16x2(exp2f(sv[0] - mref), exp2f(sv[1] - mref));
-        const uint32_t p23 = pack_bf16x2(exp2f(sv[2] - mref), exp2f(sv[3] - mref));
-        // normalise with the same bf16-rounded weights the PV product uses
-        lsum = lsum * alpha + ((bf16_to_f32(p01 & 0xffffu) + bf16_to_f32(p01 >> 16)) +
-                               (bf16_to_f32(p23 & 0xffffu) + bf16_to_f32(p23 >> 16)));
-        m = mnew;
-        const i16x4 pop = as_i16x4(make_uint2(p01, p23));
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m = -inf
 #pragma unroll
-        for (int t = 0; t < VT; ++t) {
-          acc[t] *= alpha;
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(vb[s][t]), pop, acc[t], 0, 0, 0);
-        }
+        for (int t = 0; t < VT; ++t) acc[t] *= alpha;
+        lsum *= alpha;
+        m = mnew;
+      }
+      const float mref = m == kNegInf ? 0.f : m;
+      float pw[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = __builtin_amdgcn_exp2f(sva[i] - mref);
+        pw[4 + i] = __builtin_amdgcn_exp2f(svb[i] - mref);
+      }
+      u32x4 phi, plo;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t h = cvt_pk_bf16(pw[2 * k], pw[2 * k + 1]);
+        phi[k] = h;
+        plo[k] = cvt_pk_bf16(pw[2 * k] - __uint_as_float(h << 16),
+                             pw[2 * k + 1] - __uint_as_float(h & 0xffff0000u));
+      }
+      lsum += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+      const bf16x8 bhi = as_bf16x8(phi), blo = as_bf16x8(plo);
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        const bf16x8 vop = as_bf16x8(u32x4{vb[sa][t][0], vb[sa][t][1], vb[sb][t][0], vb[sb][t][1]});
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, bhi, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, blo, acc[t], 0, 0, 0);
       }
     }
   }
-  if (bad && lane == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+  if (bad) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = rows_sum(lsum);
   if (n < a.group) {
     const int h = kvh * a.group + n;
     const int64_t row = ((int64_t)b * a.hq + h) * a.max_parts + p;
@@ -286,11 +337,23 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ launchers
+template <int D, int BSL>
+static hipError_t launch_mfma_db(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int PAIRS = D <= 128 ? 2 : 1;  // tile pairs held in registers
+  hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS>), grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_mfma_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int NBUF = D <= 128 ? 3 : 2;
-  hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, NBUF>), grid, dim3(64), 0, st, a);
-  return hipGetLastError();
+  switch (a.bs_shift) {
+    case 4: return launch_mfma_db<D, 4>(a, grid, st);
+    case 5: return launch_mfma_db<D, 5>(a, grid, st);
+    case 6: return launch_mfma_db<D, 6>(a, grid, st);
+    case 7: return launch_mfma_db<D, 7>(a, grid, st);
+    case 8: return launch_mfma_db<D, 8>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {

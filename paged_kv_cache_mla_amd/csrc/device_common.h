@@ -14,6 +14,8 @@ namespace kvattn {
 struct RegionTable {
   const char* base[KVATTN_MAX_REGIONS];
   int64_t first[KVATTN_MAX_REGIONS + 1];
+  uint64_t adj[KVATTN_MAX_REGIONS];  // (uint64)base[r] - first[r] * block_bytes (mod 2^64)
+  int32_t first32[KVATTN_MAX_REGIONS];  // first[r] (ids fit in int32)
   int64_t block_bytes;
   int32_t n;
   int32_t total;  // number of valid ids
@@ -69,6 +71,25 @@ __device__ __forceinline__ const char* block_ptr(const RegionTable& rt, int32_t 
   return rt.base[r] + ((int64_t)pid - rt.first[r]) * rt.block_bytes;
 }
 
+// Pointers into device memory in the global address space, so that loads through them are
+// global (not flat) loads: flat loads also count against the LDS wait counter, which would
+// make every LDS wait drain the outstanding HBM loads.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const char gchar;
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const u32x2 gu32x2;
+
+// Start of block `pid`, which must be a valid id, with selects only (no dynamic indexing of
+// the kernarg table, no branches): the last region whose first id is <= pid owns it.
+__device__ __forceinline__ gchar* block_addr(const RegionTable& rt, int32_t pid) {
+  uint64_t a = rt.adj[0];
+#pragma unroll
+  for (int i = 1; i < KVATTN_MAX_REGIONS; ++i)
+    a = (i < rt.n && pid >= rt.first32[i]) ? rt.adj[i] : a;
+  return reinterpret_cast<gchar*>(a + (uint64_t)(int64_t)pid * (uint64_t)rt.block_bytes);
+}
+
 __device__ __forceinline__ void flag_error(int32_t* err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }
@@ -111,6 +132,34 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ i16x4 as_i16x4(uint2 v) { return __builtin_bit_cast(i16x4, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ i16x4 as_i16x4(u32x2 v) { return __builtin_bit_cast(i16x4, v); }
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with the
+// gfx950 lane-swap instructions (VALU only, no LDS round trip): v_permlane32_swap with both
+// operands = v yields v[l mod 32] and v[l mod 32 + 32]; v_permlane16_swap likewise pairs
+// rows 0/1 and 2/3.  Every lane ends with the same value, summed in the same order.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

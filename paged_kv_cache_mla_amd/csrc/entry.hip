@@ -22,6 +22,9 @@ static RegionTable region_table(const kvattn_pool* pool) {
   for (int r = 0; r < KVATTN_MAX_REGIONS; ++r) {
     rt.base[r] = static_cast<const char*>(r < pool->n_regions ? pool->base[r] : pool->base[0]);
     rt.first[r] = pool->first_id[r];
+    rt.first32[r] = static_cast<int32_t>(pool->first_id[r]);
+    rt.adj[r] = reinterpret_cast<uint64_t>(rt.base[r]) -
+                static_cast<uint64_t>(pool->first_id[r]) * static_cast<uint64_t>(pool->block_bytes);
   }
   rt.first[KVATTN_MAX_REGIONS] = pool->first_id[KVATTN_MAX_REGIONS];
   rt.block_bytes = pool->block_bytes;
@@ -92,6 +95,9 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
     if (group > 16)
       return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: at most 16 query heads per KV head");
     kind = (L.kv_dtype == KVATTN_BF16 && bs >= 16 && !force_generic()) ? K_MFMA : K_GENERIC;
+    // the matrix-core kernel keeps a partition's block ids in two 64-lane registers
+    for (int b = 0; b < batch && kind == K_MFMA; ++b)
+      if (part_tokens[b] > 0 && part_tokens[b] / bs + 1 > 128) kind = K_GENERIC;
   }
 
   // per-sequence checks and grid size
