@@ -46,6 +46,8 @@ def log(msg):
 
 
 def kernel_hash(workload):
+    """Hash of the sources the workload's dominant kernel is built from (plus the build
+    flags): stored counter readings apply only while this hash is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_mla_amd", "csrc")
     for f in KERNEL_SOURCES.get(workload, DEFAULT_KERNEL_SOURCES):
@@ -56,17 +58,121 @@ def kernel_hash(workload):
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload, launches_bytes):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken on
-    the current kernel source; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def profile_path(workload):
+    return os.path.join(ROOT, "profiles", f"decode_partial_and_merge.{workload}.md")
+
+
+def read_profile_values(path):
+    """`key: value` lines of a profile summary (the lines between the two `values` markers)."""
+    vals = {}
+    inside = False
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line == "<!-- values -->":
+                inside = not inside
+                continue
+            if inside and ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    return vals
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; None otherwise."""
+    path = profile_path(workload)
     if not os.path.exists(path):
         return None
-    with open(path) as fh:
-        t = json.load(fh)
-    if t.get("kernel_hash") != kernel_hash(workload):
+    vals = read_profile_values(path)
+    if vals.get("kernel_hash") != kernel_hash(workload) or "hbm_bytes_per_launch" not in vals:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return int(vals["hbm_bytes_per_launch"])
+
+
+# --------------------------------------------------------------- rocprofv3 summaries
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 2 << 30  # the device-to-device copy of copy_bandwidth(): 2 GiB read, 2 GiB written
+
+
+def _short(name):
+    name = name.split("(")[0]
+    return name.replace("void ", "")
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _counter_by_kernel(rows, counter):
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def _copy_factor(per_kernel):
+    """Known bytes / counter bytes for the large device-to-device copies of copy_bandwidth()."""
+    runs = per_kernel.get(COPY_KERNEL, [])
+    if not runs:
+        raise RuntimeError("no copy kernel in the counter run")
+    big = max(g for g, _ in runs)
+    vals = [v for g, v in runs if g == big]
+    return COPY_BYTES / (1024.0 * sum(vals) / len(vals))
+
+
+def summarize_profile(workload, fetch_dir, write_dir, stats_dir, out_path, commands):
+    """Write the text summary of one workload's rocprofv3 runs: kernel-trace statistics and
+    FETCH_SIZE / WRITE_SIZE per dispatch, scaled by the copy-kernel calibration."""
+    import glob
+    stats = _read_csv(glob.glob(os.path.join(stats_dir, "*kernel_stats.csv"))[0])
+    fetch = _counter_by_kernel(_read_csv(glob.glob(os.path.join(fetch_dir, "*counter_collection.csv"))[0]), "FETCH_SIZE")
+    write = _counter_by_kernel(_read_csv(glob.glob(os.path.join(write_dir, "*counter_collection.csv"))[0]), "WRITE_SIZE")
+    f_fetch, f_write = _copy_factor(fetch), _copy_factor(write)
+    ours = [r for r in stats if "kvattn::" in r["Name"]]
+    ours.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# rocprofv3 summary: {workload} ({DESCR[workload]})", "",
+             "Commands (from the repository root; rocprofv3 runs were started from /tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "## Kernel trace (--kernel-trace --stats)", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in ours:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## HBM counters (--pmc, one counter per run), KiB per dispatch", "",
+              f"Calibration: a {COPY_BYTES >> 30} GiB device-to-device copy ({COPY_KERNEL}) reads "
+              f"FETCH_SIZE x {f_fetch:.4f} and WRITE_SIZE x {f_write:.4f} of its known size; the "
+              "bytes below are scaled by these factors.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read bytes | scaled write bytes |",
+              "|---|---|---|---|---|"]
+    dom = None
+    for r in ours:
+        name = r["Name"]
+        fv = [v for _, v in fetch.get(name, [])]
+        wv = [v for _, v in write.get(name, [])]
+        if not fv or not wv:
+            continue
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        rb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
+        lines.append(f"| {_short(name)} | {fk:.0f} | {wk:.0f} | {rb:.0f} | {wb:.0f} |")
+        if dom is None:
+            dom = (name, float(r["AverageNs"]), rb + wb)
+    lines += ["", "Values read by bench.py (dominant kernel; void once the kernel source changes):", "",
+              "<!-- values -->",
+              f"kernel: {_short(dom[0])}",
+              f"kernel_hash: {kernel_hash(workload)}",
+              f"avg_duration_us: {dom[1] / 1e3:.2f}",
+              f"fetch_factor: {f_fetch:.5f}",
+              f"write_factor: {f_write:.5f}",
+              f"hbm_bytes_per_launch: {dom[2]:.0f}",
+              "<!-- values -->", ""]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines))
+    return out_path
 
 
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
@@ -127,7 +233,16 @@ def main():
     ap.add_argument("--workload", default="gqa_32k", choices=sorted(DESCR))
     ap.add_argument("--r", type=float, default=0.5, help="host share of split_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
+                    help="write profiles/decode_partial_and_merge.<workload>.md from rocprofv3 "
+                         "output directories (no GPU needed) and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize: a command line to record in the summary")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize_profile(args.workload, *args.summarize, profile_path(args.workload),
+                                args.command))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library has "
               "no multi-GPU path)", file=sys.stderr)
@@ -236,7 +351,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": stored_traffic(args.workload, kernel_bytes),
+            "traffic": stored_traffic(args.workload),
             "alg_bytes_per_launch": kernel_bytes,
             "avg_launch_us": round(avg_part_ms * 1e3, 2),
         },
