@@ -35,6 +35,10 @@ DESCR = {
     "mla_16k": "DeepSeek-V2-Lite-shaped MLA latent decode, B32 x 16K",
     "tiny_fp32": "tiny fp32 paged decode",
 }
+# Partitions merged on chip into each written partial, per workload (the launch configuration
+# the full-size parity tests use too): fewer partial writes next to the K/V read stream.
+GROUP_PARTS = {"gqa_32k": 4, "split_128k": 4, "prefix_shared": 4, "mla_16k": 1, "tiny_fp32": 1}
+
 KERNEL_SOURCES = {
     "mla_16k": ["decode_mla.hip", "device_common.h"],
 }
@@ -175,6 +179,50 @@ def summarize_profile(workload, fetch_dir, write_dir, stats_dir, out_path, comma
     return out_path
 
 
+class HipTimer:
+    """HIP timing events on an explicit stream, through the HIP runtime torch itself loaded,
+    created with hipEventDisableSystemFence: recording them neither writes back nor
+    invalidates the caches, so they do not perturb the kernels they bracket."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                f = line.split()[-1]
+                if os.path.basename(f).startswith("libamdhip64"):
+                    path = f
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self._c = ctypes
+        self.hip = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [vp, vp]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.events = []
+
+    def event(self):
+        e = self._c.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self._c.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.events.append(e)
+        return e
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, self._c.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        f = self._c.c_float()
+        if self.hip.hipEventElapsedTime(self._c.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -193,21 +241,23 @@ def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """Float64 oracle on a bounded sample: whole sequences, all heads, until ~budget_s."""
+def cpu_baseline(case, budget_s=10.0):
+    """The float64 oracle on a bounded sample of the same workload: whole sequences (all
+    heads), cycling over the batch until ~budget_s of CPU time has been spent."""
     import numpy as np
     import oracle
     lay = oracle.Layout(case.block_size, case.num_kv_heads, case.head_dim_k, case.head_dim_v,
                         case.dtype, case.latent)
     t0 = time.perf_counter()
     done_tokens = 0
-    seqs = []
-    for b in range(case.batch):
+    n_seq = 0
+    while True:
+        b = n_seq % case.batch
         oracle.decode_reference(lay, case.regions, case.region_blocks, case.table, case.ctx_lens,
                                 case.q, case.scale, tok_begin=case.tok_begin, seqs=[b])
         beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
         done_tokens += int(case.ctx_lens[b]) - beg
-        seqs.append(b)
+        n_seq += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
@@ -219,10 +269,10 @@ def cpu_baseline(case, budget_s=12.0):
     except Exception:
         pass
     cores = len(os.sched_getaffinity(0))
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads or cores,
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads or cores,
             "host_cpus": cores, "kind": "oracle",
-            "sample": f"{len(seqs)} of {case.batch} sequences (all heads), {done_tokens} tokens, "
-                      f"float64 numpy, {dt:.1f} s"}
+            "sample": f"{n_seq} sequence passes over the {case.batch} sequences (all heads), "
+                      f"{done_tokens} tokens, {nbytes} KV bytes, float64 numpy, {dt:.1f} s"}
 
 
 def main():
@@ -232,6 +282,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_32k", choices=sorted(DESCR))
     ap.add_argument("--r", type=float, default=0.5, help="host share of split_128k")
+    ap.add_argument("--group-parts", type=int, default=0,
+                    help="partitions merged on chip per written partial (default: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
                     help="write profiles/decode_partial_and_merge.<workload>.md from rocprofv3 "
@@ -260,8 +312,9 @@ def main():
     log(f"[bench] generating {args.workload} (full)")
     kw = {"r": args.r} if args.workload == "split_128k" else {}
     case = make_case(args.workload, "full" if args.workload != "tiny_fp32" else "small", **kw)
-    log("[bench] uploading")
-    dc = DeviceCase(case)
+    group_parts = args.group_parts or GROUP_PARTS[args.workload]
+    log(f"[bench] uploading (group_parts {group_parts})")
+    dc = DeviceCase(case, group_parts=group_parts)
     o_ext = lse_ext = None
     if case.ext_regions is not None:
         # the host share's partial enters the merge as an opaque (o, lse) input; its values do
@@ -278,21 +331,24 @@ def main():
     if int(dc.step.err.item()) != 0:
         raise RuntimeError(f"kernel error flag {int(dc.step.err.item())}")
 
-    stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The dominant kernel's duration: HIP events recorded on the launch stream around every
+    # decode_partial of the timed loop.  They are created without the system-scope fence, so
+    # recording one does not write back and invalidate the caches (torch's timing events do,
+    # which adds ~3 us per event to the step on MI355X).
+    timer = HipTimer()
+    sp = torch.cuda.current_stream().cuda_stream
+    evs = [(timer.event(), timer.event()) for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        evs[i][0].record(stream)
+        timer.record(evs[i][0], sp)
         dc.partial()
-        evs[i][1].record(stream)
+        timer.record(evs[i][1], sp)
         dc.merge(o_ext, lse_ext)
-        evs[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_part = [e[0].elapsed_time(e[1]) for e in evs]
-    t_merge = [e[1].elapsed_time(e[2]) for e in evs]
+    t_part = [timer.elapsed_ms(a, b) for a, b in evs]
     ms_step = wall * 1e3 / args.steps
 
     kv_bytes = case.device_tokens() * case.kv_bytes_per_token()
@@ -327,7 +383,8 @@ def main():
         "attn_only_model_tokens_per_s": (round(case.batch / (layers * ms_step * 1e-3), 1)
                                          if layers else None),
         "t_partial_us": round(avg_part_ms * 1e3, 2),
-        "t_merge_us": round(float(np.mean(t_merge)) * 1e3, 2),
+        # the rest of the step: the merge kernel plus the launch gaps around it
+        "t_merge_and_gaps_us": round((ms_step - avg_part_ms) * 1e3, 2),
         "kv_bytes": kv_bytes,
         "copy_GBps": round(copy_gbps, 1),
         "config": {
@@ -340,6 +397,7 @@ def main():
             "head_dim_v": case.head_dim_v,
             "block_size": case.block_size,
             "part_tokens": int(case.part_tokens[0]),
+            "group_parts": group_parts,
             "kv_dtype": case.dtype,
             "device_tokens": case.device_tokens(),
             **({"r": args.r} if args.workload == "split_128k" else {}),

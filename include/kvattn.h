@@ -73,6 +73,7 @@ enum { KVATTN_F32 = 0, KVATTN_BF16 = 1 };
 
 #define KVATTN_BLOCK_ABSENT (-1) /* table entry with no block on this device */
 #define KVATTN_MAX_REGIONS 8
+#define KVATTN_MAX_GROUP_PARTS 16 /* largest group_parts of kvattn_decode_partial */
 
 /* Error bits a decode kernel may set in *err_dev (see kvattn_decode_partial). */
 #define KVATTN_ERR_BAD_BLOCK 1   /* a table entry inside a sequence's range is not a valid id */
@@ -176,41 +177,54 @@ int32_t kvattn_partition_count(int32_t ctx_len, int32_t tok_begin, int32_t part_
 /*
  * One decode step's partial attention ([InplaceKVCache] §5.1 and §6.1: exact attention,
  * online softmax with a running max and normaliser, fp32 accumulation; sequence-dimension
- * split).  For every sequence b, KV head group and partition p of [tok_begin[b],
- * ctx_lens[b]) (geometry as in kvattn_partition_count with part_tokens[b]) it writes
- *     o_part[b][h][p][:] = sum_t w_t V(t) / sum_t w_t,  w_t = exp(s_t - max s),
- *     s_t = scale * q[b][h] . K(t),      lse_part[b][h][p] = max s + ln(sum_t w_t)
- * over the partition's tokens t, for every query head h, with KV head h / (Hq / Hkv)
- * (consecutive query heads share a KV head; MLA: all heads share the latent).  Logical
- * token t of sequence b lives at offset t % bs of physical block table_dev[b][t / bs].
+ * split).  The device-resident range [tok_begin[b], ctx_lens[b]) of every sequence b is cut
+ * into partitions of part_tokens[b] tokens (geometry as in kvattn_partition_count), and
+ * consecutive partitions are taken group_parts at a time: group k of sequence b covers
+ * partitions [k * group_parts, min(np_b, (k + 1) * group_parts)), i.e. the tokens
+ *     [tok_begin + k * group_parts * part_tokens, min(ctx_len, tok_begin + (k+1) * ...)).
+ * For every group and query head h (KV head h / (Hq / Hkv): consecutive query heads share a
+ * KV head; MLA: all heads share the latent) one partial is written:
+ *     o_part[b][h][k][:] = sum_t w_t V(t) / sum_t w_t,  w_t = exp(s_t - max s),
+ *     s_t = scale * q[b][h] . K(t),      lse_part[b][h][k] = max s + ln(sum_t w_t)
+ * over the group's tokens t.  The matrix-core GQA kernel computes each partition of a group
+ * on its own wave and merges the group's partials on chip, exactly, by the LSE rescaling of
+ * kvattn_merge_lse; the other kernels walk the group's tokens in order.  group_parts = 1
+ * writes one partial per partition; larger groups write fewer partials, which is faster on
+ * long contexts (partial writes compete with the K/V read stream).  Logical token t of
+ * sequence b lives at offset t % bs of physical block table_dev[b][t / bs].
  *
  *   q            device [batch][num_q_heads][Dk], element type q_dtype (must equal kv_dtype)
  *   table_dev    device [batch][max_blocks] int32 (entries of the range must be valid ids)
  *   ctx_lens, tok_begin (NULL = 0), part_tokens: host [batch] int32 used for validation and
  *                grid sizing; seq_dev: device int32 [3][batch] holding the same three arrays
  *                (row 1 all zeros if tok_begin is NULL), read by the kernels.
- *   max_parts    partitions per sequence the o_part / lse_part arrays have room for
+ *   max_parts    partials per sequence the o_part / lse_part arrays have room for
+ *   group_parts  partitions per written partial, 1 .. KVATTN_MAX_GROUP_PARTS
  *   o_part       device fp32 [batch][num_q_heads][max_parts][Dv]
  *   lse_part     device fp32 [batch][num_q_heads][max_parts]
- *   nparts_dev   device int32 [batch]: receives the partition count of each sequence
+ *   nparts_dev   device int32 [batch]: receives the number of partials written for each
+ *                sequence, ceil(np_b / group_parts)
  *   err_dev      device int32 or NULL: KVATTN_ERR_* bits are OR-ed in (never cleared) if a
  *                kernel meets an invalid block id or device lengths that disagree with the
  *                host ones; the offending block contributes nothing / the sequence gets no
- *                partitions, and no memory outside the arguments is touched.
- * Entries of o_part / lse_part for p >= nparts[b] are not written.
+ *                partials, and no memory outside the arguments is touched.
+ * Entries of o_part / lse_part for k >= nparts[b] are not written.
  * Validation (E_INVAL): null pointers, batch < 1, num_q_heads % Hkv != 0, per sequence
  * 0 <= tok_begin <= ctx_len <= max_blocks * bs, part_tokens > 0 and part_tokens % bs == 0,
- * partition count <= max_parts.  E_UNSUPPORTED: q_dtype != kv_dtype, or a head / dim
- * combination without a kernel (GQA: Dk = Dv in {64, 128, 256}, Hq / Hkv <= 16;
- * MLA: BF16, Dk = 576, Dv = 512, Hq <= 16, bs = 64).  E_HIP: launch failure.
+ * partials per sequence <= max_parts, group_parts outside [1, KVATTN_MAX_GROUP_PARTS].
+ * E_UNSUPPORTED: q_dtype != kv_dtype, or a head / dim combination without a kernel (GQA:
+ * Dk = Dv in {64, 128, 256}, Hq / Hkv <= 16; MLA: BF16, Dk = 576, Dv = 512, Hq <= 16,
+ * bs = 64); for the bf16 GQA kernel (block size >= 16) also group_parts above 16 (Dk 64) or
+ * 8 (Dk 128, 256), or group_parts * (Hq / Hkv) * (Dk + 1) * 4 > 65536.  E_HIP: launch failure.
  */
 kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int32_t q_dtype,
                                     int32_t batch, int32_t num_q_heads, float scale,
                                     const int32_t* table_dev, int32_t max_blocks,
                                     const int32_t* ctx_lens, const int32_t* tok_begin,
                                     const int32_t* part_tokens, const int32_t* seq_dev,
-                                    int32_t max_parts, float* o_part, float* lse_part,
-                                    int32_t* nparts_dev, int32_t* err_dev, void* hip_stream);
+                                    int32_t max_parts, int32_t group_parts, float* o_part,
+                                    float* lse_part, int32_t* nparts_dev, int32_t* err_dev,
+                                    void* hip_stream);
 
 /*
  * Exact LSE merge of each (sequence, head)'s partials ([InplaceKVCache] §4.2, §5.1, §5.2:

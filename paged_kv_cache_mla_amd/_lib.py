@@ -20,6 +20,7 @@ F32 = 0
 BF16 = 1
 BLOCK_ABSENT = -1
 MAX_REGIONS = 8
+MAX_GROUP_PARTS = 16
 ERR_BAD_BLOCK = 1
 ERR_BAD_SEQ = 2
 
@@ -55,7 +56,7 @@ _SIGNATURES = {
     "kvattn_pool_refcount": (_I32, [_P, _I32]),
     "kvattn_partition_count": (_I32, [_I32, _I32, _I32]),
     "kvattn_decode_partial": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32,
-                                     _PI32, _PI32, _PI32, _P, _I32, _P, _P, _P, _P, _P]),
+                                     _PI32, _PI32, _PI32, _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_merge_lse": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_resolve_offsets": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
     "kvattn_last_error": (ctypes.c_char_p, []),

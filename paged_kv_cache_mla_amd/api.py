@@ -123,14 +123,15 @@ class Pool:
 
 def decode_partial(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, ctx_lens,
                    tok_begin, part_tokens, seq_dev, max_parts, o_part, lse_part, nparts,
-                   err=None, stream=None):
+                   err=None, stream=None, group_parts=1):
     lib = _lib.load()
     ctx, beg, part = _host_i32(ctx_lens), _host_i32(tok_begin), _host_i32(part_tokens)
     st = lib.kvattn_decode_partial(pool.handle, _dptr(q), int(q_dtype), int(ctx.shape[0]),
                                    int(num_q_heads), ctypes.c_float(scale), _dptr(table_dev),
                                    int(max_blocks), _i32p(ctx), _i32p(beg), _i32p(part),
-                                   _dptr(seq_dev), int(max_parts), _dptr(o_part),
-                                   _dptr(lse_part), _dptr(nparts), _dptr(err), _stream(stream))
+                                   _dptr(seq_dev), int(max_parts), int(group_parts),
+                                   _dptr(o_part), _dptr(lse_part), _dptr(nparts), _dptr(err),
+                                   _stream(stream))
     check(st, "decode_partial")
 
 
@@ -157,11 +158,12 @@ class DecodeStep:
 
     Holds the block table, the per-sequence [ctx_len, tok_begin, part_tokens] rows and the
     partial / output buffers on the device; `run` enqueues decode_partial then merge_lse on
-    the current stream.
+    the current stream.  `group_parts` consecutive partitions are merged on chip into each
+    written partial (1: one partial per partition).
     """
 
     def __init__(self, pool, table, ctx_lens, part_tokens, num_q_heads, head_dim_v,
-                 tok_begin=None, device="cuda"):
+                 tok_begin=None, device="cuda", group_parts=1):
         import torch
         self.pool = pool
         self.ctx = _host_i32(ctx_lens)
@@ -176,7 +178,8 @@ class DecodeStep:
         counts = [partition_count(int(c), int(b), int(p)) for c, b, p in zip(self.ctx, begs, self.part)]
         if min(counts) < 0:
             raise ValueError("invalid partition arguments")
-        self.max_parts = max(1, max(counts))
+        self.group_parts = int(group_parts)
+        self.max_parts = max(1, max(-(-c // self.group_parts) for c in counts))
         self.table_dev = torch.from_numpy(table).to(device)
         self.seq_dev = torch.from_numpy(np.stack([self.ctx, begs, self.part]).astype(np.int32)).to(device)
         f32 = torch.float32
@@ -190,7 +193,7 @@ class DecodeStep:
     def partial(self, q, q_dtype, scale, stream=None):
         decode_partial(self.pool, q, q_dtype, self.hq, scale, self.table_dev, self.max_blocks,
                        self.ctx, self.beg, self.part, self.seq_dev, self.max_parts, self.o_part,
-                       self.lse_part, self.nparts, self.err, stream)
+                       self.lse_part, self.nparts, self.err, stream, self.group_parts)
 
     def merge(self, o_ext=None, lse_ext=None, stream=None):
         merge_lse(self.o_part, self.lse_part, self.nparts, self.batch, self.hq, self.max_parts,

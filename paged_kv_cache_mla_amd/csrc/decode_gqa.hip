@@ -6,20 +6,30 @@
 // Balancing in MoE Inference", §6.1 -- and emits (o normalised by its own sum, lse) so that
 // partials of disjoint token ranges merge exactly (same page, §5.1).
 //
+// Work items are groups of `group_parts` consecutive partitions of one (sequence, KV head);
+// one partial is written per group (with group_parts = 1, one per partition).
+//
 // Two kernels:
-//  * gqa_decode_mfma_kernel (bf16, block size >= 16): one wave per work item.  Each 16-token
-//    tile is a dense contraction on the matrix cores: S^T[16 tok x 16 heads] = K Q^T with
-//    v_mfma_f32_16x16x32_bf16 (query heads of the group in the N columns, padded to 16),
-//    then, per pair of tiles, O^T[D x 16 heads] += V^T P^T, also 16x16x32.  The block layout
-//    makes both operands plain 16-byte / 8-byte per-lane loads straight from HBM: K is stored
-//    in 16-byte chunks with the chunks of consecutive tokens side by side (one k-step of one
-//    tile is 1 KiB contiguous), V is stored transposed (one 16-dim slice of a tile is 512 B
-//    contiguous).  The MFMA output layout of S^T (lane = head column, 4 consecutive tokens per
-//    lane) is exactly the B-operand layout the PV product needs, so no data moves between
-//    lanes except two lane swaps for the per-head max.  The next pair of tiles is prefetched
-//    into registers while the current pair is computed.
-//  * gqa_decode_generic_kernel (fp32 or bf16, any block size): a plain VALU version, one token
-//    per lane, used for fp32 caches and as an independent cross-check of the MFMA kernel.
+//  * gqa_decode_mfma_kernel (bf16, block size >= 16): one workgroup per group, one wave per
+//    partition.  Each 16-token tile is a dense contraction on the matrix cores:
+//    S^T[16 tok x 16 heads] = K Q^T with v_mfma_f32_16x16x32_bf16 (query heads of the group
+//    in the N columns, padded to 16), then, per pair of tiles, O^T[D x 16 heads] += V^T P^T,
+//    also 16x16x32.  The block layout makes both operands plain 16-byte / 8-byte per-lane
+//    loads straight from HBM: K is stored in 16-byte chunks with the chunks of consecutive
+//    tokens side by side (one k-step of one tile is 1 KiB contiguous), V is stored transposed
+//    (one 16-dim slice of a tile is 512 B contiguous).  The MFMA output layout of S^T (lane =
+//    head column, 4 consecutive tokens per lane) is exactly the B-operand layout the PV
+//    product needs, so no data moves between lanes except two lane swaps for the per-head
+//    max.  The next pair of tiles is prefetched into registers while the current pair is
+//    computed.  K and V are read once per step, so their loads carry the non-temporal hint.
+//    The waves' partials (o, lse) go to LDS and are merged there exactly, by the same LSE
+//    rescaling as the merge kernel, before one partial per group is written: writes of
+//    partial outputs are expensive while the read stream is running (on MI355X, 16.9 MB of
+//    partials written next to the 1 GiB of 16 x 32K K/V cost ~16 us, ~8% of the step), and
+//    the group merge divides them by group_parts.
+//  * gqa_decode_generic_kernel (fp32 or bf16, any block size): a plain VALU version, one wave
+//    per group walking its tokens in order, used for fp32 caches and as an independent
+//    cross-check of the MFMA kernel.
 
 #include "device_common.h"
 
@@ -33,6 +43,16 @@ static constexpr float kLn2 = 0.693147180559945309f;
 // the rescale (a pass over every accumulator) happens only a few times per partition.
 static constexpr float kRescaleSlack = 8.f;
 
+// Largest workgroup (waves = partitions merged on chip) of the matrix-core kernel for head
+// dim D: the waves of one group must fit on one CU at the kernel's register use.
+template <int D>
+constexpr int mfma_max_group() { return D <= 64 ? 16 : 8; }
+
+// Partial of one partition [lo, hi) of sequence b for the query heads of KV head kvh, on the
+// calling wave.  On return lane (n, g4) holds, for head n of the group: acc[t] = unnormalised
+// output dims 16t + 4*g4 .. +3, m = reference max (log2 domain), lsum = its share of the
+// normaliser (to be summed over the four lane rows).
+//
 // Tiles are consumed in pairs.  For a pair (A, B) the PV product is one
 // v_mfma_f32_16x16x32_bf16 per 16-dim output tile with k-slot (g4, i) = token 4*g4 + i of A
 // for i < 4 and of B for i >= 4: the A operand is then just the two tiles' 8-byte V^T slices
@@ -40,31 +60,15 @@ static constexpr float kRescaleSlack = 8.f;
 // weights enter as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)), two MFMAs per
 // output tile, so P V is accurate to ~2^-16 relative rather than bf16's 2^-9.
 template <int D, int BSL, int PAIRS>
-__global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, int kvh, int lo,
+                                                   int hi, int lane, f32x4 (&acc)[D / 16],
+                                                   float& m, float& lsum) {
   constexpr int BS = 1 << BSL;
   constexpr int KS = D / 32;       // k-steps of the QK product (32 dims each)
   constexpr int VT = D / 16;       // 16-dim output tiles of the PV product
   constexpr int RING = 2 * PAIRS;  // tiles held in registers
-  const int lane = threadIdx.x;
-  const int n = lane & 15;  // MFMA row / column index
-  const int g4 = lane >> 4; // lane group: k-slot of the operands, row group of the output
-
-  int w = blockIdx.x;
-  const int p = w % a.grid_np;
-  w /= a.grid_np;
-  const int kvh = w % a.hkv;
-  const int b = w / a.hkv;
-
-  int beg, P;
-  const int np = seq_partitions(a, b, &beg, &P);
-  if (p == 0 && kvh == 0 && lane == 0) {
-    a.nparts[b] = np < 0 ? 0 : np;
-    if (np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
-  }
-  if (p >= np) return;  // also covers np < 0
-  const int L = a.seq[b];
-  const int lo = beg + p * P;
-  const int hi = min(L, lo + P);
+  const int n = lane & 15;   // MFMA row / column index
+  const int g4 = lane >> 4;  // lane group: k-slot of the operands, row group of the output
   const int t_lo = lo >> 4;
   const int ntiles = ((hi + 15) >> 4) - t_lo;
 
@@ -97,11 +101,24 @@ __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
   const uint32_t voff = (uint32_t)((((kvh * D + n) << BSL) + 4 * g4) * 2);
   const int64_t kpart_bytes = (int64_t)a.hkv * BS * D * 2;
 
+  // The ring starts zeroed: a slot that is never loaded (partitions shorter than the
+  // prologue) enters the masked PV product as finite zeros, never as stale register bits.
   u32x4 kb[RING][KS];
   u32x2 vb[RING][VT];
   bool vld[RING];
+#pragma unroll
+  for (int s = 0; s < RING; ++s) {
+    vld[s] = false;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kb[s][j] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < VT; ++t) vb[s][t] = u32x2{0u, 0u};
+  }
 
+  // Loads of tile `rel` into ring slot `slot`; nothing is loaded past the partition's last
+  // tile (a wave-uniform skip), so every byte of the partition is fetched exactly once.
   auto issue = [&](int slot, int rel) {
+    if (rel >= ntiles) return;
     const int tok0 = (t_lo + rel) << 4;
     const int blk = tok0 >> BSL;
     const int sub = tok0 & (BS - 1);
@@ -116,17 +133,16 @@ __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
     gchar* vbase = base + kpart_bytes + sub * 2;
 #pragma unroll
     for (int j = 0; j < KS; ++j)
-      kb[slot][j] = *reinterpret_cast<gu32x4*>(kbase + koff + j * (4 * BS * 16));
+      kb[slot][j] = __builtin_nontemporal_load(reinterpret_cast<gu32x4*>(kbase + koff + j * (4 * BS * 16)));
 #pragma unroll
     for (int t = 0; t < VT; ++t)
-      vb[slot][t] = *reinterpret_cast<gu32x2*>(vbase + voff + t * (16 * BS * 2));
+      vb[slot][t] = __builtin_nontemporal_load(reinterpret_cast<gu32x2*>(vbase + voff + t * (16 * BS * 2)));
   };
 
-  f32x4 acc[VT];
 #pragma unroll
   for (int t = 0; t < VT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf;  // reference max of this lane's head (log2 domain)
-  float lsum = 0.f;   // this lane's share of the normaliser
+  m = kNegInf;
+  lsum = 0.f;
   bool bad = false;
   const float scale_log2 = a.scale_log2;
 
@@ -148,10 +164,10 @@ __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
 
   // prologue: the first PAIRS - 1 pairs
 #pragma unroll
-  for (int s = 0; s < RING - 2; ++s) issue(s, min(s, ntiles - 1));
+  for (int s = 0; s < RING - 2; ++s) issue(s, s);
 
-  // Tiles past the end of the partition are computed fully masked (zero weight, max
-  // unchanged), so the loop body has no branches around memory operations.
+  // Tiles past the end of the partition (the tail of the last ring round) are computed fully
+  // masked: zero weight, max unchanged.
   for (int it = 0; it < ntiles; it += RING) {
 #pragma unroll
     for (int ps = 0; ps < PAIRS; ++ps) {
@@ -159,8 +175,8 @@ __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
       const int ra = it + 2 * ps, rb = ra + 1;
       // refill the pair slot consumed last round with the pair RING - 2 tiles ahead
       const int fs = (sa + RING - 2) % RING;
-      issue(fs, min(ra + RING - 2, ntiles - 1));
-      issue(fs + 1, min(ra + RING - 1, ntiles - 1));
+      issue(fs, ra + RING - 2);
+      issue(fs + 1, ra + RING - 1);
       float sva[4], svb[4];
       scores(sa, ra, sva);
       scores(sb, rb, svb);
@@ -200,17 +216,91 @@ __global__ __launch_bounds__(64) void gqa_decode_mfma_kernel(DecodeArgs a) {
     }
   }
   if (bad) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+}
 
+// One workgroup of group_parts waves per (sequence, KV head, group of partitions).  Dynamic
+// LDS (group_parts > 1 only): [group_parts][group][D] partial outputs, then
+// [group_parts][group] lse values (log2 domain).
+template <int D, int BSL, int PAIRS>
+__global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kernel(DecodeArgs a) {
+  constexpr int VT = D / 16;
+  extern __shared__ float smem[];
+  const int G = a.group_parts;
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+
+  int w = blockIdx.x;
+  const int k = w % a.grid_ng;
+  w /= a.grid_ng;
+  const int kvh = w % a.hkv;
+  const int b = w / a.hkv;
+
+  int beg, P, ng;
+  const int np = seq_partitions(a, b, &beg, &P, &ng);
+  if (k == 0 && kvh == 0 && threadIdx.x == 0) {
+    a.nparts[b] = ng < 0 ? 0 : ng;
+    if (np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+  }
+  if (k >= ng) return;  // uniform over the workgroup; also covers ng < 0
+  const int p = k * G + wv;
+  const int L = a.seq[b];
+
+  f32x4 acc[VT];
+  float m = kNegInf, lsum = 0.f;
+  if (p < np) {  // uniform over the wave: waves past the sequence's last partition idle
+    const int lo = beg + p * P;
+    gqa_partition_mfma<D, BSL, PAIRS>(a, b, kvh, lo, min(L, lo + P), lane, acc, m, lsum);
+  }
   lsum = rows_sum(lsum);
-  if (n < a.group) {
-    const int h = kvh * a.group + n;
-    const int64_t row = ((int64_t)b * a.hq + h) * a.max_parts + p;
-    const float inv = 1.f / lsum;
-    float* op = a.o_part + row * D;
+  const int grp = a.group;
+
+  if (G == 1) {  // the wave's partial is the group's partial
+    if (n < grp) {
+      const int64_t row = ((int64_t)b * a.hq + kvh * grp + n) * a.max_parts + k;
+      const float inv = 1.f / lsum;
+      float* op = a.o_part + row * D;
 #pragma unroll
-    for (int t = 0; t < VT; ++t)
-      *reinterpret_cast<f32x4*>(op + 16 * t + 4 * g4) = acc[t] * inv;
-    if (g4 == 0) a.lse_part[row] = (m + log2f(lsum)) * kLn2;
+      for (int t = 0; t < VT; ++t)
+        *reinterpret_cast<f32x4*>(op + 16 * t + 4 * g4) = acc[t] * inv;
+      if (g4 == 0) a.lse_part[row] = (m + log2f(lsum)) * kLn2;
+    }
+    return;
+  }
+
+  // Exact LSE merge of the group's partials in LDS:
+  //   M = max_w lse_w, s = sum_w 2^(lse_w - M), o = sum_w 2^(lse_w - M) o_w / s.
+  float* so = smem;                  // [G][grp][D]
+  float* sl = smem + G * grp * D;    // [G][grp]
+  if (n < grp) {
+    if (p < np) {
+      const float inv = 1.f / lsum;
+      float* op = so + (wv * grp + n) * D;
+#pragma unroll
+      for (int t = 0; t < VT; ++t)
+        *reinterpret_cast<f32x4*>(op + 16 * t + 4 * g4) = acc[t] * inv;
+    }
+    if (g4 == 0) sl[wv * grp + n] = p < np ? m + log2f(lsum) : kNegInf;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < grp * D; idx += 64 * G) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float mx = kNegInf;
+    for (int u = 0; u < G; ++u) mx = fmaxf(mx, sl[u * grp + h]);
+    float s = 0.f, o = 0.f;
+    for (int u = 0; u < G; ++u) {
+      const float l = sl[u * grp + h];
+      if (l != kNegInf) {  // idle waves wrote no output
+        const float e = exp2f(l - mx);
+        s += e;
+        o += e * so[(u * grp + h) * D + d];
+      }
+    }
+    const int64_t row = ((int64_t)b * a.hq + kvh * grp + h) * a.max_parts + k;
+    a.o_part[row * D + d] = o / s;
+    if (d == 0) a.lse_part[row] = (mx + log2f(s)) * kLn2;
   }
 }
 
@@ -223,7 +313,9 @@ __device__ __forceinline__ float load_elem(const char* p) {
   }
 }
 
-// Plain VALU version: one token per lane for the scores, lanes over dims for P V.
+// Plain VALU version: one token per lane for the scores, lanes over dims for P V.  One wave
+// per (sequence, KV head, group of partitions) walks the group's tokens in order; the online
+// softmax simply continues across the partition boundaries inside the group.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   constexpr int R = D / 64;                // dims per lane in the output
@@ -232,21 +324,22 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
 
   int w = blockIdx.x;
-  const int p = w % a.grid_np;
-  w /= a.grid_np;
+  const int k = w % a.grid_ng;
+  w /= a.grid_ng;
   const int kvh = w % a.hkv;
   const int b = w / a.hkv;
 
-  int beg, P;
-  const int np = seq_partitions(a, b, &beg, &P);
-  if (p == 0 && kvh == 0 && lane == 0) {
-    a.nparts[b] = np < 0 ? 0 : np;
+  int beg, P, ng;
+  const int np = seq_partitions(a, b, &beg, &P, &ng);
+  if (k == 0 && kvh == 0 && lane == 0) {
+    a.nparts[b] = ng < 0 ? 0 : ng;
     if (np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
   }
-  if (p >= np) return;
+  if (k >= ng) return;
   const int L = a.seq[b];
-  const int lo = beg + p * P;
-  const int hi = min(L, lo + P);
+  const int64_t span = (int64_t)P * a.group_parts;
+  const int lo = (int)(beg + k * span);
+  const int hi = (int)min((int64_t)L, lo + span);
   const int G = a.group;
 
   for (int h = 0; h < G; ++h) {
@@ -328,7 +421,7 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
 #pragma unroll
   for (int h = 0; h < 16; ++h) {
     if (h >= G) continue;
-    const int64_t row = ((int64_t)b * a.hq + kvh * G + h) * a.max_parts + p;
+    const int64_t row = ((int64_t)b * a.hq + kvh * G + h) * a.max_parts + k;
     float* op = a.o_part + row * D;
 #pragma unroll
     for (int r = 0; r < R; ++r) op[lane + 64 * r] = acc[h][r] / l[h];
@@ -337,30 +430,45 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ launchers
+int gqa_mfma_max_group(int d) {
+  switch (d) {
+    case 64: return mfma_max_group<64>();
+    case 128: return mfma_max_group<128>();
+    case 256: return mfma_max_group<256>();
+    default: return 0;
+  }
+}
+
 template <int D, int BSL>
-static hipError_t launch_mfma_db(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t launch_mfma_db(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   constexpr int PAIRS = D <= 128 ? 2 : 1;  // tile pairs held in registers
-  hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS>), grid, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS>), grid, dim3(64 * a.group_parts),
+                     lds, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_mfma_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t launch_mfma_d(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   switch (a.bs_shift) {
-    case 4: return launch_mfma_db<D, 4>(a, grid, st);
-    case 5: return launch_mfma_db<D, 5>(a, grid, st);
-    case 6: return launch_mfma_db<D, 6>(a, grid, st);
-    case 7: return launch_mfma_db<D, 7>(a, grid, st);
-    case 8: return launch_mfma_db<D, 8>(a, grid, st);
+    case 4: return launch_mfma_db<D, 4>(a, grid, lds, st);
+    case 5: return launch_mfma_db<D, 5>(a, grid, lds, st);
+    case 6: return launch_mfma_db<D, 6>(a, grid, lds, st);
+    case 7: return launch_mfma_db<D, 7>(a, grid, lds, st);
+    case 8: return launch_mfma_db<D, 8>(a, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
 
+size_t gqa_mfma_lds_bytes(int group_parts, int group, int d) {
+  return group_parts > 1 ? (size_t)group_parts * group * (d + 1) * sizeof(float) : 0;
+}
+
 hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {
+  const size_t lds = gqa_mfma_lds_bytes(a.group_parts, a.group, d);
   switch (d) {
-    case 64: return launch_mfma_d<64>(a, grid, st);
-    case 128: return launch_mfma_d<128>(a, grid, st);
-    case 256: return launch_mfma_d<256>(a, grid, st);
+    case 64: return launch_mfma_d<64>(a, grid, lds, st);
+    case 128: return launch_mfma_d<128>(a, grid, lds, st);
+    case 256: return launch_mfma_d<256>(a, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -8,8 +8,9 @@
 // in MoE Inference", §6.1, compressed-MLA variant).  Here that reuse is staged in LDS:
 //
 //   one workgroup of 4 waves per (sequence, partition); per 64-token block
-//   1. the block's 72 KiB latent is fetched with fully coalesced 16-byte loads (prefetched
-//      one block ahead in registers) and written to LDS with an XOR swizzle
+//   1. the block's 72 KiB latent is fetched with fully coalesced 16-byte non-temporal loads
+//      (read once per step; prefetched one block ahead in registers) and written to LDS with
+//      an XOR swizzle
 //      (slot(c, t) = c*64 + (t ^ (c & 15)) for 16-byte chunk c of token t);
 //   2. wave w scores tokens 16w..16w+15 against all 16 heads on the matrix cores,
 //      S^T = C Q^T with v_mfma_f32_16x16x32_bf16 (18 k-steps over 576 dims), and posts the
@@ -46,18 +47,21 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
   const int n = lane & 15;
   const int g4 = lane >> 4;
 
-  const int p = blockIdx.x % a.grid_np;
-  const int b = blockIdx.x / a.grid_np;
-  int beg, P;
-  const int np = seq_partitions(a, b, &beg, &P);
-  if (p == 0 && tid == 0) {
-    a.nparts[b] = np < 0 ? 0 : np;
+  // one workgroup per (sequence, group of group_parts partitions); the group's partitions
+  // are walked in order, the online softmax continuing across their boundaries
+  const int k = blockIdx.x % a.grid_ng;
+  const int b = blockIdx.x / a.grid_ng;
+  int beg, P, ng;
+  const int np = seq_partitions(a, b, &beg, &P, &ng);
+  if (k == 0 && tid == 0) {
+    a.nparts[b] = ng < 0 ? 0 : ng;
     if (np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
   }
-  if (p >= np) return;
+  if (k >= ng) return;
   const int L = a.seq[b];
-  const int lo = beg + p * P;
-  const int hi = min(L, lo + P);
+  const int64_t span = (int64_t)P * a.group_parts;
+  const int lo = (int)(beg + k * span);
+  const int hi = (int)min((int64_t)L, lo + span);
   const int st_lo = lo >> 6;
   const int nst = ((hi + kMlaBs - 1) >> 6) - st_lo;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
@@ -81,9 +85,10 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
   auto fetch = [&](int st_rel) {
     const int32_t pid = trow[st_lo + st_rel];
     vld_next = valid_block(a.rt, pid);
-    const uint4* src = reinterpret_cast<const uint4*>(block_ptr(a.rt, pid));
+    gu32x4* src = reinterpret_cast<gu32x4*>(block_addr(a.rt, vld_next ? pid : 0));
 #pragma unroll
-    for (int r = 0; r < kMlaLoads; ++r) stage[r] = src[r * 256 + tid];
+    for (int r = 0; r < kMlaLoads; ++r)
+      stage[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(src + r * 256 + tid));
   };
 
   f32x4 acc[8];
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
       const int q = r * 256 + tid;  // chunk q / 64, token q % 64
       lat[lat_slot(q >> 6, q & 63)] = stage[r];
     }
-    fetch(min(s + 1, nst - 1));
+    if (s + 1 < nst) fetch(s + 1);  // nothing is fetched past the partition
     __syncthreads();  // latent of this stage visible
 
     // 2. scores of tokens 16*wv .. +15
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (n < a.hq) {
-    const int64_t row = ((int64_t)b * a.hq + n) * a.max_parts + p;
+    const int64_t row = ((int64_t)b * a.hq + n) * a.max_parts + k;
     const float inv = 1.f / lsum;
     float* op = a.o_part + row * kMlaDv;
 #pragma unroll

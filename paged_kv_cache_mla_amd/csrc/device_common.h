@@ -32,7 +32,9 @@ struct DecodeArgs {
   int32_t* nparts;         // [B]
   int32_t* err;            // nullable
   int32_t batch, hq, hkv, group;
-  int32_t max_blocks, max_parts, grid_np;
+  int32_t max_blocks, max_parts;
+  int32_t group_parts;     // consecutive partitions merged on chip into one written partial
+  int32_t grid_ng;         // work items per (sequence, KV head): the largest group count
   int32_t bs, bs_shift;
   float scale;             // softmax scale
   float scale_log2;        // scale * log2(e)
@@ -94,20 +96,24 @@ __device__ __forceinline__ void flag_error(int32_t* err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }
 
-// Partition count of sequence b from the device copy of the per-sequence values; returns
-// 0 (and flags KVATTN_ERR_BAD_SEQ) if they are inconsistent with the launch.
-__device__ __forceinline__ int seq_partitions(const DecodeArgs& a, int b, int* lo_tok,
-                                              int* part) {
+// Partition count of sequence b from the device copy of the per-sequence values, and in *ng
+// the number of partials written for it, ceil(np / group_parts).  Returns -1 (and *ng = -1)
+// if the values are inconsistent with the launch.
+__device__ __forceinline__ int seq_partitions(const DecodeArgs& a, int b, int* lo_tok, int* part,
+                                              int* ng) {
   const int L = a.seq[b];
   const int beg = a.seq[a.batch + b];
   const int P = a.seq[2 * a.batch + b];
   *lo_tok = beg;
   *part = P;
+  *ng = -1;
   const bool ok = beg >= 0 && beg <= L && (int64_t)L <= ((int64_t)a.max_blocks << a.bs_shift) &&
                   P > 0 && (P & (a.bs - 1)) == 0;
   if (!ok) return -1;
   const int np = (int)(((int64_t)L - beg + P - 1) / P);
-  if (np > a.max_parts || np > a.grid_np) return -1;
+  const int groups = (np + a.group_parts - 1) / a.group_parts;
+  if (groups > a.max_parts || groups > a.grid_ng) return -1;
+  *ng = groups;
   return np;
 }
 

@@ -10,6 +10,8 @@
 namespace kvattn {
 
 hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, dim3 grid, hipStream_t st);
+int gqa_mfma_max_group(int d);
+size_t gqa_mfma_lds_bytes(int group_parts, int group, int d);
 hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, hipStream_t st);
 hipError_t launch_mla(const DecodeArgs& a, dim3 grid, hipStream_t st);
 
@@ -60,14 +62,17 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
                                     const int32_t* table_dev, int32_t max_blocks,
                                     const int32_t* ctx_lens, const int32_t* tok_begin,
                                     const int32_t* part_tokens, const int32_t* seq_dev,
-                                    int32_t max_parts, float* o_part, float* lse_part,
-                                    int32_t* nparts_dev, int32_t* err_dev, void* hip_stream) {
+                                    int32_t max_parts, int32_t group_parts, float* o_part,
+                                    float* lse_part, int32_t* nparts_dev, int32_t* err_dev,
+                                    void* hip_stream) {
   clear_error();
   if (!pool || !q || !table_dev || !ctx_lens || !part_tokens || !seq_dev || !o_part ||
       !lse_part || !nparts_dev)
     return set_error(KVATTN_E_INVAL, "decode_partial: null argument");
   if (batch < 1 || num_q_heads < 1 || max_blocks < 1 || max_parts < 1)
     return set_error(KVATTN_E_INVAL, "decode_partial: batch, heads, max_blocks and max_parts must be >= 1");
+  if (group_parts < 1 || group_parts > KVATTN_MAX_GROUP_PARTS)
+    return set_error(KVATTN_E_INVAL, "decode_partial: group_parts must be in [1, KVATTN_MAX_GROUP_PARTS]");
   if (!std::isfinite(scale)) return set_error(KVATTN_E_INVAL, "decode_partial: scale must be finite");
   if (!aligned16(q) || !aligned16(o_part))
     return set_error(KVATTN_E_INVAL, "decode_partial: q and o_part must be 16-byte aligned");
@@ -98,10 +103,21 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
     // the matrix-core kernel keeps a partition's block ids in two 64-lane registers
     for (int b = 0; b < batch && kind == K_MFMA; ++b)
       if (part_tokens[b] > 0 && part_tokens[b] / bs + 1 > 128) kind = K_GENERIC;
+    if (kind == K_MFMA && group_parts > 1) {
+      // one wave per partition of a group, the group's partials merged in LDS
+      if (group_parts > gqa_mfma_max_group(d))
+        return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: group_parts above " +
+                                                   std::to_string(gqa_mfma_max_group(d)) +
+                                                   " for head dim " + std::to_string(d));
+      if (gqa_mfma_lds_bytes(group_parts, group, d) > 65536)
+        return set_error(KVATTN_E_UNSUPPORTED,
+                         "decode_partial: group_parts x heads per KV head x (head dim + 1) x 4 "
+                         "bytes exceeds 64 KiB");
+    }
   }
 
   // per-sequence checks and grid size
-  int max_np = 0;
+  int max_ng = 0;  // most partials any sequence writes
   for (int b = 0; b < batch; ++b) {
     const int len = ctx_lens[b];
     const int beg = tok_begin ? tok_begin[b] : 0;
@@ -112,15 +128,16 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
     if (P <= 0 || P % bs != 0)
       return set_error(KVATTN_E_INVAL, "decode_partial: part_tokens must be a positive multiple of block_size");
     const int np = kvattn_partition_count(len, beg, P);
-    if (np > max_parts)
+    const int ng = (np + group_parts - 1) / group_parts;
+    if (ng > max_parts)
       return set_error(KVATTN_E_INVAL, "decode_partial: sequence " + std::to_string(b) +
-                                           " has more partitions than max_parts");
-    if (np > max_np) max_np = np;
+                                           " writes more partials than max_parts");
+    if (ng > max_ng) max_ng = ng;
   }
-  if (max_np > 0 && pool->total_blocks == 0)
+  if (max_ng > 0 && pool->total_blocks == 0)
     return set_error(KVATTN_E_INVAL, "decode_partial: the pool holds no blocks");
-  const int grid_np = max_np > 0 ? max_np : 1;
-  const int64_t items = (int64_t)batch * (kind == K_MLA ? 1 : hkv) * grid_np;
+  const int grid_ng = max_ng > 0 ? max_ng : 1;
+  const int64_t items = (int64_t)batch * (kind == K_MLA ? 1 : hkv) * grid_ng;
   if (items > INT32_MAX) return set_error(KVATTN_E_INVAL, "decode_partial: launch too large");
 
   DecodeArgs a{};
@@ -138,7 +155,8 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
   a.group = group;
   a.max_blocks = max_blocks;
   a.max_parts = max_parts;
-  a.grid_np = grid_np;
+  a.grid_ng = grid_ng;
+  a.group_parts = group_parts;
   a.bs = bs;
   a.bs_shift = log2_exact(bs);
   a.scale = scale;

@@ -4,13 +4,17 @@
 // §4.2 and §5.1-5.2: the engines' partial outputs merge exactly by log-sum-exp rescaling,
 // one join per step, performed on the GPU; the other engine ships only its partial output
 // and normaliser.  For each (sequence, head):
-//     M = max_p lse_p,  lse = M + ln sum_p exp(lse_p - M),  o = sum_p exp(lse_p - lse) o_p.
+//     M = max_p lse_p,  T = sum_p exp(lse_p - M),  lse = M + ln T,
+//     o = sum_p exp(lse_p - M) o_p / T        (= sum_p exp(lse_p - lse) o_p).
 //
-// One 256-thread workgroup per (sequence, head).  The partition weights exp(lse_p - lse)
-// are computed once (block-wide max and sum) into LDS; then thread (g, c) of a
-// [groups x dv/4] arrangement sums 16-byte columns c of partitions p = g, g + groups, ...,
-// and the groups are reduced through LDS.  Partitions are processed in chunks of kChunk so
-// any partition count works with a fixed LDS footprint.
+// One 256-thread workgroup per (sequence, head).  Thread (g, c) of a [groups x dv/4]
+// arrangement owns 16-byte column c of partitions g, g + groups, ...  The merge is bound by
+// the latency of a few dependent steps, not by bandwidth, so the order is: issue the loads of
+// the thread's first kR partial columns and of the first lse values at once, before the
+// partition count is known (bounded by max_parts), then take the block max, write the weights
+// to LDS while summing them, and only then consume the partial columns already in registers.
+// Partitions beyond kR * groups (long sequences, wide heads) are handled by a second, plain
+// loop.  Every sum runs in a fixed order, so the result is bitwise reproducible.
 
 #include "device_common.h"
 
@@ -18,7 +22,8 @@ namespace kvattn {
 
 static constexpr float kNegInfG = -__builtin_huge_valf();
 static constexpr int kThreads = 256;
-static constexpr int kChunk = 1024;
+static constexpr int kWts = 2048;  // partitions whose weights are kept in LDS
+static constexpr int kR = 16;      // partial columns per thread held in registers
 
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
@@ -39,55 +44,69 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 __global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
-  __shared__ float wts[kChunk];
+  __shared__ float wts[kWts];
   __shared__ f32x4 part[kThreads];
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;  // b * Hq + h
   const int b = (int)(row / a.hq);
-  int np = a.nparts[b];
-  np = np < 0 ? 0 : (np > a.max_parts ? a.max_parts : np);
+  const int np_raw = a.nparts[b];
   const float* lrow = a.lse_part + row * a.max_parts;
   const bool ext = a.o_ext != nullptr;
   const float lx = ext ? a.lse_ext[row] : kNegInfG;
 
-  // M = max over partitions (and the external partial)
-  float mx = lx;
-  for (int p = tid; p < np; p += kThreads) mx = fmaxf(mx, lrow[p]);
-  const float big = block_max(mx, red);
   const int cols = a.dv >> 2;
-  const int groups = kThreads / cols;       // >= 1 since dv <= 1024
+  const int groups = kThreads / cols;  // >= 1 since dv <= 1024
   const int g = tid / cols;
   const int c = tid - g * cols;
   const bool active = g < groups;
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.o_part + row * a.max_parts * a.dv);
+
+  // 1. loads issued before the partition count arrives: the partial columns of the first
+  //    kR * groups partition slots and the first 256 lse slots, bounded by max_parts (slots
+  //    past the sequence's count hold stale data and are discarded by selection below)
+  f32x4 ov[kR];
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    const int p = g + k * groups;
+    ov[k] = (active && p < a.max_parts) ? orow[(int64_t)p * cols + c] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float l0 = tid < a.max_parts ? lrow[tid] : kNegInfG;
+  const int np = np_raw < 0 ? 0 : (np_raw > a.max_parts ? a.max_parts : np_raw);
+
+  // 2. M = max over partitions (and the external partial)
+  float mx = lx;
+  if (tid < np) mx = fmaxf(mx, l0);
+  for (int p = tid + kThreads; p < np; p += kThreads) mx = fmaxf(mx, lrow[p]);
+  const float big = block_max(mx, red);
   f32x4* orow_out = reinterpret_cast<f32x4*>(a.o_out + row * a.dv);
-  if (big == kNegInfG) {  // nothing of positive weight
+  if (big == kNegInfG) {  // nothing of positive weight (uniform across the block)
     if (tid < cols) orow_out[tid] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (a.lse_out && tid == 0) a.lse_out[row] = kNegInfG;
     return;
   }
-  float sm = (ext && tid == 0) ? expf(lx - big) : 0.f;
-  for (int p = tid; p < np; p += kThreads) sm += expf(lrow[p] - big);
-  const float tot = block_sum(sm, red);
-  const float lse = big + logf(tot);
 
-  const f32x4* orow = reinterpret_cast<const f32x4*>(a.o_part + row * a.max_parts * a.dv);
+  // 3. weights exp(lse_p - M) into LDS, T = their sum (+ the external weight)
+  const float wx = ext ? expf(lx - big) : 0.f;
+  float sm = tid == 0 ? wx : 0.f;
+  for (int p = tid; p < np; p += kThreads) {
+    const float w = expf((p == tid ? l0 : lrow[p]) - big);
+    sm += w;
+    if (p < kWts) wts[p] = w;
+  }
+  const float tot = block_sum(sm, red);  // its barriers also publish wts
+
+  // 4. weighted sum of the partial columns
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < np; p0 += kChunk) {
-    const int n = min(kChunk, np - p0);
-    __syncthreads();  // previous chunk's weights consumed
-    for (int p = tid; p < n; p += kThreads) wts[p] = expf(lrow[p0 + p] - lse);
-    __syncthreads();
-    if (active) {
-      int p = g;
-      for (; p + 3 * groups < n; p += 4 * groups) {
-        const f32x4 v0 = orow[(int64_t)(p0 + p) * cols + c];
-        const f32x4 v1 = orow[(int64_t)(p0 + p + groups) * cols + c];
-        const f32x4 v2 = orow[(int64_t)(p0 + p + 2 * groups) * cols + c];
-        const f32x4 v3 = orow[(int64_t)(p0 + p + 3 * groups) * cols + c];
-        acc += v0 * wts[p] + v1 * wts[p + groups] + v2 * wts[p + 2 * groups] + v3 * wts[p + 3 * groups];
-      }
-      for (; p < n; p += groups) acc += orow[(int64_t)(p0 + p) * cols + c] * wts[p];
+  if (active) {
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int p = g + k * groups;
+      if (p < np) acc += ov[k] * wts[p];  // a select: stale slots never enter the sum
+    }
+    for (int p = g + kR * groups; p < np; p += groups) {
+      const float w = p < kWts ? wts[p] : expf(lrow[p] - big);
+      acc += orow[(int64_t)p * cols + c] * w;
     }
   }
   part[tid] = acc;
@@ -95,10 +114,10 @@ __global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
   if (tid < cols) {
     f32x4 o = part[tid];
     for (int k = 1; k < groups; ++k) o += part[k * cols + tid];
-    if (ext) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[tid] * expf(lx - lse);
-    orow_out[tid] = o;
+    if (ext) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[tid] * wx;
+    orow_out[tid] = o * (1.f / tot);
   }
-  if (a.lse_out && tid == 0) a.lse_out[row] = lse;
+  if (a.lse_out && tid == 0) a.lse_out[row] = big + logf(tot);
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {

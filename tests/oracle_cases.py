@@ -75,3 +75,20 @@ def out_tol(case):
 
 def lse_tol(case):
     return F32_ABS_TOL if case.dtype == "f32" else LSE_ABS_TOL
+
+
+def grouped_partials(case, group_parts, seqs=None):
+    """The partials a decode step writes when `group_parts` consecutive partitions are merged
+    into one: the oracle's merge of each group's per-partition partials.  List over the
+    sequences of (o [ngroups, Hq, Dv], lse [ngroups, Hq])."""
+    out = []
+    for po, pl in device_partials(case, seqs):
+        n = po.shape[0]
+        os_, ls_ = [], []
+        for g0 in range(0, n, group_parts):
+            o, l = oracle.merge(list(po[g0:g0 + group_parts]), list(pl[g0:g0 + group_parts]))
+            os_.append(o)
+            ls_.append(l)
+        hq, dv = po.shape[1], po.shape[2]
+        out.append((np.array(os_).reshape(len(os_), hq, dv), np.array(ls_).reshape(len(ls_), hq)))
+    return out

@@ -190,7 +190,7 @@ def test_partition_count_matches_oracle():
 def _decode_call(lib, pool, **over):
     args = dict(q=FAKE, q_dtype=_lib.BF16, batch=2, hq=8, scale=0.1, table=FAKE, max_blocks=4,
                 ctx=[64, 50], beg=None, part=[32, 32], seq=FAKE, max_parts=2, o=FAKE, lse=FAKE,
-                nparts=FAKE, err=None)
+                nparts=FAKE, err=None, group_parts=1)
     args.update(over)
     arr = lambda v: None if v is None else np.ascontiguousarray(np.asarray(v, np.int32))  # noqa: E731
     ctx, beg, part = arr(args["ctx"]), arr(args["beg"]), arr(args["part"])
@@ -199,8 +199,9 @@ def _decode_call(lib, pool, **over):
     return lib.kvattn_decode_partial(pool.handle, vp(args["q"]), args["q_dtype"], args["batch"],
                                      args["hq"], ctypes.c_float(args["scale"]), vp(args["table"]),
                                      args["max_blocks"], p32(ctx), p32(beg), p32(part),
-                                     vp(args["seq"]), args["max_parts"], vp(args["o"]),
-                                     vp(args["lse"]), vp(args["nparts"]), vp(args["err"]), None)
+                                     vp(args["seq"]), args["max_parts"], args["group_parts"],
+                                     vp(args["o"]), vp(args["lse"]), vp(args["nparts"]),
+                                     vp(args["err"]), None)
 
 
 def test_decode_partial_validation_without_gpu(lib):
@@ -218,6 +219,13 @@ def test_decode_partial_validation_without_gpu(lib):
     assert _decode_call(lib, pool, max_parts=1) == _lib.E_INVAL             # 2 partitions needed
     assert _decode_call(lib, pool, scale=float("nan")) == _lib.E_INVAL
     assert _decode_call(lib, pool, batch=0) == _lib.E_INVAL
+    assert _decode_call(lib, pool, group_parts=0) == _lib.E_INVAL
+    assert _decode_call(lib, pool, group_parts=17) == _lib.E_INVAL          # > KVATTN_MAX_GROUP_PARTS
+    p128 = _pool(8, 0, bs=16, hkv=2, d=128)
+    assert _decode_call(lib, p128, group_parts=9) == _lib.E_UNSUPPORTED     # > 8 waves at d 128
+    p256 = _pool(8, 0, bs=16, hkv=2, d=256)
+    assert _decode_call(lib, p256, hq=32, group_parts=8) == _lib.E_UNSUPPORTED  # LDS > 64 KiB
+    assert "64 KiB" in lib.kvattn_last_error().decode()
     pool3 = _pool(8, 0, bs=16, hkv=2, d=96)
     assert _decode_call(lib, pool3) == _lib.E_UNSUPPORTED                   # d 96 has no kernel
     mla = _pool(8, 0, bs=32, hkv=1, d=576, latent=False)

@@ -35,9 +35,9 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-def _run(case, ext=None):
+def _run(case, ext=None, group_parts=1):
     from paged_kv_cache_mla_amd.session import DeviceCase
-    dc = DeviceCase(case)
+    dc = DeviceCase(case, group_parts=group_parts)
     o_ext = lse_ext = None
     if ext is not None:
         o_ext = torch.from_numpy(ext[0].astype(np.float32)).cuda()
@@ -47,14 +47,15 @@ def _run(case, ext=None):
     return dc, o.cpu().numpy(), lse.cpu().numpy()
 
 
-def _check_partials(case, dc, seqs=None):
-    parts = oc.device_partials(case, seqs)
+def _check_partials(case, dc, seqs=None, group_parts=1):
+    parts = oc.grouped_partials(case, group_parts, seqs)
     nparts = dc.step.nparts.cpu().numpy()
     o_part = dc.step.o_part.cpu().numpy()
     l_part = dc.step.lse_part.cpu().numpy()
     for idx, b in enumerate(range(case.batch) if seqs is None else seqs):
         beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
-        assert nparts[b] == oracle.partition_count(int(case.ctx_lens[b]), beg, int(case.part_tokens[b]))
+        count = oracle.partition_count(int(case.ctx_lens[b]), beg, int(case.part_tokens[b]))
+        assert nparts[b] == -(-count // group_parts)
         po, pl = parts[idx]
         n = po.shape[0]
         if n == 0:
@@ -81,6 +82,28 @@ def test_small_workload_matches_oracle(name):
     assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
     assert int(dc.step.err.item()) == 0
     _check_partials(case, dc)
+
+
+GROUPED = [("gqa_32k", 2), ("gqa_32k", 3), ("gqa_32k", 8), ("prefix_shared", 4),
+           ("prefix_shared", 7), ("split_128k", 4), ("mla_16k", 3), ("tiny_fp32", 2)]
+
+
+@pytest.mark.parametrize("name,group_parts", GROUPED, ids=[f"{n}-g{g}" for n, g in GROUPED])
+def test_grouped_partials_match_oracle(name, group_parts):
+    """Partials of group_parts consecutive partitions merged on chip (one wave per partition
+    and an LDS merge in the matrix-core kernel; an in-order walk elsewhere) equal the oracle's
+    merge of those partitions' partials; the final output is unchanged."""
+    case = make_case(name, "small")
+    _say(f"[grouped] {name} group_parts={group_parts}")
+    ext = oc.external_partial(case) if case.ext_regions is not None else None
+    dc, o, lse = _run(case, ext, group_parts)
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    _say(f"[grouped] {name} g{group_parts}: out error {err:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc, group_parts=group_parts)
 
 
 @pytest.mark.parametrize("name", ["gqa_32k", "prefix_shared", "split_128k"])
@@ -203,16 +226,20 @@ FULL = [("gqa_32k", {}, [0, 7, 15]), ("mla_16k", {}, [0, 31]),
 
 @pytest.mark.parametrize("name,kw,seqs", FULL, ids=[f"{n}-{k.get('r', '')}" for n, k, _ in FULL])
 def test_full_size_sampled_sequences(name, kw, seqs):
-    _say(f"[full] generating {name} {kw}")
+    """Full-size workloads in the launch configuration bench.py times (its group_parts)."""
+    from bench import GROUP_PARTS
+    group_parts = GROUP_PARTS[name]
+    _say(f"[full] generating {name} {kw} group_parts={group_parts}")
     case = make_case(name, "full", **kw)
     ext = oc.external_partial(case, seqs) if case.ext_regions is not None else None
     _say(f"[full] running {name} B={case.batch} device tokens={case.device_tokens()}")
-    dc, o, lse = _run(case, ext)
+    dc, o, lse = _run(case, ext, group_parts)
     assert int(dc.step.err.item()) == 0
     nparts = dc.step.nparts.cpu().numpy()
     for b in range(case.batch):
         beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
-        assert nparts[b] == oracle.partition_count(int(case.ctx_lens[b]), beg, int(case.part_tokens[b]))
+        count = oracle.partition_count(int(case.ctx_lens[b]), beg, int(case.part_tokens[b]))
+        assert nparts[b] == -(-count // group_parts)
     o_ref, lse_ref = oc.full_reference(case, seqs)
     err = oc.out_error(case, o[seqs], o_ref[seqs])
     _say(f"[full] {name} {kw} sampled seqs {seqs}: out error {err:.3e}")
