@@ -186,9 +186,11 @@ int32_t kvattn_partition_count(int32_t ctx_len, int32_t tok_begin, int32_t part_
  * KV head; MLA: all heads share the latent) one partial is written:
  *     o_part[b][h][k][:] = sum_t w_t V(t) / sum_t w_t,  w_t = exp(s_t - max s),
  *     s_t = scale * q[b][h] . K(t),      lse_part[b][h][k] = max s + ln(sum_t w_t)
- * over the group's tokens t.  The matrix-core GQA kernel computes each partition of a group
- * on its own wave and merges the group's partials on chip, exactly, by the LSE rescaling of
- * kvattn_merge_lse; the other kernels walk the group's tokens in order.  group_parts = 1
+ * over the group's tokens t.  The matrix-core GQA kernel spreads a group's partitions over
+ * the waves of one workgroup (two consecutive partitions per wave when group_parts is even
+ * and at least 4 and two partitions span at most 127 blocks, else one) and merges the waves'
+ * partials on chip, exactly, by the LSE rescaling of kvattn_merge_lse; the other kernels
+ * walk the group's tokens in order.  group_parts = 1
  * writes one partial per partition; larger groups write fewer partials, which is faster on
  * long contexts (partial writes compete with the K/V read stream).  Logical token t of
  * sequence b lives at offset t % bs of physical block table_dev[b][t / bs].
@@ -214,8 +216,9 @@ int32_t kvattn_partition_count(int32_t ctx_len, int32_t tok_begin, int32_t part_
  * partials per sequence <= max_parts, group_parts outside [1, KVATTN_MAX_GROUP_PARTS].
  * E_UNSUPPORTED: q_dtype != kv_dtype, or a head / dim combination without a kernel (GQA:
  * Dk = Dv in {64, 128, 256}, Hq / Hkv <= 16; MLA: BF16, Dk = 576, Dv = 512, Hq <= 16,
- * bs = 64); for the bf16 GQA kernel (block size >= 16) also group_parts above 16 (Dk 64) or
- * 8 (Dk 128, 256), or group_parts * (Hq / Hkv) * (Dk + 1) * 4 > 65536.  E_HIP: launch failure.
+ * bs = 64); for the bf16 GQA kernel (block size >= 16) also a group needing more than 16
+ * waves (Dk 64) or 8 waves (Dk 128, 256), or waves * (Hq / Hkv) * (Dk + 1) * 4 > 65536 bytes
+ * of LDS.  E_HIP: launch failure.
  */
 kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int32_t q_dtype,
                                     int32_t batch, int32_t num_q_heads, float scale,

@@ -10,8 +10,8 @@
 // one partial is written per group (with group_parts = 1, one per partition).
 //
 // Two kernels:
-//  * gqa_decode_mfma_kernel (bf16, block size >= 16): one workgroup per group, one wave per
-//    partition.  Each 16-token tile is a dense contraction on the matrix cores:
+//  * gqa_decode_mfma_kernel (bf16, block size >= 16): one workgroup per group, one or two
+//    consecutive partitions per wave.  Each 16-token tile is a dense contraction on the matrix cores:
 //    S^T[16 tok x 16 heads] = K Q^T with v_mfma_f32_16x16x32_bf16 (query heads of the group
 //    in the N columns, padded to 16), then, per pair of tiles, O^T[D x 16 heads] += V^T P^T,
 //    also 16x16x32.  The block layout makes both operands plain 16-byte / 8-byte per-lane
@@ -48,10 +48,11 @@ static constexpr float kRescaleSlack = 8.f;
 template <int D>
 constexpr int mfma_max_group() { return D <= 64 ? 16 : 8; }
 
-// Partial of one partition [lo, hi) of sequence b for the query heads of KV head kvh, on the
-// calling wave.  On return lane (n, g4) holds, for head n of the group: acc[t] = unnormalised
-// output dims 16t + 4*g4 .. +3, m = reference max (log2 domain), lsum = its share of the
-// normaliser (to be summed over the four lane rows).
+// Partial of the token range [lo, hi) of sequence b (one or more consecutive partitions, at
+// most 127 blocks) for the query heads of KV head kvh, on the calling wave.  On return lane
+// (n, g4) holds, for head n of the group: acc[t] = unnormalised output dims 16t + 4*g4 .. +3,
+// m = reference max (log2 domain), lsum = its share of the normaliser (to be summed over the
+// four lane rows).
 //
 // Tiles are consumed in pairs.  For a pair (A, B) the PV product is one
 // v_mfma_f32_16x16x32_bf16 per 16-dim output tile with k-slot (g4, i) = token 4*g4 + i of A
@@ -72,7 +73,7 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
   const int t_lo = lo >> 4;
   const int ntiles = ((hi + 15) >> 4) - t_lo;
 
-  // Block ids of the partition (at most 128 blocks; the launcher checks), two per lane:
+  // Block ids of the range (at most 128 blocks; the launcher checks), two per lane:
   // pid0 lane i = block wbase + i, pid1 lane i = block wbase + 64 + i.
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
   const int blk_last = ((t_lo + ntiles - 1) << 4) >> BSL;
@@ -218,14 +219,16 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
   if (bad) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 }
 
-// One workgroup of group_parts waves per (sequence, KV head, group of partitions).  Dynamic
-// LDS (group_parts > 1 only): [group_parts][group][D] partial outputs, then
-// [group_parts][group] lse values (log2 domain).
+// One workgroup of W = group_parts / wave_parts waves per (sequence, KV head, group of
+// partitions); wave w takes the group's partitions [w * wave_parts, (w + 1) * wave_parts),
+// its online softmax continuing across their boundary.  Dynamic LDS (W > 1 only):
+// [W][group][D] partial outputs, then [W][group] lse values (log2 domain).
 template <int D, int BSL, int PAIRS>
 __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kernel(DecodeArgs a) {
   constexpr int VT = D / 16;
   extern __shared__ float smem[];
-  const int G = a.group_parts;
+  const int S = a.wave_parts;
+  const int G = a.group_parts / S;  // waves of the workgroup
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
@@ -244,14 +247,15 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
     if (np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
   }
   if (k >= ng) return;  // uniform over the workgroup; also covers ng < 0
-  const int p = k * G + wv;
+  const int p = k * a.group_parts + wv * S;  // the wave's first partition
   const int L = a.seq[b];
 
   f32x4 acc[VT];
   float m = kNegInf, lsum = 0.f;
   if (p < np) {  // uniform over the wave: waves past the sequence's last partition idle
     const int lo = beg + p * P;
-    gqa_partition_mfma<D, BSL, PAIRS>(a, b, kvh, lo, min(L, lo + P), lane, acc, m, lsum);
+    gqa_partition_mfma<D, BSL, PAIRS>(a, b, kvh, lo, (int)min((int64_t)L, (int64_t)lo + S * P),
+                                      lane, acc, m, lsum);
   }
   lsum = rows_sum(lsum);
   const int grp = a.group;
@@ -442,8 +446,8 @@ int gqa_mfma_max_group(int d) {
 template <int D, int BSL>
 static hipError_t launch_mfma_db(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   constexpr int PAIRS = D <= 128 ? 2 : 1;  // tile pairs held in registers
-  hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS>), grid, dim3(64 * a.group_parts),
-                     lds, st, a);
+  hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS>), grid,
+                     dim3(64 * (a.group_parts / a.wave_parts)), lds, st, a);
   return hipGetLastError();
 }
 
@@ -459,12 +463,12 @@ static hipError_t launch_mfma_d(const DecodeArgs& a, dim3 grid, size_t lds, hipS
   }
 }
 
-size_t gqa_mfma_lds_bytes(int group_parts, int group, int d) {
-  return group_parts > 1 ? (size_t)group_parts * group * (d + 1) * sizeof(float) : 0;
+size_t gqa_mfma_lds_bytes(int waves, int group, int d) {
+  return waves > 1 ? (size_t)waves * group * (d + 1) * sizeof(float) : 0;
 }
 
 hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {
-  const size_t lds = gqa_mfma_lds_bytes(a.group_parts, a.group, d);
+  const size_t lds = gqa_mfma_lds_bytes(a.group_parts / a.wave_parts, a.group, d);
   switch (d) {
     case 64: return launch_mfma_d<64>(a, grid, lds, st);
     case 128: return launch_mfma_d<128>(a, grid, lds, st);

@@ -34,6 +34,7 @@ struct DecodeArgs {
   int32_t batch, hq, hkv, group;
   int32_t max_blocks, max_parts;
   int32_t group_parts;     // consecutive partitions merged on chip into one written partial
+  int32_t wave_parts;      // matrix-core GQA kernel: consecutive partitions per wave
   int32_t grid_ng;         // work items per (sequence, KV head): the largest group count
   int32_t bs, bs_shift;
   float scale;             // softmax scale

@@ -41,6 +41,14 @@ static int log2_exact(int v) {
   return s;
 }
 
+// Tuning override of the partitions per wave of the matrix-core kernel (1 or 2; 0 = auto).
+static int wave_parts_override() {
+  const char* e = std::getenv("KVATTN_WAVE_PARTS");
+  if (!e) return 0;
+  const int v = std::atoi(e);
+  return (v == 1 || v == 2) ? v : 0;
+}
+
 static bool force_generic() {
   const char* e = std::getenv("KVATTN_FORCE_GENERIC");
   return e && e[0] == '1';
@@ -87,6 +95,7 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
 
   // kernel choice
   enum { K_MFMA, K_GENERIC, K_MLA } kind;
+  int wave_parts = 1;
   if (L.latent) {
     if (L.kv_dtype != KVATTN_BF16 || L.head_dim_k != 576 || L.head_dim_v != 512 || bs != 64 ||
         num_q_heads > 16)
@@ -100,16 +109,25 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
     if (group > 16)
       return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: at most 16 query heads per KV head");
     kind = (L.kv_dtype == KVATTN_BF16 && bs >= 16 && !force_generic()) ? K_MFMA : K_GENERIC;
-    // the matrix-core kernel keeps a partition's block ids in two 64-lane registers
-    for (int b = 0; b < batch && kind == K_MFMA; ++b)
+    // Partitions per wave of the matrix-core kernel: two when the group splits evenly, so
+    // that a long batch needs half the waves (at its register use a CU holds 8 waves of
+    // head dim 128 or 256, and a second round of waves restarts the load pipeline).
+    wave_parts = wave_parts_override();
+    if (wave_parts == 0) wave_parts = (group_parts >= 4 && group_parts % 2 == 0) ? 2 : 1;
+    if (group_parts % wave_parts != 0) wave_parts = 1;
+    // the matrix-core kernel keeps a wave's block ids in two 64-lane registers
+    for (int b = 0; b < batch && kind == K_MFMA; ++b) {
+      if (part_tokens[b] > 0 && (int64_t)wave_parts * part_tokens[b] / bs + 1 > 128) wave_parts = 1;
       if (part_tokens[b] > 0 && part_tokens[b] / bs + 1 > 128) kind = K_GENERIC;
-    if (kind == K_MFMA && group_parts > 1) {
-      // one wave per partition of a group, the group's partials merged in LDS
-      if (group_parts > gqa_mfma_max_group(d))
+    }
+    if (kind == K_MFMA && group_parts / wave_parts > 1) {
+      // waves of a group merge their partials in LDS
+      const int waves = group_parts / wave_parts;
+      if (waves > gqa_mfma_max_group(d))
         return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: group_parts above " +
                                                    std::to_string(gqa_mfma_max_group(d)) +
                                                    " for head dim " + std::to_string(d));
-      if (gqa_mfma_lds_bytes(group_parts, group, d) > 65536)
+      if (gqa_mfma_lds_bytes(waves, group, d) > 65536)
         return set_error(KVATTN_E_UNSUPPORTED,
                          "decode_partial: group_parts x heads per KV head x (head dim + 1) x 4 "
                          "bytes exceeds 64 KiB");
@@ -157,6 +175,7 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
   a.max_parts = max_parts;
   a.grid_ng = grid_ng;
   a.group_parts = group_parts;
+  a.wave_parts = wave_parts;
   a.bs = bs;
   a.bs_shift = log2_exact(bs);
   a.scale = scale;

@@ -84,7 +84,7 @@ def test_small_workload_matches_oracle(name):
     _check_partials(case, dc)
 
 
-GROUPED = [("gqa_32k", 2), ("gqa_32k", 3), ("gqa_32k", 8), ("prefix_shared", 4),
+GROUPED = [("gqa_32k", 2), ("gqa_32k", 3), ("gqa_32k", 4), ("gqa_32k", 8), ("gqa_32k", 16), ("prefix_shared", 4),
            ("prefix_shared", 7), ("split_128k", 4), ("mla_16k", 3), ("tiny_fp32", 2)]
 
 
