@@ -116,10 +116,12 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
     for (int t = 0; t < VT; ++t) vb[s][t] = u32x2{0u, 0u};
   }
 
-  // Loads of tile `rel` into ring slot `slot`; nothing is loaded past the partition's last
-  // tile (a wave-uniform skip), so every byte of the partition is fetched exactly once.
-  auto issue = [&](int slot, int rel) {
-    if (rel >= ntiles) return;
+  // Loads of tile `rel` into ring slot `slot`.  Callers in the main loop pass only tiles of
+  // the range (GUARD = false), so every round issues the same loads and the compiler's wait
+  // counts stay exact (a conditional load anywhere in the loop would make it wait for all
+  // outstanding loads, the prefetch included); the last round skips tiles past the end.
+  auto issue = [&](int slot, int rel, bool guard) {
+    if (guard && rel >= ntiles) return;
     const int tok0 = (t_lo + rel) << 4;
     const int blk = tok0 >> BSL;
     const int sub = tok0 & (BS - 1);
@@ -163,21 +165,18 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
     bad |= !vld[slot] & (rel < ntiles);
   };
 
-  // prologue: the first PAIRS - 1 pairs
-#pragma unroll
-  for (int s = 0; s < RING - 2; ++s) issue(s, s);
-
-  // Tiles past the end of the partition (the tail of the last ring round) are computed fully
+  // One ring round: RING tiles starting at `it`, each pair's refill issued RING - 2 tiles
+  // ahead.  Tiles past the end of the range (the tail of the last round) are computed fully
   // masked: zero weight, max unchanged.
-  for (int it = 0; it < ntiles; it += RING) {
+  auto round = [&](int it, bool guard) {
 #pragma unroll
     for (int ps = 0; ps < PAIRS; ++ps) {
       const int sa = 2 * ps, sb = 2 * ps + 1;
       const int ra = it + 2 * ps, rb = ra + 1;
       // refill the pair slot consumed last round with the pair RING - 2 tiles ahead
       const int fs = (sa + RING - 2) % RING;
-      issue(fs, ra + RING - 2);
-      issue(fs + 1, ra + RING - 1);
+      issue(fs, ra + RING - 2, guard);
+      issue(fs + 1, ra + RING - 1, guard);
       float sva[4], svb[4];
       scores(sa, ra, sva);
       scores(sb, rb, svb);
@@ -215,7 +214,17 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, blo, acc[t], 0, 0, 0);
       }
     }
-  }
+  };
+
+  // prologue: the first PAIRS - 1 pairs, unguarded so the wait counts stay exact (in a range
+  // shorter than the prologue the extra tile reads a clamped, valid block id: a harmless
+  // redundant load)
+#pragma unroll
+  for (int s = 0; s < RING - 2; ++s) issue(s, s, false);
+  // rounds whose refills all fall inside the range, then the last round(s)
+  int it = 0;
+  for (; it + 2 * RING - 2 <= ntiles; it += RING) round(it, false);
+  for (; it < ntiles; it += RING) round(it, true);
   if (bad) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 }
 

@@ -5,23 +5,27 @@
 // the latent's leading 512 columns, so decode reduces to a query-side projection and an
 // output-side expansion around one shared latent, and each latent need be read from DRAM
 // only once for all heads ("Physically Partitioned KVCache Format for CPU-GPU Load Balancing
-// in MoE Inference", §6.1, compressed-MLA variant).  Here that reuse is staged in LDS:
+// in MoE Inference", §6.1, compressed-MLA variant).
 //
-//   one workgroup of 4 waves per (sequence, partition); per 64-token block
-//   1. the block's 72 KiB latent is fetched with fully coalesced 16-byte non-temporal loads
-//      (read once per step; prefetched one block ahead in registers) and written to LDS with
-//      an XOR swizzle
-//      (slot(c, t) = c*64 + (t ^ (c & 15)) for 16-byte chunk c of token t);
-//   2. wave w scores tokens 16w..16w+15 against all 16 heads on the matrix cores,
-//      S^T = C Q^T with v_mfma_f32_16x16x32_bf16 (18 k-steps over 576 dims), and posts the
-//      scores to LDS;
-//   3. every wave reads all 64 x 16 scores, updates the running max / normaliser and forms
-//      the bf16 P^T operands itself (one barrier, no second exchange);
-//   4. wave w accumulates O^T for its 128 output dims, V^T P^T with
-//      v_mfma_f32_16x16x16_bf16, reading 4-token x 8-dim patches of the latent from LDS and
-//      regrouping them in registers with byte permutes.
-// The swizzle makes both LDS read patterns (token-major for QK, chunk-major for PV) and the
-// write pattern free of bank conflicts.
+// One workgroup of 4 waves (one per SIMD, so each wave may hold up to 512 registers) per
+// (sequence, group of partitions), walking the group's 64-token blocks ("stages") in order:
+//   1. wave w loads the latent rows of tokens 16w .. 16w+15 of a stage straight into
+//      registers with 16-byte non-temporal loads (the latent is read once per step) -- lane
+//      (n, g4) holds token n, 16-byte chunks g4 + 4j -- into a ring of kRing stages, so
+//      kRing - 1 stages (2 x 72 KiB per CU) are in flight while one is computed;
+//   2. the same registers are the A operand of the scores S^T = C Q^T on the matrix cores
+//      (v_mfma_f32_16x16x32_bf16, 18 k-steps over the 576 dims, heads in the N columns; the
+//      Q^T operand is read from LDS, leaving the registers to the ring);
+//   3. the value part (chunks 0..63) is written to LDS with an XOR swizzle
+//      (slot(c, t) = c*64 + (t ^ (c & 15)) for chunk c of token t, conflict-free for this
+//      write and for the transposed read below), and the scores to LDS;
+//   4. after one barrier every wave reads all 64 x 16 scores, updates the running max /
+//      normaliser and forms the bf16 P^T operands, then accumulates O^T for its 128 output
+//      dims, V^T P^T with v_mfma_f32_16x16x16_bf16, reading 4-token x 8-dim patches of the
+//      value part from LDS and regrouping them in registers with byte permutes.
+// LDS (values and scores) is double-buffered by stage parity, so one barrier per stage
+// orders both the writes of a stage before its reads and the reads of the previous use of
+// a buffer before its next writes.
 
 #include "device_common.h"
 
@@ -32,15 +36,18 @@ static constexpr float kLn2M = 0.693147180559945309f;
 
 static constexpr int kMlaDk = 576;
 static constexpr int kMlaDv = 512;
-static constexpr int kMlaChunks = kMlaDk / 8;  // 72 chunks of 8 bf16
+static constexpr int kMlaChunks = kMlaDk / 8;   // 72 chunks of 8 bf16
+static constexpr int kMlaVChunks = kMlaDv / 8;  // 64 chunks hold the value part
+static constexpr int kMlaKs = kMlaChunks / 4;   // 18 k-steps of the score product
 static constexpr int kMlaBs = 64;
-static constexpr int kMlaLoads = kMlaChunks * kMlaBs / 256;  // 16-byte loads per thread: 18
+static constexpr int kRing = 3;                 // stages held in registers per wave
 
 __device__ __forceinline__ int lat_slot(int c, int t) { return c * kMlaBs + (t ^ (c & 15)); }
 
-__global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
-  __shared__ uint4 lat[kMlaChunks * kMlaBs];  // 73,728 B
-  __shared__ float sx[kMlaBs][16];            // scores of the stage, [token][head]
+__global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
+  __shared__ uint4 vlat[2][kMlaVChunks * kMlaBs];  // value part of a stage: 2 x 64 KiB
+  __shared__ float sx[2][kMlaBs][16];             // scores of a stage, [token][head]
+  __shared__ uint4 qs[kMlaKs * 64];                // Q^T operand, [k-step][lane]
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int lane = tid & 63;
@@ -67,28 +74,45 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
 
   // Q^T operand (B of the QK product): head n, dims 8*(g4+4j) .. +7.
-  bf16x8 qop[kMlaChunks / 4];
-  {
+  if (wv == 0) {
     const bool hv = n < a.hq;
     const uint4* qrow = reinterpret_cast<const uint4*>(
         static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (hv ? n : 0)) * kMlaDk);
 #pragma unroll
-    for (int j = 0; j < kMlaChunks / 4; ++j) {
+    for (int j = 0; j < kMlaKs; ++j) {
       uint4 v = qrow[g4 + 4 * j];
       if (!hv) v = make_uint4(0u, 0u, 0u, 0u);
-      qop[j] = as_bf16x8(v);
+      qs[j * 64 + lane] = v;
     }
   }
+  __syncthreads();
 
-  uint4 stage[kMlaLoads];
-  bool vld_next = true;
-  auto fetch = [&](int st_rel) {
-    const int32_t pid = trow[st_lo + st_rel];
-    vld_next = valid_block(a.rt, pid);
-    gu32x4* src = reinterpret_cast<gu32x4*>(block_addr(a.rt, vld_next ? pid : 0));
+  // Register ring of latent rows: stage s lives in slot s % kRing.  It starts zeroed, so a
+  // slot never loaded (short groups) is finite; its scores are masked anyway.
+  u32x4 kb[kRing][kMlaKs];
+  bool vld[kRing];
 #pragma unroll
-    for (int r = 0; r < kMlaLoads; ++r)
-      stage[r] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(src + r * 256 + tid));
+  for (int r = 0; r < kRing; ++r) {
+    vld[r] = false;
+#pragma unroll
+    for (int j = 0; j < kMlaKs; ++j) kb[r][j] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // lane (n, g4) of wave w: token 16w + n, chunk g4 + 4j at byte ((g4 + 4j) * 64 + token) * 16.
+  // Stage s is loaded into slot s % kRing.  The main loop passes only stages of the group
+  // (guard = false), so every stage issues the same loads and the compiler's wait counts stay
+  // exact (a conditional load anywhere in the loop would make it wait for all outstanding
+  // loads, the prefetch included); the prologue's loads past a short group re-read its last
+  // block (clamped, harmless), the last round skips them.
+  const uint32_t loff = (uint32_t)((g4 * kMlaBs + 16 * wv + n) * 16);
+  auto issue = [&](int slot, int s, bool guard) {
+    if (guard && s >= nst) return;
+    const int32_t pid = trow[st_lo + min(s, nst - 1)];
+    const bool ok = valid_block(a.rt, pid);
+    vld[slot] = ok;
+    gchar* base = block_addr(a.rt, ok ? pid : 0) + loff;
+#pragma unroll
+    for (int j = 0; j < kMlaKs; ++j)
+      kb[slot][j] = __builtin_nontemporal_load(reinterpret_cast<gu32x4*>(base + j * (4 * kMlaBs * 16)));
   };
 
   f32x4 acc[8];
@@ -97,45 +121,40 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
   float m = kNegInfM, lsum = 0.f;
   bool bad = false;
 
-  fetch(0);
-  for (int s = 0; s < nst; ++s) {
-    const bool vld = vld_next;
-    bad |= !vld;
-    __syncthreads();  // previous stage's LDS reads are done
-#pragma unroll
-    for (int r = 0; r < kMlaLoads; ++r) {
-      const int q = r * 256 + tid;  // chunk q / 64, token q % 64
-      lat[lat_slot(q >> 6, q & 63)] = stage[r];
-    }
-    if (s + 1 < nst) fetch(s + 1);  // nothing is fetched past the partition
-    __syncthreads();  // latent of this stage visible
+  // One stage: refill the slot of stage s + kRing - 1, then compute stage s from slot r.
+  auto stage = [&](int r, int s, bool guard) {
+    issue((r + kRing - 1) % kRing, s + kRing - 1, guard);
+    const int buf = s & 1;
+    bad |= !vld[r];
 
-    // 2. scores of tokens 16*wv .. +15
+    // 2. scores of tokens 16*wv .. +15 from the registers
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int tok = 16 * wv + n;
 #pragma unroll
-    for (int j = 0; j < kMlaChunks / 4; ++j) {
-      const int c = g4 + 4 * j;
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lat[lat_slot(c, tok)]), qop[j], sacc, 0, 0, 0);
-    }
-    const int tbase = ((st_lo + s) << 6);
+    for (int j = 0; j < kMlaKs; ++j)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[r][j]), as_bf16x8(qs[j * 64 + lane]), sacc, 0, 0, 0);
+
+    // 3. value part and scores to LDS
+#pragma unroll
+    for (int j = 0; j < kMlaVChunks / 4; ++j)
+      vlat[buf][lat_slot(g4 + 4 * j, 16 * wv + n)] = __builtin_bit_cast(uint4, kb[r][j]);
+    const int tbase = (st_lo + s) << 6;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tl = 16 * wv + 4 * g4 + i;
       const int t = tbase + tl;
-      const bool ok = vld && t >= lo && t < hi;
-      sx[tl][n] = ok ? sacc[i] * a.scale_log2 : kNegInfM;
+      const bool ok = vld[r] & (t >= lo) & (t < hi);
+      sx[buf][tl][n] = ok ? sacc[i] * a.scale_log2 : kNegInfM;
     }
     __syncthreads();
 
-    // 3. softmax update over the 64 tokens, all waves alike
+    // 4a. softmax update over the 64 tokens, all waves alike
     float sv[4][4];
     float mx = kNegInfM;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[ks][i] = sx[16 * ks + 4 * g4 + i][n];
+        sv[ks][i] = sx[buf][16 * ks + 4 * g4 + i][n];
         mx = fmaxf(mx, sv[ks][i]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -150,13 +169,14 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
       const uint32_t p01 = pack_bf16x2(exp2f(sv[ks][0] - mref), exp2f(sv[ks][1] - mref));
       const uint32_t p23 = pack_bf16x2(exp2f(sv[ks][2] - mref), exp2f(sv[ks][3] - mref));
+      // the normaliser sums the bf16 weights the PV product uses
       part += (bf16_to_f32(p01 & 0xffffu) + bf16_to_f32(p01 >> 16)) +
               (bf16_to_f32(p23 & 0xffffu) + bf16_to_f32(p23 >> 16));
       pop[ks] = as_i16x4(make_uint2(p01, p23));
     }
     lsum = lsum * alpha + part;
 
-    // 4. O^T for dims 8*c + e, c = 16*wv + row (row = MFMA row), e = 0..7
+    // 4b. O^T for dims 8*c + e, c = 16*wv + row (row = MFMA row), e = 0..7
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     const int c = 16 * wv + n;
@@ -164,22 +184,35 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(DecodeArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
       uint4 r4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r4[i] = lat[lat_slot(c, 16 * ks + 4 * g4 + i)];
+      for (int i = 0; i < 4; ++i) r4[i] = vlat[buf][lat_slot(c, 16 * ks + 4 * g4 + i)];
       const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r4[0]);
       const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r4[1]);
       const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r4[2]);
       const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r4[3]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // dims 8c + 2k (low halves) and 8c + 2k + 1 (high halves) of the 4 tokens
-        const uint2 lo_op = make_uint2((w0[k] & 0xffffu) | (w1[k] << 16), (w2[k] & 0xffffu) | (w3[k] << 16));
-        const uint2 hi_op = make_uint2((w0[k] >> 16) | (w1[k] & 0xffff0000u), (w2[k] >> 16) | (w3[k] & 0xffff0000u));
-        acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(lo_op), pop[ks], acc[2 * k], 0, 0, 0);
-        acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(hi_op), pop[ks], acc[2 * k + 1], 0, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        // dims 8c + 2q (low halves) and 8c + 2q + 1 (high halves) of the 4 tokens
+        const uint2 lo_op = make_uint2((w0[q] & 0xffffu) | (w1[q] << 16), (w2[q] & 0xffffu) | (w3[q] << 16));
+        const uint2 hi_op = make_uint2((w0[q] >> 16) | (w1[q] & 0xffff0000u), (w2[q] >> 16) | (w3[q] & 0xffff0000u));
+        acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(lo_op), pop[ks], acc[2 * q], 0, 0, 0);
+        acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(hi_op), pop[ks], acc[2 * q + 1], 0, 0, 0);
       }
     }
+  };
+
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r) issue(r, r, false);
+  int it = 0;
+  for (; it + 2 * kRing - 1 <= nst; it += kRing) {  // every refill inside the group
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) stage(r, it + r, false);
   }
-  if (bad && tid == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+  for (; it < nst; it += kRing) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r)
+      if (it + r < nst) stage(r, it + r, true);  // uniform over the workgroup
+  }
+  if (bad && lane == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
