@@ -37,7 +37,7 @@ DESCR = {
 }
 # Partitions merged on chip into each written partial, per workload (the launch configuration
 # the full-size parity tests use too): fewer partial writes next to the K/V read stream.
-GROUP_PARTS = {"gqa_32k": 16, "split_128k": 4, "prefix_shared": 4, "mla_16k": 4, "tiny_fp32": 1}
+GROUP_PARTS = {"gqa_32k": 16, "split_128k": 8, "prefix_shared": 2, "mla_16k": 4, "tiny_fp32": 1}
 
 KERNEL_SOURCES = {
     "mla_16k": ["decode_mla.hip", "device_common.h"],

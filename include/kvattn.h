@@ -161,6 +161,12 @@ kvattn_status kvattn_block_release(kvattn_pool* pool, const int32_t* table, int3
 /* Free blocks left in the pool, or -1 for NULL. */
 int64_t kvattn_pool_num_free(const kvattn_pool* pool);
 
+/* Blocks referenced by two or more table entries (shared prefixes), or -1 for NULL.  While
+ * the pool holds shared blocks, the bf16 GQA decode kernel reads K/V with cache-retaining
+ * loads so that sequences sharing a prefix can reuse its blocks from the caches; otherwise
+ * it streams them with non-temporal loads (every block is read once per step). */
+int64_t kvattn_pool_shared_blocks(const kvattn_pool* pool);
+
 /* Reference count of block `id`, or -1 if out of range. */
 int32_t kvattn_pool_refcount(const kvattn_pool* pool, int32_t id);
 

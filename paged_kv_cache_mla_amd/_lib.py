@@ -54,6 +54,7 @@ _SIGNATURES = {
     "kvattn_block_release": (_I32, [_P, _PI32, _I32, _I32]),
     "kvattn_pool_num_free": (_I64, [_P]),
     "kvattn_pool_refcount": (_I32, [_P, _I32]),
+    "kvattn_pool_shared_blocks": (_I64, [_P]),
     "kvattn_partition_count": (_I32, [_I32, _I32, _I32]),
     "kvattn_decode_partial": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32,
                                      _PI32, _PI32, _PI32, _P, _I32, _I32, _P, _P, _P, _P, _P]),

@@ -98,6 +98,10 @@ class Pool:
     def num_free(self):
         return int(self._lib.kvattn_pool_num_free(self.handle))
 
+    @property
+    def shared_blocks(self):
+        return int(self._lib.kvattn_pool_shared_blocks(self.handle))
+
     def refcount(self, block_id):
         return int(self._lib.kvattn_pool_refcount(self.handle, int(block_id)))
 

@@ -21,7 +21,9 @@
 //    head column, 4 consecutive tokens per lane) is exactly the B-operand layout the PV
 //    product needs, so no data moves between lanes except two lane swaps for the per-head
 //    max.  The next pair of tiles is prefetched into registers while the current pair is
-//    computed.  K and V are read once per step, so their loads carry the non-temporal hint.
+//    computed.  K and V are read once per step, so their loads carry the non-temporal hint,
+//    unless the pool holds blocks shared by several sequences (prefix sharing): then plain,
+//    cache-retaining loads let the sharing sequences reuse those blocks from L2 / MALL.
 //    The waves' partials (o, lse) go to LDS and are merged there exactly, by the same LSE
 //    rescaling as the merge kernel, before one partial per group is written: writes of
 //    partial outputs are expensive while the read stream is running (on MI355X, 16.9 MB of
@@ -60,7 +62,7 @@ constexpr int mfma_max_group() { return D <= 64 ? 16 : 8; }
 // side by side, and the B operand the two tiles' score-layout weights side by side.  The
 // weights enter as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)), two MFMAs per
 // output tile, so P V is accurate to ~2^-16 relative rather than bf16's 2^-9.
-template <int D, int BSL, int PAIRS>
+template <int D, int BSL, int PAIRS, bool NT>
 __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, int kvh, int lo,
                                                    int hi, int lane, f32x4 (&acc)[D / 16],
                                                    float& m, float& lsum) {
@@ -135,11 +137,15 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
     gchar* kbase = base + sub * 16;
     gchar* vbase = base + kpart_bytes + sub * 2;
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
-      kb[slot][j] = __builtin_nontemporal_load(reinterpret_cast<gu32x4*>(kbase + koff + j * (4 * BS * 16)));
+    for (int j = 0; j < KS; ++j) {
+      gu32x4* pk = reinterpret_cast<gu32x4*>(kbase + koff + j * (4 * BS * 16));
+      kb[slot][j] = NT ? __builtin_nontemporal_load(pk) : *pk;
+    }
 #pragma unroll
-    for (int t = 0; t < VT; ++t)
-      vb[slot][t] = __builtin_nontemporal_load(reinterpret_cast<gu32x2*>(vbase + voff + t * (16 * BS * 2)));
+    for (int t = 0; t < VT; ++t) {
+      gu32x2* pv = reinterpret_cast<gu32x2*>(vbase + voff + t * (16 * BS * 2));
+      vb[slot][t] = NT ? __builtin_nontemporal_load(pv) : *pv;
+    }
   };
 
 #pragma unroll
@@ -232,7 +238,7 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
 // partitions); wave w takes the group's partitions [w * wave_parts, (w + 1) * wave_parts),
 // its online softmax continuing across their boundary.  Dynamic LDS (W > 1 only):
 // [W][group][D] partial outputs, then [W][group] lse values (log2 domain).
-template <int D, int BSL, int PAIRS>
+template <int D, int BSL, int PAIRS, bool NT>
 __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kernel(DecodeArgs a) {
   constexpr int VT = D / 16;
   extern __shared__ float smem[];
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
   float m = kNegInf, lsum = 0.f;
   if (p < np) {  // uniform over the wave: waves past the sequence's last partition idle
     const int lo = beg + p * P;
-    gqa_partition_mfma<D, BSL, PAIRS>(a, b, kvh, lo, (int)min((int64_t)L, (int64_t)lo + S * P),
+    gqa_partition_mfma<D, BSL, PAIRS, NT>(a, b, kvh, lo, (int)min((int64_t)L, (int64_t)lo + S * P),
                                       lane, acc, m, lsum);
   }
   lsum = rows_sum(lsum);
@@ -453,21 +459,26 @@ int gqa_mfma_max_group(int d) {
 }
 
 template <int D, int BSL>
-static hipError_t launch_mfma_db(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+static hipError_t launch_mfma_db(const DecodeArgs& a, dim3 grid, size_t lds, bool stream,
+                                 hipStream_t st) {
   constexpr int PAIRS = D <= 128 ? 2 : 1;  // tile pairs held in registers
-  hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS>), grid,
-                     dim3(64 * (a.group_parts / a.wave_parts)), lds, st, a);
+  const dim3 block(64 * (a.group_parts / a.wave_parts));
+  if (stream)
+    hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS, true>), grid, block, lds, st, a);
+  else
+    hipLaunchKernelGGL((gqa_decode_mfma_kernel<D, BSL, PAIRS, false>), grid, block, lds, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_mfma_d(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+static hipError_t launch_mfma_d(const DecodeArgs& a, dim3 grid, size_t lds, bool stream,
+                                hipStream_t st) {
   switch (a.bs_shift) {
-    case 4: return launch_mfma_db<D, 4>(a, grid, lds, st);
-    case 5: return launch_mfma_db<D, 5>(a, grid, lds, st);
-    case 6: return launch_mfma_db<D, 6>(a, grid, lds, st);
-    case 7: return launch_mfma_db<D, 7>(a, grid, lds, st);
-    case 8: return launch_mfma_db<D, 8>(a, grid, lds, st);
+    case 4: return launch_mfma_db<D, 4>(a, grid, lds, stream, st);
+    case 5: return launch_mfma_db<D, 5>(a, grid, lds, stream, st);
+    case 6: return launch_mfma_db<D, 6>(a, grid, lds, stream, st);
+    case 7: return launch_mfma_db<D, 7>(a, grid, lds, stream, st);
+    case 8: return launch_mfma_db<D, 8>(a, grid, lds, stream, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -476,12 +487,14 @@ size_t gqa_mfma_lds_bytes(int waves, int group, int d) {
   return waves > 1 ? (size_t)waves * group * (d + 1) * sizeof(float) : 0;
 }
 
-hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {
+// `stream`: non-temporal K/V loads (every block read once per step); otherwise
+// cache-retaining loads, for pools whose blocks are shared by several sequences.
+hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, bool stream, dim3 grid, hipStream_t st) {
   const size_t lds = gqa_mfma_lds_bytes(a.group_parts / a.wave_parts, a.group, d);
   switch (d) {
-    case 64: return launch_mfma_d<64>(a, grid, lds, st);
-    case 128: return launch_mfma_d<128>(a, grid, lds, st);
-    case 256: return launch_mfma_d<256>(a, grid, lds, st);
+    case 64: return launch_mfma_d<64>(a, grid, lds, stream, st);
+    case 128: return launch_mfma_d<128>(a, grid, lds, stream, st);
+    case 256: return launch_mfma_d<256>(a, grid, lds, stream, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -9,7 +9,7 @@
 
 namespace kvattn {
 
-hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, dim3 grid, hipStream_t st);
+hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, bool stream, dim3 grid, hipStream_t st);
 int gqa_mfma_max_group(int d);
 size_t gqa_mfma_lds_bytes(int group_parts, int group, int d);
 hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, hipStream_t st);
@@ -186,7 +186,7 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
   hipError_t e;
   switch (kind) {
     case K_MLA: e = launch_mla(a, grid, st); break;
-    case K_MFMA: e = launch_gqa_mfma(a, L.head_dim_k, grid, st); break;
+    case K_MFMA: e = launch_gqa_mfma(a, L.head_dim_k, pool->shared_blocks == 0, grid, st); break;
     default: e = launch_gqa_generic(a, L.head_dim_k, L.kv_dtype == KVATTN_F32, grid, st); break;
   }
   return hip_status(e, "decode_partial launch");

@@ -13,8 +13,8 @@
 // the thread's first kR partial columns and of the first lse values at once, before the
 // partition count is known (bounded by max_parts), then take the block max, write the weights
 // to LDS while summing them, and only then consume the partial columns already in registers.
-// Partitions beyond kR * groups (long sequences, wide heads) are handled by a second, plain
-// loop.  Every sum runs in a fixed order, so the result is bitwise reproducible.
+// Partitions beyond kR * groups (long sequences, wide heads) follow in further chunks of
+// kR * groups.  Every sum runs in a fixed order, so the result is bitwise reproducible.
 
 #include "device_common.h"
 
@@ -96,17 +96,26 @@ __global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
   }
   const float tot = block_sum(sm, red);  // its barriers also publish wts
 
-  // 4. weighted sum of the partial columns
+  // 4. weighted sum of the partial columns, chunk by chunk of kR * groups partitions; the
+  //    loads of a chunk are all issued before any is used, so kR are in flight per thread
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (active) {
+    for (int p0 = 0; p0 < np; p0 += kR * groups) {
+      if (p0 > 0) {
 #pragma unroll
-    for (int k = 0; k < kR; ++k) {
-      const int p = g + k * groups;
-      if (p < np) acc += ov[k] * wts[p];  // a select: stale slots never enter the sum
-    }
-    for (int p = g + kR * groups; p < np; p += groups) {
-      const float w = p < kWts ? wts[p] : expf(lrow[p] - big);
-      acc += orow[(int64_t)p * cols + c] * w;
+        for (int k = 0; k < kR; ++k) {
+          const int p = p0 + g + k * groups;
+          ov[k] = p < np ? orow[(int64_t)p * cols + c] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kR; ++k) {
+        const int p = p0 + g + k * groups;
+        if (p < np) {  // a select: stale slots never enter the sum
+          const float w = p < kWts ? wts[p] : expf(lrow[p] - big);
+          acc += ov[k] * w;
+        }
+      }
     }
   }
   part[tid] = acc;

@@ -126,6 +126,10 @@ int64_t kvattn_pool_num_free(const kvattn_pool* pool) {
   return pool ? (int64_t)pool->free_stack.size() : -1;
 }
 
+int64_t kvattn_pool_shared_blocks(const kvattn_pool* pool) {
+  return pool ? pool->shared_blocks : -1;
+}
+
 int32_t kvattn_pool_refcount(const kvattn_pool* pool, int32_t id) {
   if (!pool || id < 0 || id >= pool->total_blocks) return -1;
   return pool->refcount[(size_t)id];
@@ -158,7 +162,10 @@ static kvattn_status explicit_claim(kvattn_pool* p, int32_t batch, const int32_t
   for (const auto& kv : counts)
     if (p->refcount[(size_t)kv.first] != 0)
       return set_error(KVATTN_E_STATE, "block_table: block " + std::to_string(kv.first) + " is not free");
-  for (const auto& kv : counts) p->refcount[(size_t)kv.first] = kv.second;
+  for (const auto& kv : counts) {
+    p->refcount[(size_t)kv.first] = kv.second;
+    if (kv.second >= 2) ++p->shared_blocks;
+  }
   std::vector<int32_t> kept;
   kept.reserve(p->free_stack.size());
   for (int32_t id : p->free_stack)
@@ -220,7 +227,7 @@ kvattn_status kvattn_block_table(kvattn_pool* pool, int32_t batch, const int32_t
       if (i < pl.nabs) continue;
       if (i < pl.nsh) {
         const int32_t pid = table_out[(size_t)pl.src * max_blocks + i];
-        ++pool->refcount[(size_t)pid];
+        if (++pool->refcount[(size_t)pid] == 2) ++pool->shared_blocks;
         row[i] = pid;
       } else {
         const int32_t pid = pool->free_stack.back();
@@ -254,7 +261,9 @@ kvattn_status kvattn_block_release(kvattn_pool* pool, const int32_t* table, int3
   for (size_t i = 0; i < n; ++i) {
     const int32_t pid = table[i];
     if (pid == KVATTN_BLOCK_ABSENT) continue;
-    if (--pool->refcount[(size_t)pid] == 0) pool->free_stack.push_back(pid);
+    const int32_t left = --pool->refcount[(size_t)pid];
+    if (left == 1) --pool->shared_blocks;
+    if (left == 0) pool->free_stack.push_back(pid);
   }
   return KVATTN_OK;
 }

@@ -17,6 +17,7 @@ struct kvattn_pool {
   int64_t total_blocks = 0;
   std::vector<int32_t> free_stack;  // next block handed out = back()
   std::vector<int32_t> refcount;
+  int64_t shared_blocks = 0;        // blocks with refcount >= 2
 };
 
 namespace kvattn {

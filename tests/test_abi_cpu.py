@@ -128,6 +128,7 @@ def test_pool_matches_model_over_random_operations():
             assert pool.num_free == len(model.free)
             for pid in range(total):
                 assert pool.refcount(pid) == model.ref[pid]
+            assert pool.shared_blocks == sum(1 for r in model.ref if r >= 2)
 
 
 def test_exhaustion_is_all_or_nothing_and_reports_shortfall():

@@ -158,6 +158,32 @@ def test_physical_relabelling_is_bitwise_invisible(name):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def _unshared(case):
+    """Same logical content with every shared block given its own physical copy per table
+    entry: the pool then holds no shared blocks."""
+    import copy
+    per = case.elems_per_block()
+    flat = np.concatenate(case.regions)
+    ids = case.table[case.table >= 0]
+    c2 = copy.copy(case)
+    c2.regions = [np.concatenate([flat[int(i) * per:(int(i) + 1) * per] for i in ids])]
+    c2.region_blocks = [int(ids.size)]
+    t = np.full_like(case.table, -1)
+    t[case.table >= 0] = np.arange(ids.size, dtype=np.int32)
+    c2.table = t
+    return c2
+
+
+def test_shared_and_unshared_prefix_give_bitwise_equal_output():
+    """Pools with shared blocks are read with cache-retaining loads, others with streaming
+    loads; the arithmetic is the same, so unsharing the prefixes changes no bit."""
+    case = make_case("prefix_shared", "small")
+    dc1, o1, l1 = _run(case)
+    dc2, o2, l2 = _run(_unshared(case))
+    assert dc1.pool.shared_blocks > 0 and dc2.pool.shared_blocks == 0
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 @pytest.mark.parametrize("name", ["prefix_shared", "mla_16k", "split_128k", "tiny_fp32"])
 def test_resolution_offsets_bitwise(name):
     from paged_kv_cache_mla_amd.api import resolve_offsets
