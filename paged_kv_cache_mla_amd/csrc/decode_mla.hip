@@ -23,6 +23,8 @@
 //      normaliser and forms the bf16 P^T operands, then accumulates O^T for its 128 output
 //      dims, V^T P^T with v_mfma_f32_16x16x16_bf16, reading 4-token x 8-dim patches of the
 //      value part from LDS and regrouping them in registers with byte permutes.
+// The swizzle only touches the low 4 token bits, so all LDS addresses are a few per-lane bases
+// plus immediate offsets; computing those bases once keeps ~100 registers free for the ring.
 // LDS (values and scores) is double-buffered by stage parity, so one barrier per stage
 // orders both the writes of a stage before its reads and the reads of the previous use of
 // a buffer before its next writes.
@@ -120,11 +122,21 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInfM, lsum = 0.f;
   bool bad = false;
+  // LDS slots (16-byte units within a value buffer): the value-part write of chunk g4 + 4j
+  // is wslot[j % 4] + (j / 4) * 1024, the transposed read of chunk 16 wv + n, token
+  // 16 ks + 4 g4 + i is rslot[i] + 16 ks (the swizzle only touches the low 4 token bits)
+  int wslot[4], rslot[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    wslot[q] = lat_slot(g4 + 4 * q, 16 * wv + n);
+    rslot[q] = lat_slot(16 * wv + n, 4 * g4 + q);
+  }
 
   // One stage: refill the slot of stage s + kRing - 1, then compute stage s from slot r.
   auto stage = [&](int r, int s, bool guard) {
     issue((r + kRing - 1) % kRing, s + kRing - 1, guard);
     const int buf = s & 1;
+    uint4* vbuf = vlat[buf];
     bad |= !vld[r];
 
     // 2. scores of tokens 16*wv .. +15 from the registers
@@ -136,7 +148,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     // 3. value part and scores to LDS
 #pragma unroll
     for (int j = 0; j < kMlaVChunks / 4; ++j)
-      vlat[buf][lat_slot(g4 + 4 * j, 16 * wv + n)] = __builtin_bit_cast(uint4, kb[r][j]);
+      vbuf[(j >> 2) * 1024 + wslot[j & 3]] = __builtin_bit_cast(uint4, kb[r][j]);
     const int tbase = (st_lo + s) << 6;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -161,14 +173,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx);
     const float mref = mnew == kNegInfM ? 0.f : mnew;
-    const float alpha = exp2f(m - mref);
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
     m = mnew;
     i16x4 pop[4];
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t p01 = pack_bf16x2(exp2f(sv[ks][0] - mref), exp2f(sv[ks][1] - mref));
-      const uint32_t p23 = pack_bf16x2(exp2f(sv[ks][2] - mref), exp2f(sv[ks][3] - mref));
+      const uint32_t p01 = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[ks][0] - mref), __builtin_amdgcn_exp2f(sv[ks][1] - mref));
+      const uint32_t p23 = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[ks][2] - mref), __builtin_amdgcn_exp2f(sv[ks][3] - mref));
       // the normaliser sums the bf16 weights the PV product uses
       part += (bf16_to_f32(p01 & 0xffffu) + bf16_to_f32(p01 >> 16)) +
               (bf16_to_f32(p23 & 0xffffu) + bf16_to_f32(p23 >> 16));
@@ -184,7 +196,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
       uint4 r4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r4[i] = vlat[buf][lat_slot(c, 16 * ks + 4 * g4 + i)];
+      for (int i = 0; i < 4; ++i) r4[i] = vbuf[16 * ks + rslot[i]];
       const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r4[0]);
       const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r4[1]);
       const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r4[2]);
