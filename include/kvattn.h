@@ -258,6 +258,37 @@ kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,
                                void* hip_stream);
 
 /*
+ * CPU share of a decode step, computed on the host ([InplaceKVCache] §5.1: the engines take
+ * disjoint token ranges of every sequence over all heads; §4.2: the CPU returns only its
+ * partial output and normaliser, which the GPU merges; §6.1: the CPU kernel reads the blocks
+ * in place with an online softmax and fp32 accumulation, and for MLA reads each latent once
+ * for all heads).  For every sequence b and query head h it writes the partial over tokens
+ * [0, tok_end[b]):
+ *     o_out[b][h][:] = sum_t w_t V(t) / sum_t w_t,   lse_out[b][h] = max s + ln(sum_t w_t)
+ * (natural log; tok_end[b] = 0 gives o = 0, lse = -INFINITY), ready to be passed to
+ * kvattn_merge_lse as the external partial once copied to the device.
+ *   layout         block layout, exactly as for the device pool (header comment above)
+ *   host_regions   1..KVATTN_MAX_REGIONS regions of host memory holding whole blocks; block ids
+ *                  run consecutively over them in order (like kvattn_pool_alloc)
+ *   q              host [batch][num_q_heads][Dk], element type q_dtype (= kv_dtype)
+ *   table          host [batch][max_blocks] int32; entries below ceil(tok_end[b] / bs) must be
+ *                  valid ids of the host regions (E_RANGE otherwise)
+ *   tok_end        host [batch] int32, 0 <= tok_end[b] <= max_blocks * bs
+ *   o_out, lse_out host fp32 [batch][num_q_heads][Dv] and [batch][num_q_heads]
+ *   n_threads      worker threads (<= 0: the hardware concurrency)
+ * Work items are (sequence, KV head, 1024-token chunk of whole blocks) taken by the threads
+ * from a shared counter; the chunk partials are merged in chunk order, so the result does not
+ * depend on n_threads.  Synchronous; all memory is the caller's.  Errors: E_INVAL, E_RANGE,
+ * E_UNSUPPORTED (q_dtype != kv_dtype, more than 16 query heads per KV head).
+ */
+kvattn_status kvattn_host_partial(const kvattn_layout* layout, const kvattn_region* host_regions,
+                                  int32_t n_regions, const void* q, int32_t q_dtype,
+                                  int32_t batch, int32_t num_q_heads, float scale,
+                                  const int32_t* table, int32_t max_blocks,
+                                  const int32_t* tok_end, float* o_out, float* lse_out,
+                                  int32_t n_threads);
+
+/*
  * Address-resolution probe (for tests): runs the same device resolution code as the decode
  * kernels ([CrossPool] §3.1: logical KV address -> physical page) and writes, for every
  * sequence b and token t < ctx_lens[b] with a resident block, the region index and the byte

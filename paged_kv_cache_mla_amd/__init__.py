@@ -6,7 +6,7 @@ loads nothing; the first call loads the library and raises if it has not been bu
 """
 
 from .api import (BF16, F32, DecodeStep, KvattnError, Pool, block_bytes, decode_partial,
-                  merge_lse, partition_count, resolve_offsets)
+                  host_partial, merge_lse, partition_count, resolve_offsets)
 
 __all__ = ["BF16", "F32", "DecodeStep", "KvattnError", "Pool", "block_bytes", "decode_partial",
-           "merge_lse", "partition_count", "resolve_offsets"]
+           "host_partial", "merge_lse", "partition_count", "resolve_offsets"]

@@ -13,7 +13,7 @@ from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
 __all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets",
-           "partition_count", "block_bytes", "KvattnError", "BF16", "F32"]
+           "partition_count", "block_bytes", "host_partial", "KvattnError", "BF16", "F32"]
 
 
 def _i32p(arr):
@@ -155,6 +155,39 @@ def resolve_offsets(pool, table_dev, max_blocks, ctx_lens_dev, max_tokens, regio
                                     int(max_blocks), _dptr(ctx_lens_dev), int(max_tokens),
                                     _dptr(region_out), _dptr(offset_out), _stream(stream))
     check(st, "resolve_offsets")
+
+
+def host_partial(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent, regions, q,
+                 num_q_heads, scale, table, tok_end, n_threads=0):
+    """CPU share of a decode step over host-resident blocks (numpy arrays): returns
+    (o [B, Hq, Dv] float32, lse [B, Hq] float32) over tokens [0, tok_end[b]) of each sequence.
+
+    `regions` are numpy arrays holding whole blocks (uint16 bf16 bit patterns or float32), in
+    the device pool's block layout; block ids run over them in order."""
+    lib = _lib.load()
+    lay = _layout(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent)
+    nbytes = block_bytes(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent)
+    arr = (_lib.Region * len(regions))()
+    keep = []
+    for i, r in enumerate(regions):
+        r = np.ascontiguousarray(r)
+        keep.append(r)
+        arr[i].base = ctypes.c_void_p(r.ctypes.data)
+        arr[i].num_blocks = int(r.nbytes // nbytes)
+    qh = np.ascontiguousarray(q)
+    tab = np.ascontiguousarray(np.asarray(table, np.int32))
+    te = _host_i32(tok_end)
+    bsz = int(te.shape[0])
+    dv = head_dim_v
+    o = np.empty((bsz, num_q_heads, dv), np.float32)
+    lse = np.empty((bsz, num_q_heads), np.float32)
+    st = lib.kvattn_host_partial(ctypes.byref(lay), arr, len(regions),
+                                 ctypes.c_void_p(qh.ctypes.data), F32 if dtype in ("f32", F32) else BF16,
+                                 bsz, int(num_q_heads), ctypes.c_float(scale), _i32p(tab),
+                                 int(tab.shape[1]), _i32p(te), ctypes.c_void_p(o.ctypes.data),
+                                 ctypes.c_void_p(lse.ctypes.data), int(n_threads))
+    check(st, "host_partial")
+    return o, lse
 
 
 class DecodeStep:

@@ -26,6 +26,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+# host code targets x86-64-v3 (AVX2 + FMA), present on every EPYC host of an MI355X
+HOST_CPU = ["-mavx2", "-mfma", "-fno-math-errno"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]
 
@@ -34,8 +36,8 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
         cmd = [HIPCC, *COMMON, *DEVICE, "-c", src, "-o", obj]
-    else:  # host-only C++ (the pool); no HIP headers involved
-        cmd = [HIPCC, *COMMON, "-x", "c++", "-c", src, "-o", obj]
+    else:  # host-only C++ (pool, host attention); no HIP headers involved
+        cmd = [HIPCC, *COMMON, *HOST_CPU, "-x", "c++", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -53,7 +55,7 @@ def build(verbose: bool = True) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-lpthread", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

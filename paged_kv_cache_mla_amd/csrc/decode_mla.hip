@@ -191,7 +191,6 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     // 4b. O^T for dims 8*c + e, c = 16*wv + row (row = MFMA row), e = 0..7
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-    const int c = 16 * wv + n;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       uint4 r4[4];
