@@ -289,6 +289,88 @@ kvattn_status kvattn_host_partial(const kvattn_layout* layout, const kvattn_regi
                                   int32_t n_threads);
 
 /*
+ * ---- CPU / GPU share policy ([InplaceKVCache] §5.2 Eq. 1, §5.3 Eq. 2) ----
+ *
+ * Cost model of one decode step whose sequence of already-placed length L is split with the
+ * CPU taking the oldest r * L tokens and the GPU the rest (§5.1):
+ *     T_CPU(r) = r * A * L + C_CPU,     T_GPU(r) = (1 - r) * B * L + C_GPU          (Eq. 1)
+ * A: CPU cost per KV token it reads; B: GPU cost per KV token routed to it (on the pages, the
+ * host-to-device transfer; here whatever the caller measures for its GPU side); C_CPU, C_GPU:
+ * fixed per-step overheads.  Any time unit, the same for all four.  Balancing the two gives
+ *     r(L) = min(1, max(0, B / (A + B) + (C_GPU - C_CPU) / ((A + B) * L)))          (Eq. 2)
+ * which tends to p = B / (A + B) for long sequences.
+ */
+typedef struct {
+  double cpu_cost;  /* A  >= 0 */
+  double gpu_cost;  /* B  >= 0, A + B > 0 */
+  double cpu_fixed; /* C_CPU (any sign) */
+  double gpu_fixed; /* C_GPU (any sign) */
+} kvattn_share_model;
+
+/*
+ * Eq. 2 for one length.  r_out (host) receives r(L) in [0, 1].
+ * E_INVAL: null pointers, a non-finite field, A < 0, B < 0, A + B == 0, or L not finite and > 0.
+ */
+kvattn_status kvattn_share_optimum(const kvattn_share_model* model, double placed_len,
+                                   double* r_out);
+
+/*
+ * Offline calibration ([InplaceKVCache] §5.3: the parameters are scanned at several data
+ * volumes for the target model): ordinary least-squares line through the points
+ * (tokens[i], seconds[i]), i < count, so that seconds ~ slope * tokens + intercept -- A and
+ * C_CPU from CPU timings, B and C_GPU from GPU ones.  Host arrays of doubles.
+ * E_INVAL: null pointers, count < 2, non-finite values, or all tokens[i] equal.
+ */
+kvattn_status kvattn_share_fit(const double* tokens, const double* seconds, int32_t count,
+                               double* slope, double* intercept);
+
+/*
+ * Share controller of one sequence (or of a batch whose sequences grow in step): where each
+ * batch of tokens leaving the GPU's staging window (the D-window of [InplaceKVCache] §4.2)
+ * is stored, so that the CPU's cumulative share R(L) follows r(L) (§5.3).
+ *  - kvattn_share_admit(L0, block_tokens): the prefill of L0 tokens is placed with the CPU
+ *    taking the oldest round(r(L0) * L0 / block_tokens) whole blocks (at most the whole blocks
+ *    of L0), so R(L0) = r(L0) up to one block; returns that token count.
+ *  - kvattn_share_observe(t, n): one measured CPU component latency t of a decode step that
+ *    read n CPU tokens.  The last `window` samples are kept; their sliding average gives A back
+ *    as (sum t - k * C_CPU) / sum n over the k samples held.
+ *  - kvattn_share_route(D): a batch of D tokens leaves the window.  If the window of samples is
+ *    full, A is first replaced by the back-computed value (kept unchanged when sum n == 0 or
+ *    the value is not > 0).  Then, with L the placed length and c the CPU tokens so far, the
+ *    target is r(L + D) * (L + D) (Eq. 2 with the current A); the batch goes to the CPU iff
+ *    c + D / 2 < target, i.e. iff that leaves c nearer the target (ties stay on the GPU).
+ *    While A, B and the overheads hold still the target grows by p * D per batch, so the CPU
+ *    takes a fraction p of the batches and R(L) stays within D / (2 L) of r(L); the pages'
+ *    R(L) = p + (R(L0) - p) * L0 / L is that with R(L0) = r(L0).  Already placed tokens never
+ *    move.
+ * Not thread-safe; one controller per caller thread or an external lock.
+ * Errors: E_INVAL for null pointers, an invalid model (as kvattn_share_optimum), window < 1 or
+ * > 65536, L0 < 0, block_tokens < 1, batch_tokens < 1, t or n non-finite or negative;
+ * E_STATE for route / observe before admit, or admit twice.
+ */
+typedef struct kvattn_share_ctl kvattn_share_ctl;
+
+typedef struct {
+  int64_t placed_tokens; /* L: tokens placed so far (prefill + routed batches) */
+  int64_t cpu_tokens;    /* c: of which on the CPU side */
+  int64_t cpu_batches;   /* routed batches sent to the CPU */
+  int64_t batches;       /* routed batches */
+  double cpu_cost;       /* A currently used */
+  double converged;      /* p = B / (A + B) with that A */
+  double target_share;   /* r(L) with that A (0 when L == 0) */
+  int32_t samples;       /* samples held in the window */
+} kvattn_share_state;
+
+kvattn_status kvattn_share_ctl_create(const kvattn_share_model* model, int32_t window,
+                                      kvattn_share_ctl** out);
+void kvattn_share_ctl_free(kvattn_share_ctl* ctl);
+kvattn_status kvattn_share_admit(kvattn_share_ctl* ctl, int64_t prefill_tokens,
+                                 int64_t block_tokens, int64_t* cpu_tokens);
+kvattn_status kvattn_share_observe(kvattn_share_ctl* ctl, double cpu_seconds, double cpu_tokens);
+kvattn_status kvattn_share_route(kvattn_share_ctl* ctl, int64_t batch_tokens, int32_t* to_cpu);
+kvattn_status kvattn_share_get_state(const kvattn_share_ctl* ctl, kvattn_share_state* out);
+
+/*
  * Address-resolution probe (for tests): runs the same device resolution code as the decode
  * kernels ([CrossPool] §3.1: logical KV address -> physical page) and writes, for every
  * sequence b and token t < ctx_lens[b] with a resident block, the region index and the byte

@@ -11,7 +11,8 @@ Sources (cited by tag):
   [InplaceKVCache] "Physically Partitioned KVCache Format for CPU-GPU Load Balancing in MoE
                    Inference" -- §4.1 block-organised regions, §4.2 the CPU returns only its
                    partial output and normalisers and the GPU merges, §5.1 sequence-dimension
-                   split with exact LSE merge, §6.1 exact attention with online softmax.
+                   split with exact LSE merge, §5.2-5.3 Eq. 1-2 the share policy
+                   (``oracle.share``), §6.1 exact attention with online softmax.
   [CrossPool]      "CrossPool: Efficient Multi-LLM Serving for Cold MoE Models through
                    KV-Cache and Weight Disaggregation" -- §3.1 paged KV interface over a
                    logical KV address space.
@@ -21,7 +22,8 @@ Sources (cited by tag):
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
 invariants, brute force at 50 digits, a library special case) or, for the allocator model,
 by ``tests/test_alloc_oracle.py`` (published SplitMix64 outputs, exhaustive permutation
-counts).  None is "parity unpinned".
+counts), or, for the share policy, by ``tests/test_share_policy.py`` (brute-force minimum of
+Eq. 1's step time, balance, limits, exact cost recovery, a library line fit).  None is "parity unpinned".
 """
 
 from .bf16 import bf16_bits_to_f64
@@ -30,6 +32,7 @@ from .attention import attend, merge, partial_over_range
 from .partition import partition_count, partition_ranges
 from .decode import decode_reference, decode_partials_reference, resolve_offsets_reference
 from . import alloc
+from . import share
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -46,4 +49,5 @@ __all__ = [
     "decode_partials_reference",
     "resolve_offsets_reference",
     "alloc",
+    "share",
 ]

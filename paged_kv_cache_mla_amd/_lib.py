@@ -39,6 +39,18 @@ class Region(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("num_blocks", ctypes.c_int64)]
 
 
+class ShareModel(ctypes.Structure):
+    _fields_ = [("cpu_cost", ctypes.c_double), ("gpu_cost", ctypes.c_double),
+                ("cpu_fixed", ctypes.c_double), ("gpu_fixed", ctypes.c_double)]
+
+
+class ShareState(ctypes.Structure):
+    _fields_ = [("placed_tokens", ctypes.c_int64), ("cpu_tokens", ctypes.c_int64),
+                ("cpu_batches", ctypes.c_int64), ("batches", ctypes.c_int64),
+                ("cpu_cost", ctypes.c_double), ("converged", ctypes.c_double),
+                ("target_share", ctypes.c_double), ("samples", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -62,6 +74,16 @@ _SIGNATURES = {
     "kvattn_resolve_offsets": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
     "kvattn_host_partial": (_I32, [ctypes.POINTER(Layout), ctypes.POINTER(Region), _I32, _P, _I32,
                                    _I32, _I32, ctypes.c_float, _PI32, _I32, _PI32, _P, _P, _I32]),
+    "kvattn_share_optimum": (_I32, [ctypes.POINTER(ShareModel), ctypes.c_double,
+                                    ctypes.POINTER(ctypes.c_double)]),
+    "kvattn_share_fit": (_I32, [_P, _P, _I32, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double)]),
+    "kvattn_share_ctl_create": (_I32, [ctypes.POINTER(ShareModel), _I32, ctypes.POINTER(_P)]),
+    "kvattn_share_ctl_free": (None, [_P]),
+    "kvattn_share_admit": (_I32, [_P, _I64, _I64, _PI64]),
+    "kvattn_share_observe": (_I32, [_P, ctypes.c_double, ctypes.c_double]),
+    "kvattn_share_route": (_I32, [_P, _I64, _PI32]),
+    "kvattn_share_get_state": (_I32, [_P, ctypes.POINTER(ShareState)]),
     "kvattn_last_error": (ctypes.c_char_p, []),
     "kvattn_version": (ctypes.c_char_p, []),
 }

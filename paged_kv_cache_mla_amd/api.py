@@ -13,7 +13,8 @@ from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
 __all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets",
-           "partition_count", "block_bytes", "host_partial", "KvattnError", "BF16", "F32"]
+           "partition_count", "block_bytes", "host_partial", "share_optimum", "share_fit",
+           "ShareController", "KvattnError", "BF16", "F32"]
 
 
 def _i32p(arr):
@@ -188,6 +189,73 @@ def host_partial(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent
                                  ctypes.c_void_p(lse.ctypes.data), int(n_threads))
     check(st, "host_partial")
     return o, lse
+
+
+def _share_model(cpu_cost, gpu_cost, cpu_fixed=0.0, gpu_fixed=0.0):
+    return _lib.ShareModel(float(cpu_cost), float(gpu_cost), float(cpu_fixed), float(gpu_fixed))
+
+
+def share_optimum(cpu_cost, gpu_cost, cpu_fixed, gpu_fixed, placed_len):
+    """r(L) of the balance of the two engines' step latencies (kvattn_share_optimum)."""
+    m = _share_model(cpu_cost, gpu_cost, cpu_fixed, gpu_fixed)
+    r = ctypes.c_double()
+    check(_lib.load().kvattn_share_optimum(ctypes.byref(m), float(placed_len), ctypes.byref(r)),
+          "share_optimum")
+    return r.value
+
+
+def share_fit(tokens, seconds):
+    """Least-squares (slope, intercept) of seconds ~ slope * tokens + intercept."""
+    x = np.ascontiguousarray(tokens, np.float64)
+    y = np.ascontiguousarray(seconds, np.float64)
+    if x.shape != y.shape or x.ndim != 1:
+        raise ValueError("tokens and seconds must be 1-D arrays of one length")
+    a, b = ctypes.c_double(), ctypes.c_double()
+    check(_lib.load().kvattn_share_fit(ctypes.c_void_p(x.ctypes.data), ctypes.c_void_p(y.ctypes.data),
+                                       int(x.shape[0]), ctypes.byref(a), ctypes.byref(b)), "share_fit")
+    return a.value, b.value
+
+
+class ShareController:
+    """Routing of tokens leaving the GPU staging window (kvattn_share_ctl_*)."""
+
+    def __init__(self, cpu_cost, gpu_cost, cpu_fixed=0.0, gpu_fixed=0.0, window=256):
+        self._lib = _lib.load()
+        m = _share_model(cpu_cost, gpu_cost, cpu_fixed, gpu_fixed)
+        h = ctypes.c_void_p()
+        check(self._lib.kvattn_share_ctl_create(ctypes.byref(m), int(window), ctypes.byref(h)),
+              "share_ctl_create")
+        self._h = h
+
+    def close(self):
+        h = getattr(self, "_h", None)  # absent if the constructor raised
+        if h:
+            self._lib.kvattn_share_ctl_free(h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def admit(self, prefill_tokens, block_tokens):
+        c = ctypes.c_int64()
+        check(self._lib.kvattn_share_admit(self._h, int(prefill_tokens), int(block_tokens),
+                                           ctypes.byref(c)), "share_admit")
+        return c.value
+
+    def observe(self, cpu_seconds, cpu_tokens):
+        check(self._lib.kvattn_share_observe(self._h, float(cpu_seconds), float(cpu_tokens)),
+              "share_observe")
+
+    def route(self, batch_tokens):
+        to_cpu = ctypes.c_int32()
+        check(self._lib.kvattn_share_route(self._h, int(batch_tokens), ctypes.byref(to_cpu)),
+              "share_route")
+        return bool(to_cpu.value)
+
+    def state(self):
+        s = _lib.ShareState()
+        check(self._lib.kvattn_share_get_state(self._h, ctypes.byref(s)), "share_get_state")
+        return {f: getattr(s, f) for f, _ in _lib.ShareState._fields_}
 
 
 class DecodeStep:

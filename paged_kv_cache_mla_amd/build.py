@@ -26,8 +26,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
-# host code targets x86-64-v3 (AVX2 + FMA), present on every EPYC host of an MI355X
-HOST_CPU = ["-mavx2", "-mfma", "-fno-math-errno"]
+# host code targets x86-64-v3 (AVX2 + FMA), present on every EPYC host of an MI355X; no
+# implicit contraction into FMA, so scalar double arithmetic (the share policy) rounds exactly
+# as written -- vector FMAs are spelled out where they are wanted
+HOST_CPU = ["-mavx2", "-mfma", "-fno-math-errno", "-ffp-contract=off"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]
 
