@@ -12,16 +12,20 @@
 // Restated for this library: work items are (sequence, KV head, chunk of whole blocks); each
 // block of an item is widened to fp32 into small tiles laid out so that both products run
 // over contiguous memory with AVX2 (plain loops for partial blocks and fp32 caches), then
-// folded into a per-head online softmax.  Items are taken by the threads from a shared counter; each item's
-// partial is merged into the sequence's result in chunk order, so the output does not depend
-// on the thread count or timing.
+// folded into a per-head online softmax.  Items are taken by persistent worker threads from a
+// shared counter; each item's partial is merged into the sequence's result in chunk order, so
+// the output does not depend on the thread count or timing.
 // Pure C++17 with no HIP dependency.
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
+#include <condition_variable>
 #include <cstdint>
 #include <cstring>
+#include <functional>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -35,6 +39,90 @@ namespace {
 
 constexpr int kMaxGroup = 16;        // query heads per KV head
 constexpr int kChunkTokens = 1024;   // tokens per work item (rounded to whole blocks)
+
+// Persistent workers: the per-step fixed cost of the CPU share (thread start-up, first touch of
+// the partial workspace) is paid once per process, not once per decode step.  Between calls a
+// worker spins on the job counter for kSpinNs before sleeping on a condition variable, so calls
+// that follow each other within a decode loop wake it without a system call.  One call runs at
+// a time (call_mu); the workspace vectors are reused across calls under that lock.  The pool is
+// never destroyed (its threads sleep until the process ends).
+class WorkerPool {
+ public:
+  static WorkerPool& get() {
+    static WorkerPool* p = new WorkerPool();
+    return *p;
+  }
+
+  // Runs fn(i) for i in [0, n) on n workers, the calling thread being worker 0; returns when all
+  // have finished.  The caller holds call_mu.
+  void run(int n, const std::function<void(int)>& fn) {
+    while ((int)threads_.size() < n - 1) {
+      const int idx = (int)threads_.size() + 1;
+      threads_.emplace_back([this, idx] { loop(idx); });
+      threads_.back().detach();
+    }
+    job_ = &fn;
+    pending_.store(n - 1, std::memory_order_relaxed);
+    // generation and worker count change together, so a worker never pairs one call's count
+    // with another call's generation; the release publishes job_ and pending_
+    const uint64_t gen = (state_.load(std::memory_order_relaxed) >> 8) + 1;
+    state_.store(gen << 8 | (uint64_t)n, std::memory_order_release);
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      if (sleeping_ > 0) cv_.notify_all();
+    }
+    fn(0);
+    while (pending_.load(std::memory_order_acquire) != 0) _mm_pause();
+  }
+
+  std::mutex call_mu;
+  std::vector<float> ws_o, ws_m, ws_l;
+
+ private:
+  static constexpr int64_t kSpinNs = 2000000;  // 2 ms
+
+  // state_ = generation << 8 | workers of that generation's call
+  void loop(int idx) {
+    uint64_t seen = 0;  // generation last handled
+    for (;;) {
+      uint64_t w = state_.load(std::memory_order_acquire);
+      if (w >> 8 == seen) {
+        const auto t0 = std::chrono::steady_clock::now();
+        int polls = 0;
+        while ((w = state_.load(std::memory_order_acquire)) >> 8 == seen) {
+          _mm_pause();
+          if (++polls == 256) {
+            polls = 0;
+            if (std::chrono::duration_cast<std::chrono::nanoseconds>(
+                    std::chrono::steady_clock::now() - t0).count() > kSpinNs)
+              break;
+          }
+        }
+        if (w >> 8 == seen) {
+          std::unique_lock<std::mutex> lk(mu_);
+          ++sleeping_;
+          cv_.wait(lk, [&] { return (w = state_.load(std::memory_order_acquire)) >> 8 != seen; });
+          --sleeping_;
+        }
+      }
+      seen = w >> 8;
+      // a worker of this generation's call: the caller waits for it before the next call, so
+      // job_ is still this call's job
+      if ((uint64_t)idx < (w & 255)) {
+        (*job_)(idx);
+        pending_.fetch_sub(1, std::memory_order_acq_rel);
+      }
+    }
+  }
+
+  std::mutex mu_;
+  std::condition_variable cv_;
+  int sleeping_ = 0;  // guarded by mu_
+  std::vector<std::thread> threads_;
+  const std::function<void(int)>* job_ = nullptr;
+  std::atomic<uint64_t> state_{0};
+  std::atomic<int> pending_{0};
+};
 
 struct HostCtx {
   kvattn_layout L;
@@ -368,11 +456,20 @@ extern "C" kvattn_status kvattn_host_partial(const kvattn_layout* layout,
   first_item[(size_t)batch * c.hkv] = (int)item_b.size();
   const int nitems = (int)item_b.size();
   const int dk = layout->head_dim_k, dv = layout->head_dim_v, g = c.group;
-  std::vector<float> part_o((size_t)nitems * g * dv), part_m((size_t)nitems * g), part_l((size_t)nitems * g);
+  WorkerPool& wp = WorkerPool::get();
+  std::lock_guard<std::mutex> call_lock(wp.call_mu);
+  if (wp.ws_o.size() < (size_t)nitems * g * dv) wp.ws_o.resize((size_t)nitems * g * dv);
+  if (wp.ws_m.size() < (size_t)nitems * g) {
+    wp.ws_m.resize((size_t)nitems * g);
+    wp.ws_l.resize((size_t)nitems * g);
+  }
+  float* part_o = wp.ws_o.data();
+  float* part_m = wp.ws_m.data();
+  float* part_l = wp.ws_l.data();
 
   std::atomic<int> next{0};
   const bool fast = layout->kv_dtype == KVATTN_BF16 && bs % 8 == 0;
-  auto worker = [&]() {
+  const std::function<void(int)> worker = [&](int) {
     std::vector<float> kt((size_t)dk * bs), vt((size_t)bs * dv), qf((size_t)g * dk);
     std::vector<float> sbuf((size_t)g * bs);
     State st;
@@ -411,11 +508,8 @@ extern "C" kvattn_status kvattn_host_partial(const kvattn_layout* layout,
       }
     }
   };
-  const int nt = std::max(1, std::min<int>(n_threads > 0 ? n_threads : (int)std::thread::hardware_concurrency(), nitems));
-  std::vector<std::thread> pool;
-  for (int i = 1; i < nt; ++i) pool.emplace_back(worker);
-  worker();
-  for (auto& th : pool) th.join();
+  const int nt = std::max(1, std::min({n_threads > 0 ? n_threads : (int)std::thread::hardware_concurrency(), nitems, 255}));
+  wp.run(nt, worker);
 
   // exact merge of each (sequence, head)'s chunk partials, in chunk order
   for (int b = 0; b < batch; ++b)

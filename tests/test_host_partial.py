@@ -82,3 +82,34 @@ def test_host_partial_validation():
         _run(case, case.regions, case.region_blocks, case.table,
              np.array([case.max_blocks * case.block_size + 1, 1, 1, 1], np.int32))
     assert e.value.status == _lib.E_INVAL
+
+
+def test_host_partial_repeated_calls_changing_thread_counts_and_concurrent_callers():
+    """The persistent workers: back-to-back calls with growing and shrinking worker counts, and
+    two caller threads at once (calls are serialised inside the library), all give the same
+    bits."""
+    import threading
+
+    case = make_case("split_128k", "small")
+    ref = _run(case, case.ext_regions, case.ext_region_blocks, case.ext_table, case.tok_begin, 1)
+    counts = [1, 7, 3, 12, 2, 8, 1, 16, 5] * 12
+    for th in counts:
+        o, lse = _run(case, case.ext_regions, case.ext_region_blocks, case.ext_table,
+                      case.tok_begin, th)
+        assert np.array_equal(o, ref[0]) and np.array_equal(lse, ref[1])
+    bad = []
+
+    def caller(seed):
+        rng = np.random.default_rng(seed)
+        for _ in range(40):
+            o, lse = _run(case, case.ext_regions, case.ext_region_blocks, case.ext_table,
+                          case.tok_begin, int(rng.integers(1, 9)))
+            if not (np.array_equal(o, ref[0]) and np.array_equal(lse, ref[1])):
+                bad.append(seed)
+
+    ts = [threading.Thread(target=caller, args=(s,)) for s in (1, 2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad
