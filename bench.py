@@ -275,6 +275,165 @@ def cpu_baseline(case, budget_s=10.0):
                       f"{done_tokens} tokens, {nbytes} KV bytes, float64 numpy, {dt:.1f} s"}
 
 
+def _time_steps(torch, fn, steps, warmup):
+    """Wall-clock ms per call of fn() run back to back, bracketed by device synchronisation."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def host_share_bench(args):
+    """The sequence split of the Mixtral-shaped 4 x 128K workload with a native CPU share,
+    sized by the share policy: calibrate the per-position costs and fixed overheads of both
+    sides (least-squares lines over several token counts), take r from the balance of the
+    two step latencies, then time overlapped steps (device share on the GPU, host share on
+    the CPU at the same time, merged on the GPU) at that r and around it."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.api import DecodeStep, HostShare, share_fit, share_optimum
+    from paged_kv_cache_mla_amd.session import DeviceCase, SplitStep
+    from synth import make_case
+
+    _lib.load()
+    torch.cuda.set_device(0)
+    # one CPU is left to the HIP runtime's own threads
+    threads = args.host_threads or max(1, min(16, len(os.sched_getaffinity(0))) - 1)
+    log("[share] generating split_128k (full) with every block on the device")
+    # r = 0: the device pool holds every block; the same blocks in host memory (case.regions,
+    # case.table) serve the host share, so any split point can be timed on one upload
+    case = make_case("split_128k", "full", r=0.0)
+    G = GROUP_PARTS["split_128k"]
+    dc = DeviceCase(case, group_parts=G)
+    L, bs, B = int(case.ctx_lens[0]), case.block_size, case.batch
+
+    def dstep(begin):
+        return DecodeStep(dc.pool, dc.table, case.ctx_lens, case.part_tokens, case.num_q_heads,
+                          case.head_dim_v, tok_begin=[begin] * B, group_parts=G)
+
+    def hshare(end):
+        return HostShare(bs, case.num_kv_heads, case.head_dim_k, case.head_dim_v, case.dtype,
+                         case.latent, case.regions, case.num_q_heads, case.scale, case.table,
+                         [end] * B, n_threads=threads)
+
+    def median(xs):
+        return float(np.median(np.asarray(xs)))
+
+    # Eq. 1's GPU component: the device partial's latency from its enqueue, over device
+    # shares of 1/4 .. all of the context (the range where it is linear in the positions)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_pts = []
+    for m in (L // 4, L // 2, 3 * L // 4, L):
+        st = dstep(L - m)
+        vals = []
+        for i in range(args.warmup + 10):
+            ev0.record()
+            st.partial(dc.q, dc.q_dtype, case.scale)
+            ev1.record()
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                vals.append(ev0.elapsed_time(ev1))
+        gpu_pts.append((m, median(vals)))
+        log(f"[share] gpu partial over {m} positions: {gpu_pts[-1][1] * 1e3:.1f} us")
+    B_cost, C_gpu = share_fit([p[0] for p in gpu_pts], [p[1] for p in gpu_pts])
+    # Eq. 1's CPU component, measured inside split steps: from the device partial's enqueue
+    # until the merge of the host partial is enqueued (q out, host compute, launch)
+    def cpu_points(ns):
+        pts = []
+        for n in ns:
+            ss = SplitStep(dstep(n), dc.q, dc.q_dtype, case.scale, hshare(n), timing=True)
+            vals, host = [], []
+            for i in range(args.warmup + 10):
+                ss.run()
+                torch.cuda.synchronize()
+                if i >= args.warmup:
+                    vals.append(ss.component_ms()[1])
+                    host.append(ss.host_ms)
+            pts.append((n, median(vals), median(host)))
+            log(f"[share] cpu share of {n} positions: component {pts[-1][1] * 1e3:.1f} us "
+                f"(host compute {pts[-1][2] * 1e3:.1f} us)")
+        return pts
+
+    # a wide scan first, then a local one around the first estimate: the host's cost per
+    # position is not constant over two decades of share sizes, and Eq. 2 needs the slope
+    # and intercept where the balance falls
+    cpu_wide = cpu_points((256, 1024, 4096, 8192))
+    A_cost, C_cpu = share_fit([p[0] for p in cpu_wide], [p[1] for p in cpu_wide])
+    r_wide = share_optimum(A_cost, B_cost, C_cpu, C_gpu, L)
+    n0 = max(2 * bs, int(round(r_wide * L / bs)) * bs)
+    local = sorted({max(bs, int(round(n0 * m / bs)) * bs) for m in (0.5, 0.75, 1.0, 1.5, 2.0)})
+    cpu_pts = cpu_points(local)
+    A_cost, C_cpu = share_fit([p[0] for p in cpu_pts], [p[1] for p in cpu_pts])
+    r_pol = share_optimum(A_cost, B_cost, C_cpu, C_gpu, L)
+    begin_pol = int(round(r_pol * L / bs)) * bs
+    log(f"[share] wide fit r={r_wide:.5f}; local A={A_cost * 1e6:.2f} ns/pos C_cpu={C_cpu * 1e3:.1f} us  "
+        f"B={B_cost * 1e6:.3f} ns/pos C_gpu={C_gpu * 1e3:.1f} us  r={r_pol:.5f} -> {begin_pol}")
+
+    gpu_only = _time_steps(torch, lambda: dc.step.run(dc.q, dc.q_dtype, case.scale),
+                           args.steps, args.warmup)
+    cands = {0, begin_pol, 256, 512, 768, 1024, 1536, 2048, 4096}
+    for m in (0.5, 0.75, 1.25, 1.5, 2):
+        cands.add(int(round(begin_pol * m / bs)) * bs)
+    sweep = []
+    for begin, q_first in [(b, qf) for b in sorted(cands) for qf in (False, True)]:
+        ss = SplitStep(dstep(begin), dc.q, dc.q_dtype, case.scale, hshare(begin), q_first=q_first)
+        host = []
+
+        def one():
+            ss.run()
+            host.append(ss.host_ms)
+        ms = _time_steps(torch, one, args.steps, args.warmup)
+        o, l = ss.step.o_out, ss.step.lse_out
+        if not (torch.isfinite(o).all() and torch.isfinite(l).all()):
+            raise RuntimeError("non-finite output")
+        # the two components of the step in place (synchronised steps, so the timed loop
+        # above is not perturbed by the timing events)
+        sst = SplitStep(dstep(begin), dc.q, dc.q_dtype, case.scale, hshare(begin), timing=True,
+                        q_first=q_first)
+        comp = []
+        for i in range(8):
+            sst.run()
+            torch.cuda.synchronize()
+            if i >= 3:
+                comp.append(sst.component_ms())
+        sweep.append({"cpu_positions": begin, "r": round(begin / L, 6), "q_first": q_first,
+                      "ms_per_step": round(ms, 5),
+                      "host_ms": round(float(np.mean(host[-args.steps:])), 5),
+                      "t_gpu_us": round(median([c[0] for c in comp]) * 1e3, 1),
+                      "t_cpu_us": round(median([c[1] for c in comp]) * 1e3, 1)})
+        log(f"[share] split at {begin}{' q_first' if q_first else ''}: {ms * 1e3:.1f} us/step "
+            f"(host {sweep[-1]['host_ms'] * 1e3:.1f} us)")
+    best = min(sweep, key=lambda e: e["ms_per_step"])
+    per_pos = case.kv_bytes_per_token() * B
+    out = {
+        "mode": "host_share",
+        "workload": "split_128k: " + DESCR["split_128k"].split(",")[0] + ", B4 x 128K, CPU share by policy",
+        "host_threads": threads,
+        "calibration": {
+            "gpu": {"B_ns_per_position": round(B_cost * 1e6, 4), "C_gpu_us": round(C_gpu * 1e3, 2),
+                    "points_us": [[n, round(ms * 1e3, 2)] for n, ms in gpu_pts]},
+            "cpu": {"A_ns_per_position": round(A_cost * 1e6, 3), "C_cpu_us": round(C_cpu * 1e3, 2),
+                    "points_us": [[n, round(ms * 1e3, 2)] for n, ms, _ in cpu_pts],
+                    "host_compute_us": [[n, round(h * 1e3, 2)] for n, _, h in cpu_pts],
+                    "wide_points_us": [[n, round(ms * 1e3, 2)] for n, ms, _ in cpu_wide],
+                    "wide_r": round(r_wide, 6),
+                    "host_GBps_at_largest": round(cpu_pts[-1][0] * per_pos / (cpu_pts[-1][2] * 1e-3) / 1e9, 2)},
+        },
+        "policy": {"r": round(r_pol, 6), "p": round(B_cost / (A_cost + B_cost), 6),
+                   "cpu_positions": begin_pol},
+        "gpu_only_ms_per_step": round(gpu_only, 5),
+        "sweep": sweep,
+        "measured_best": best,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +444,11 @@ def main():
     ap.add_argument("--group-parts", type=int, default=0,
                     help="partitions merged on chip per written partial (default: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-share", choices=["off", "policy"], default="off",
+                    help="policy: time the split workload with a native CPU share sized by the "
+                         "share policy (prints its own JSON line instead of the bench line)")
+    ap.add_argument("--host-threads", type=int, default=0,
+                    help="host threads for --host-share (default: min(16, usable CPUs) - 1)")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
                     help="write profiles/decode_partial_and_merge.<workload>.md from rocprofv3 "
                          "output directories (no GPU needed) and exit")
@@ -299,6 +463,10 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this library has "
               "no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+
+    if args.host_share == "policy":
+        host_share_bench(args)
+        return
 
     import numpy as np
     import torch

@@ -244,7 +244,10 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
  * of positive weight the result is o = 0, lse = -INFINITY.
  *   o_part, lse_part, nparts_dev  as written by kvattn_decode_partial (device)
  *   o_ext, lse_ext   device fp32 [batch][num_q_heads][dv] and [batch][num_q_heads], or both
- *                    NULL
+ *                    NULL.  They may be the device addresses of mapped, coherent pinned host
+ *                    memory (hipHostMalloc with hipHostMallocMapped | hipHostMallocCoherent):
+ *                    the merge then reads a host-computed partial over the host link with no
+ *                    copy; the caller must have finished writing it before this call.
  *   o_out            device fp32 [batch][num_q_heads][dv]
  *   lse_out          device fp32 [batch][num_q_heads] or NULL
  * Errors: E_INVAL (null required pointers, one of o_ext/lse_ext NULL but not the other,
@@ -275,11 +278,14 @@ kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,
  *                  valid ids of the host regions (E_RANGE otherwise)
  *   tok_end        host [batch] int32, 0 <= tok_end[b] <= max_blocks * bs
  *   o_out, lse_out host fp32 [batch][num_q_heads][Dv] and [batch][num_q_heads]
- *   n_threads      worker threads (<= 0: the hardware concurrency)
+ *   n_threads      threads working on the call, the caller's included, at most 255 (<= 0: the
+ *                  CPUs the process may run on, at most 64)
  * Work items are (sequence, KV head, 1024-token chunk of whole blocks) taken by the threads
  * from a shared counter; the chunk partials are merged in chunk order, so the result does not
- * depend on n_threads.  Synchronous; all memory is the caller's.  Errors: E_INVAL, E_RANGE,
- * E_UNSUPPORTED (q_dtype != kv_dtype, more than 16 query heads per KV head).
+ * depend on n_threads.  The worker threads persist between calls (they spin for about 2 ms
+ * after a call, then sleep), and calls from several threads run one after another.
+ * Synchronous; all memory is the caller's.  Errors: E_INVAL, E_RANGE, E_UNSUPPORTED (q_dtype
+ * != kv_dtype, more than 16 query heads per KV head).
  */
 kvattn_status kvattn_host_partial(const kvattn_layout* layout, const kvattn_region* host_regions,
                                   int32_t n_regions, const void* q, int32_t q_dtype,

@@ -13,7 +13,7 @@ from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
 __all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets",
-           "partition_count", "block_bytes", "host_partial", "share_optimum", "share_fit",
+           "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
            "ShareController", "KvattnError", "BF16", "F32"]
 
 
@@ -30,9 +30,11 @@ def _host_i32(x):
 
 
 def _dptr(t):
-    """Device address of a torch tensor (or None)."""
+    """Device address of a torch tensor, or an int address passed through (or None)."""
     if t is None:
         return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
     if not t.is_cuda:
         raise ValueError("expected a device tensor")
     if not t.is_contiguous():
@@ -189,6 +191,42 @@ def host_partial(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent
                                  ctypes.c_void_p(lse.ctypes.data), int(n_threads))
     check(st, "host_partial")
     return o, lse
+
+
+class HostShare:
+    """kvattn_host_partial with its arguments marshalled once, for repeated decode steps over
+    the same host blocks: `compute(q, o_out, lse_out)` fills caller-owned float32 arrays (for
+    instance views of pinned host tensors) with the partial over tokens [0, tok_end[b])."""
+
+    def __init__(self, block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent, regions,
+                 num_q_heads, scale, table, tok_end, n_threads=0):
+        self._lib = _lib.load()
+        self._lay = _layout(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent)
+        nbytes = block_bytes(block_size, num_kv_heads, head_dim_k, head_dim_v, dtype, latent)
+        self._regions = [np.ascontiguousarray(r) for r in regions]
+        self._arr = (_lib.Region * len(self._regions))()
+        for i, r in enumerate(self._regions):
+            self._arr[i].base = ctypes.c_void_p(r.ctypes.data)
+            self._arr[i].num_blocks = int(r.nbytes // nbytes)
+        self._table = np.ascontiguousarray(np.asarray(table, np.int32))
+        self.tok_end = _host_i32(tok_end)
+        self.batch = int(self.tok_end.shape[0])
+        self.hq = int(num_q_heads)
+        self.dv = int(head_dim_v)
+        self._qdt = F32 if dtype in ("f32", F32) else BF16
+        self._scale = ctypes.c_float(scale)
+        self._n_threads = int(n_threads)
+
+    def compute(self, q, o_out, lse_out):
+        for a, shape in ((o_out, (self.batch, self.hq, self.dv)), (lse_out, (self.batch, self.hq))):
+            if a.dtype != np.float32 or a.shape != shape or not a.flags.c_contiguous:
+                raise ValueError(f"output must be a C-contiguous float32 array of shape {shape}")
+        st = self._lib.kvattn_host_partial(
+            ctypes.byref(self._lay), self._arr, len(self._regions), ctypes.c_void_p(q.ctypes.data),
+            self._qdt, self.batch, self.hq, self._scale, _i32p(self._table),
+            int(self._table.shape[1]), _i32p(self.tok_end), ctypes.c_void_p(o_out.ctypes.data),
+            ctypes.c_void_p(lse_out.ctypes.data), self._n_threads)
+        check(st, "host_partial")
 
 
 def _share_model(cpu_cost, gpu_cost, cpu_fixed=0.0, gpu_fixed=0.0):

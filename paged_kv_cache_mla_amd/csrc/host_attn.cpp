@@ -31,6 +31,7 @@
 #include <vector>
 
 #include <immintrin.h>
+#include <sched.h>
 
 #include "pool_internal.h"
 
@@ -41,9 +42,10 @@ constexpr int kMaxGroup = 16;        // query heads per KV head
 constexpr int kChunkTokens = 1024;   // tokens per work item (rounded to whole blocks)
 
 // Persistent workers: the per-step fixed cost of the CPU share (thread start-up, first touch of
-// the partial workspace) is paid once per process, not once per decode step.  Between calls a
-// worker spins on the job counter for kSpinNs before sleeping on a condition variable, so calls
-// that follow each other within a decode loop wake it without a system call.  One call runs at
+// the partial workspace) is paid once per process, not once per decode step.  After a call a
+// worker that took part spins on the job word for kSpinNs before sleeping on a condition
+// variable, so calls that follow each other within a decode loop wake it without a system
+// call; workers a call did not need go straight back to sleep.  One call runs at
 // a time (call_mu); the workspace vectors are reused across calls under that lock.  The pool is
 // never destroyed (its threads sleep until the process ends).
 class WorkerPool {
@@ -56,6 +58,10 @@ class WorkerPool {
   // Runs fn(i) for i in [0, n) on n workers, the calling thread being worker 0; returns when all
   // have finished.  The caller holds call_mu.
   void run(int n, const std::function<void(int)>& fn) {
+    if (n <= 1) {  // nothing to hand out: no worker is woken
+      fn(0);
+      return;
+    }
     while ((int)threads_.size() < n - 1) {
       const int idx = (int)threads_.size() + 1;
       threads_.emplace_back([this, idx] { loop(idx); });
@@ -83,13 +89,14 @@ class WorkerPool {
 
   // state_ = generation << 8 | workers of that generation's call
   void loop(int idx) {
-    uint64_t seen = 0;  // generation last handled
+    uint64_t seen = 0;     // generation last handled
+    bool worked = false;   // took part in that generation's call: spin before sleeping
     for (;;) {
       uint64_t w = state_.load(std::memory_order_acquire);
       if (w >> 8 == seen) {
         const auto t0 = std::chrono::steady_clock::now();
         int polls = 0;
-        while ((w = state_.load(std::memory_order_acquire)) >> 8 == seen) {
+        while (worked && (w = state_.load(std::memory_order_acquire)) >> 8 == seen) {
           _mm_pause();
           if (++polls == 256) {
             polls = 0;
@@ -108,7 +115,8 @@ class WorkerPool {
       seen = w >> 8;
       // a worker of this generation's call: the caller waits for it before the next call, so
       // job_ is still this call's job
-      if ((uint64_t)idx < (w & 255)) {
+      worked = (uint64_t)idx < (w & 255);
+      if (worked) {
         (*job_)(idx);
         pending_.fetch_sub(1, std::memory_order_acq_rel);
       }
@@ -508,7 +516,13 @@ extern "C" kvattn_status kvattn_host_partial(const kvattn_layout* layout,
       }
     }
   };
-  const int nt = std::max(1, std::min({n_threads > 0 ? n_threads : (int)std::thread::hardware_concurrency(), nitems, 255}));
+  int want = n_threads;
+  if (want <= 0) {
+    cpu_set_t set;
+    want = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : 1;
+    want = std::min(want, 64);
+  }
+  const int nt = std::max(1, std::min({want, nitems, 255}));
   wp.run(nt, worker);
 
   // exact merge of each (sequence, head)'s chunk partials, in chunk order

@@ -273,3 +273,56 @@ def test_full_size_sampled_sequences(name, kw, seqs):
     assert float(np.max(np.abs(lse[seqs] - lse_ref[seqs]))) <= oc.lse_tol(case)
     # every output finite and every lse finite
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------- native host share, merged
+HOST_THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+def _split_step(case, group_parts):
+    from paged_kv_cache_mla_amd.api import HostShare
+    from paged_kv_cache_mla_amd.session import DeviceCase, SplitStep
+    dc = DeviceCase(case, group_parts=group_parts)
+    hs = HostShare(case.block_size, case.num_kv_heads, case.head_dim_k, case.head_dim_v,
+                   case.dtype, case.latent, case.ext_regions, case.num_q_heads, case.scale,
+                   case.ext_table, case.tok_begin, n_threads=HOST_THREADS)
+    return dc, SplitStep(dc.step, dc.q, dc.q_dtype, case.scale, hs)
+
+
+@pytest.mark.parametrize("variant,kw,seqs,group_parts", [
+    ("small", {}, None, 1), ("small", {"r": 0.25}, None, 4),
+    ("full", {"r": 0.5}, [0, 3], 8)])
+def test_split_step_with_native_host_share(variant, kw, seqs, group_parts):
+    """The CPU share computed by kvattn_host_partial while the device computes its own, then
+    merged on the device straight from mapped host memory: every step of a back-to-back run
+    with changing queries matches the oracle, and repeating a query repeats the bits."""
+    import copy
+
+    from synth.workloads import bf16_round_bits
+    _say(f"[split-step] {variant} {kw} group_parts={group_parts}")
+    case = make_case("split_128k", variant, **kw)
+    dc, ss = _split_step(case, group_parts)
+    # four steps back to back, each with its own q (both mapped buffers are used twice, so a
+    # stale host partial would show), then the first q again
+    rng = np.random.default_rng(7)
+    qs = [case.q] + [bf16_round_bits(rng.standard_normal(case.q.shape, dtype=np.float32))
+                     for _ in range(3)] + [case.q]
+    outs = []
+    for q in qs:
+        dc.q.copy_(torch.from_numpy(q.view(np.int16)))
+        o, lse = ss.run()
+        outs.append((o.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    assert int(dc.step.err.item()) == 0
+    assert torch.equal(outs[-1][0], outs[0][0]) and torch.equal(outs[-1][1], outs[0][1])
+    sel = list(range(case.batch)) if seqs is None else seqs
+    for i, q in enumerate(qs[:-1] if variant == "small" else qs[:2]):
+        c = copy.copy(case)
+        c.q = q
+        o_ref, lse_ref = oc.full_reference(c, seqs)
+        o = outs[i][0].cpu().numpy()
+        lse = outs[i][1].cpu().numpy()
+        err = oc.out_error(case, o[sel], o_ref[sel])
+        _say(f"[split-step] step {i} out error {err:.3e}")
+        assert err <= oc.out_tol(case)
+        assert float(np.max(np.abs(lse[sel] - lse_ref[sel]))) <= oc.lse_tol(case)
