@@ -261,6 +261,31 @@ kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,
                                void* hip_stream);
 
 /*
+ * Paged KV append ([InplaceKVCache] §4.1: the block is the unit of write-time placement;
+ * §4.2: new decode entries are written first into the GPU's staging window and take part in
+ * attention from the next step).  For every sequence b and j < n_new, writes the new token
+ * j at logical index t = pos_dev[b] + j into block table_dev[b][t / bs], slot t % bs, in the
+ * pool's block layout (header comment above): K(h, t, :) and V(h, t, :) for every KV head,
+ * or the latent row C(t, :) of an MLA cache.
+ *   k_new     device [batch][n_new][Hkv][Dk] (latent: [batch][n_new][Dk]), element type
+ *             kv_dtype, 16-byte aligned
+ *   v_new     device [batch][n_new][Hkv][Dv]; NULL exactly for a latent cache
+ *   table_dev device [batch][max_blocks] int32; pos_dev device [batch] int32
+ *   err_dev   device int32 or NULL: KVATTN_ERR_BAD_SEQ is OR-ed in for a token whose index
+ *             is negative or beyond max_blocks * bs, KVATTN_ERR_BAD_BLOCK for a token whose
+ *             table entry is not a valid id; such tokens are not written.
+ * Blocks must have been claimed (kvattn_block_table, or a kvattn_kvstore reservation); the
+ * kernel does not allocate.  Appends to distinct slots may share a launch; two writes to one
+ * slot in one launch leave either value.  Errors: E_INVAL (null pointers, v_new present for a
+ * latent cache or missing otherwise, sizes < 1, batch * n_new >= 2^31, misalignment),
+ * E_UNSUPPORTED (kv_dtype != the pool's), E_HIP.
+ */
+kvattn_status kvattn_append_kv(const kvattn_pool* pool, const void* k_new, const void* v_new,
+                               int32_t kv_dtype, int32_t batch, int32_t n_new,
+                               const int32_t* table_dev, int32_t max_blocks,
+                               const int32_t* pos_dev, int32_t* err_dev, void* hip_stream);
+
+/*
  * CPU share of a decode step, computed on the host ([InplaceKVCache] §5.1: the engines take
  * disjoint token ranges of every sequence over all heads; §4.2: the CPU returns only its
  * partial output and normaliser, which the GPU merges; §6.1: the CPU kernel reads the blocks

@@ -30,6 +30,7 @@ from .bf16 import bf16_bits_to_f64
 from .layout import Layout, block_elems, gather_sequence, token_k_offset
 from .attention import attend, merge, partial_over_range
 from .partition import partition_count, partition_ranges
+from .write import write_tokens
 from .decode import decode_reference, decode_partials_reference, resolve_offsets_reference
 from . import alloc
 from . import share
@@ -45,6 +46,7 @@ __all__ = [
     "partial_over_range",
     "partition_count",
     "partition_ranges",
+    "write_tokens",
     "decode_reference",
     "decode_partials_reference",
     "resolve_offsets_reference",

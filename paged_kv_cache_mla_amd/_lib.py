@@ -72,6 +72,7 @@ _SIGNATURES = {
                                      _PI32, _PI32, _PI32, _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_merge_lse": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_resolve_offsets": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
+    "kvattn_append_kv": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P]),
     "kvattn_host_partial": (_I32, [ctypes.POINTER(Layout), ctypes.POINTER(Region), _I32, _P, _I32,
                                    _I32, _I32, ctypes.c_float, _PI32, _I32, _PI32, _P, _P, _I32]),
     "kvattn_share_optimum": (_I32, [ctypes.POINTER(ShareModel), ctypes.c_double,

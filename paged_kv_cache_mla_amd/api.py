@@ -12,7 +12,7 @@ import numpy as np
 from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
-__all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets",
+__all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets", "append_kv",
            "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
            "ShareController", "KvattnError", "BF16", "F32"]
 
@@ -149,6 +149,18 @@ def merge_lse(o_part, lse_part, nparts, batch, num_q_heads, max_parts, dv, o_out
                               int(num_q_heads), int(max_parts), int(dv), _dptr(o_ext),
                               _dptr(lse_ext), _dptr(o_out), _dptr(lse_out), _stream(stream))
     check(st, "merge_lse")
+
+
+def append_kv(pool, k_new, v_new, kv_dtype, table_dev, max_blocks, pos_dev, err=None,
+              stream=None):
+    """Write new tokens' K/V (device tensors [B][n_new][Hkv][D], v_new None for a latent
+    cache) at logical positions pos_dev[b] + j through table_dev (kvattn_append_kv)."""
+    lib = _lib.load()
+    batch, n_new = int(k_new.shape[0]), int(k_new.shape[1])
+    st = lib.kvattn_append_kv(pool.handle, _dptr(k_new), _dptr(v_new), int(kv_dtype), batch, n_new,
+                              _dptr(table_dev), int(max_blocks), _dptr(pos_dev), _dptr(err),
+                              _stream(stream))
+    check(st, "append_kv")
 
 
 def resolve_offsets(pool, table_dev, max_blocks, ctx_lens_dev, max_tokens, region_out,

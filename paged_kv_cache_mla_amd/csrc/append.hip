@@ -1,0 +1,91 @@
+// Paged KV append: write the key/value entries of new tokens into their blocks through a
+// block table ([InplaceKVCache] §4.1: the block is the unit of write-time placement; §4.2:
+// new decode entries are first written into the GPU's staging window, from which they take
+// part in attention at once).
+//
+// One workgroup per (sequence, new token).  Its threads copy the K part as 16-byte chunks
+// (the block stores K chunk-major, so each chunk of one token is one aligned 16-byte slot)
+// and the V part element by element (V is stored token-fastest, so one token's values are
+// scattered with a stride of the block size).  A token of a latent (MLA) cache is one row of
+// 16-byte chunks.  The volume is tiny (one token is 2 KiB for 4 KV heads of 128 bf16
+// dimensions); the kernel is bound by launch and store latency.
+
+#include "device_common.h"
+
+namespace kvattn {
+
+struct AppendArgs {
+  RegionTable rt;
+  const char* k_new;     // [B][n_new][Hkv][Dk] (latent: [B][n_new][Dk])
+  const char* v_new;     // [B][n_new][Hkv][Dv] or null (latent)
+  const int32_t* table;  // [B][max_blocks]
+  const int32_t* pos;    // [B]: logical index of each sequence's first new token
+  int32_t* err;
+  int32_t batch, n_new, max_blocks;
+  int32_t hkv, dk, dv, bs, bs_shift, esize, latent;
+};
+
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+  const int b = blockIdx.x / a.n_new;
+  const int j = blockIdx.x - b * a.n_new;
+  const int64_t t = (int64_t)a.pos[b] + j;
+  if (t < 0 || (t >> a.bs_shift) >= a.max_blocks) {
+    if (threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    return;
+  }
+  const int32_t pid = a.table[(int64_t)b * a.max_blocks + (t >> a.bs_shift)];
+  if (!valid_block(a.rt, pid)) {
+    if (threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+    return;
+  }
+  char* blk = const_cast<char*>(block_ptr(a.rt, pid));
+  const int ts = (int)(t & (a.bs - 1));
+  const int x = 16 / a.esize;          // elements per 16-byte chunk
+  const int kchunks = a.dk / x;        // chunks of one head's key
+  const int heads = a.latent ? 1 : a.hkv;
+  const int64_t row = (int64_t)b * a.n_new + j;
+  // K (or the latent): chunk c of head h goes to chunk slot ((h * kchunks + c) * bs + ts)
+  const char* ksrc = a.k_new + row * heads * a.dk * a.esize;
+  for (int i = threadIdx.x; i < heads * kchunks; i += blockDim.x) {
+    const uint4 v = *reinterpret_cast<const uint4*>(ksrc + (int64_t)i * 16);
+    *reinterpret_cast<uint4*>(blk + (((int64_t)i * a.bs + ts) << 4)) = v;
+  }
+  if (a.latent) return;
+  // V: element (h, d) goes to element hkv * bs * dk + (h * dv + d) * bs + ts
+  const char* vsrc = a.v_new + row * a.hkv * a.dv * a.esize;
+  char* vdst = blk + (int64_t)a.hkv * a.bs * a.dk * a.esize;
+  for (int i = threadIdx.x; i < a.hkv * a.dv; i += blockDim.x) {
+    const int64_t off = ((int64_t)i * a.bs + ts) * a.esize;
+    if (a.esize == 2)
+      *reinterpret_cast<uint16_t*>(vdst + off) = reinterpret_cast<const uint16_t*>(vsrc)[i];
+    else
+      *reinterpret_cast<uint32_t*>(vdst + off) = reinterpret_cast<const uint32_t*>(vsrc)[i];
+  }
+}
+
+hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const void* k_new,
+                         const void* v_new, const int32_t* table, const int32_t* pos,
+                         int32_t* err, int32_t batch, int32_t n_new, int32_t max_blocks,
+                         int bs_shift, hipStream_t st) {
+  AppendArgs a{};
+  a.rt = rt;
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.table = table;
+  a.pos = pos;
+  a.err = err;
+  a.batch = batch;
+  a.n_new = n_new;
+  a.max_blocks = max_blocks;
+  a.hkv = L.num_kv_heads;
+  a.dk = L.head_dim_k;
+  a.dv = L.head_dim_v;
+  a.bs = L.block_size;
+  a.bs_shift = bs_shift;
+  a.esize = L.kv_dtype == KVATTN_F32 ? 4 : 2;
+  a.latent = L.latent;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((int64_t)batch * n_new)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvattn

@@ -16,6 +16,10 @@ hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, h
 hipError_t launch_mla(const DecodeArgs& a, dim3 grid, hipStream_t st);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const void* k_new,
+                         const void* v_new, const int32_t* table, const int32_t* pos,
+                         int32_t* err, int32_t batch, int32_t n_new, int32_t max_blocks,
+                         int bs_shift, hipStream_t st);
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -260,4 +264,29 @@ extern "C" kvattn_status kvattn_resolve_offsets(const kvattn_pool* pool, const i
                      ctx_lens_dev, max_tokens, log2_exact(pool->layout.block_size), region_out,
                      offset_out);
   return hip_status(hipGetLastError(), "resolve_offsets launch");
+}
+
+extern "C" kvattn_status kvattn_append_kv(const kvattn_pool* pool, const void* k_new,
+                                          const void* v_new, int32_t kv_dtype, int32_t batch,
+                                          int32_t n_new, const int32_t* table_dev,
+                                          int32_t max_blocks, const int32_t* pos_dev,
+                                          int32_t* err_dev, void* hip_stream) {
+  using namespace kvattn;
+  clear_error();
+  if (!pool || !k_new || !table_dev || !pos_dev)
+    return set_error(KVATTN_E_INVAL, "append_kv: null argument");
+  const kvattn_layout& L = pool->layout;
+  if (L.latent ? v_new != nullptr : v_new == nullptr)
+    return set_error(KVATTN_E_INVAL, "append_kv: v_new must be NULL exactly for a latent cache");
+  if (batch < 1 || n_new < 1 || max_blocks < 1 || (int64_t)batch * n_new > 0x7fffffff)
+    return set_error(KVATTN_E_INVAL, "append_kv: bad sizes");
+  if (kv_dtype != L.kv_dtype)
+    return set_error(KVATTN_E_UNSUPPORTED, "append_kv: kv_dtype must equal the cache dtype");
+  const uintptr_t esize = L.kv_dtype == KVATTN_F32 ? 4 : 2;
+  if (!aligned16(k_new) || (v_new && (reinterpret_cast<uintptr_t>(v_new) % esize) != 0))
+    return set_error(KVATTN_E_INVAL, "append_kv: k_new must be 16-byte aligned, v_new element-aligned");
+  return hip_status(launch_append(region_table(pool), L, k_new, v_new, table_dev, pos_dev, err_dev,
+                                  batch, n_new, max_blocks, log2_exact(L.block_size),
+                                  static_cast<hipStream_t>(hip_stream)),
+                    "append_kv launch");
 }

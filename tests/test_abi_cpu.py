@@ -259,3 +259,25 @@ def test_partition_count_edge_values(lib):
     assert lib.kvattn_partition_count(1, 0, 16) == 1
     assert lib.kvattn_partition_count(2 ** 31 - 1, 0, 1) == 2 ** 31 - 1
     assert lib.kvattn_partition_count(10, 11, 16) == -1
+
+
+def test_append_validation_without_gpu(lib):
+    vp = ctypes.c_void_p
+    gqa = _pool(8, 0, bs=16, hkv=2, d=64)
+    mla = Pool(64, 1, 576, 512, "bf16", True, [(FAKE, 4)])
+
+    def call(pool, **over):
+        a = dict(k=vp(FAKE), v=vp(FAKE), dt=_lib.BF16, b=2, n=1, t=vp(FAKE), mb=4, pos=vp(FAKE))
+        a.update(over)
+        return lib.kvattn_append_kv(pool.handle, a["k"], a["v"], a["dt"], a["b"], a["n"], a["t"],
+                                    a["mb"], a["pos"], None, None)
+    assert call(gqa, k=None) == _lib.E_INVAL
+    assert call(gqa, v=None) == _lib.E_INVAL                  # V required for a GQA cache
+    assert call(mla) == _lib.E_INVAL                          # no V for a latent cache
+    assert call(gqa, dt=_lib.F32) == _lib.E_UNSUPPORTED
+    assert call(gqa, k=vp(FAKE + 8)) == _lib.E_INVAL          # K must be 16-byte aligned
+    assert call(gqa, v=vp(FAKE + 1)) == _lib.E_INVAL          # V element-aligned
+    assert call(gqa, n=0) == _lib.E_INVAL
+    assert call(gqa, b=0) == _lib.E_INVAL
+    assert call(gqa, b=65536, n=65536) == _lib.E_INVAL        # 2^32 tokens in one launch
+    assert call(gqa, t=None) == _lib.E_INVAL
