@@ -402,6 +402,83 @@ kvattn_status kvattn_share_route(kvattn_share_ctl* ctl, int64_t batch_tokens, in
 kvattn_status kvattn_share_get_state(const kvattn_share_ctl* ctl, kvattn_share_state* out);
 
 /*
+ * ---- Write-time placement across the two engines ([InplaceKVCache] §4.1, §4.2, §5.3) ----
+ *
+ * A kvattn_kvstore tracks, for each of `batch` sequences, three lists of whole blocks:
+ *   cpu  blocks of the host pool holding the CPU share (read by kvattn_host_partial);
+ *   gpu  blocks of the device pool holding the GPU share;
+ *   win  blocks of the device pool forming the staging window (the D-window), which receives
+ *        every new token; its tokens start at slot 0 of its first block, so only its last
+ *        filled block may be partial.
+ * Every placed block holds bs tokens.  Tokens are never moved once placed (§4.2).  Decode
+ * attention is the same for any order of the tokens (keys carry their position already), so
+ * each engine reads its own tokens through its own view:
+ *   GPU view  table = gpu ++ win (the partial block last), length = bs * |gpu| + w
+ *   CPU view  table = cpu, length = bs * |cpu|
+ * where w is the number of tokens in the window.  A new token goes to logical index
+ * bs * |gpu| + w of the GPU view, i.e. into the window (kvattn_append_kv with the GPU view).
+ *
+ * Operations (host bookkeeping; only kvattn_kvstore_place_prefill and kvattn_kvstore_flush
+ * enqueue device work):
+ *  - reserve(n_new): n_new host [batch], each >= 0.  Claims device blocks so that window b
+ *    has room for n_new[b] more tokens (ceil((w + n_new[b]) / bs) window blocks), sequences
+ *    in order, all or nothing
+ *    (E_POOL_EXHAUSTED leaves everything unchanged; E_INVAL if a GPU view would exceed
+ *    max_blocks).  Claims come from kvattn_block_table in allocate mode, one sequence at a
+ *    time.  *changed = 1 if the GPU view tables changed.
+ *  - commit(n_new): records n_new[b] appended tokens for each sequence b (E_STATE without
+ *    room; nothing changes then).
+ *  - place_prefill: once, before any flush.  For each sequence with a controller, the
+ *    controller admits the w_full = bs * floor(w / bs) tokens of the window's full blocks
+ *    (kvattn_share_admit with block_tokens = bs); that many of the oldest blocks go to the
+ *    CPU share and the other full blocks to the GPU share; a partial block stays in the
+ *    window.  Without a controller every full block goes to the GPU share.
+ *  - flush: while a window holds at least D = window_tokens tokens, its first D / bs blocks
+ *    form a batch; the controller routes it (kvattn_share_route(D); no controller: GPU).  A
+ *    GPU batch moves to the GPU share in place (no copy); a CPU batch is copied block by
+ *    block into newly claimed host blocks and its device blocks are released.
+ *  - The _plan forms do the bookkeeping only and return the copies as pairs (device id,
+ *    host id) in copy order; the others then enqueue one hipMemcpyAsync (device to host) per
+ *    pair on hip_stream.  A released device block may be claimed again by the next reserve:
+ *    its copy must be enqueued (plan callers: performed) before any later write to it, which
+ *    holds when appends go to the same stream.  The host must not read a CPU block before its
+ *    copy has completed (synchronise the stream).
+ *  - Before the host pool could run short, flush and place_prefill check that it has free
+ *    blocks for the worst case (every pending batch to the CPU) and otherwise fail with
+ *    E_POOL_EXHAUSTED, changing nothing; likewise E_INVAL if in that case a CPU view would
+ *    exceed max_blocks, or if `copies` (host int32 [max_copies][2]) has fewer than that many
+ *    pairs.
+ *  - views: host arrays gpu_table / cpu_table [batch][max_blocks] (ABSENT after the list),
+ *    gpu_len / cpu_len [batch].
+ *  - free: returns every block the store holds to its pool (the pools must still exist).
+ * The controllers (ctls[b], NULL for none; the array may be NULL; one distinct, not yet
+ * admitted controller per sequence) and pools are borrowed and must outlive the store.  Not thread-safe.  Both pools must have the same layout.
+ * Errors: E_INVAL (null pointers, batch < 1, max_blocks < 1, window_tokens not a positive
+ * multiple of bs, an n_new entry < 0, layouts differ), E_STATE (commit beyond the reservation,
+ * place_prefill twice or after a flush), E_POOL_EXHAUSTED, E_HIP (copy enqueue failed; the
+ * store is then unspecified).
+ */
+typedef struct kvattn_kvstore kvattn_kvstore;
+
+kvattn_status kvattn_kvstore_create(kvattn_pool* dev_pool, kvattn_pool* host_pool, int32_t batch,
+                                    int32_t window_tokens, int32_t max_blocks,
+                                    kvattn_share_ctl* const* ctls, kvattn_kvstore** out);
+void kvattn_kvstore_free(kvattn_kvstore* store);
+kvattn_status kvattn_kvstore_reserve(kvattn_kvstore* store, const int32_t* n_new,
+                                     int32_t* changed);
+kvattn_status kvattn_kvstore_commit(kvattn_kvstore* store, const int32_t* n_new);
+kvattn_status kvattn_kvstore_place_prefill_plan(kvattn_kvstore* store, int32_t* copies,
+                                                int32_t max_copies, int32_t* n_copies,
+                                                int32_t* changed);
+kvattn_status kvattn_kvstore_place_prefill(kvattn_kvstore* store, void* hip_stream,
+                                           int32_t* changed);
+kvattn_status kvattn_kvstore_flush_plan(kvattn_kvstore* store, int32_t* copies,
+                                        int32_t max_copies, int32_t* n_copies, int32_t* changed);
+kvattn_status kvattn_kvstore_flush(kvattn_kvstore* store, void* hip_stream, int32_t* changed);
+kvattn_status kvattn_kvstore_views(const kvattn_kvstore* store, int32_t* gpu_table,
+                                   int32_t* gpu_len, int32_t* cpu_table, int32_t* cpu_len);
+
+/*
  * Address-resolution probe (for tests): runs the same device resolution code as the decode
  * kernels ([CrossPool] §3.1: logical KV address -> physical page) and writes, for every
  * sequence b and token t < ctx_lens[b] with a resident block, the region index and the byte

@@ -5,10 +5,10 @@ The compute path is the C-ABI library ``libkvattn.so`` (hand-written HIP kernels
 loads nothing; the first call loads the library and raises if it has not been built.
 """
 
-from .api import (BF16, F32, DecodeStep, KvattnError, Pool, ShareController, block_bytes,
-                  decode_partial, host_partial, merge_lse, partition_count, resolve_offsets,
-                  share_fit, share_optimum)
+from .api import (BF16, F32, DecodeStep, HostShare, KVStore, KvattnError, Pool,
+                  ShareController, append_kv, block_bytes, decode_partial, host_partial,
+                  merge_lse, partition_count, resolve_offsets, share_fit, share_optimum)
 
-__all__ = ["BF16", "F32", "DecodeStep", "KvattnError", "Pool", "ShareController", "block_bytes",
-           "decode_partial", "host_partial", "merge_lse", "partition_count", "resolve_offsets",
-           "share_fit", "share_optimum"]
+__all__ = ["BF16", "F32", "DecodeStep", "HostShare", "KVStore", "KvattnError", "Pool",
+           "ShareController", "append_kv", "block_bytes", "decode_partial", "host_partial",
+           "merge_lse", "partition_count", "resolve_offsets", "share_fit", "share_optimum"]

@@ -85,6 +85,16 @@ _SIGNATURES = {
     "kvattn_share_observe": (_I32, [_P, ctypes.c_double, ctypes.c_double]),
     "kvattn_share_route": (_I32, [_P, _I64, _PI32]),
     "kvattn_share_get_state": (_I32, [_P, ctypes.POINTER(ShareState)]),
+    "kvattn_kvstore_create": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.POINTER(_P),
+                                     ctypes.POINTER(_P)]),
+    "kvattn_kvstore_free": (None, [_P]),
+    "kvattn_kvstore_reserve": (_I32, [_P, _PI32, _PI32]),
+    "kvattn_kvstore_commit": (_I32, [_P, _PI32]),
+    "kvattn_kvstore_place_prefill_plan": (_I32, [_P, _PI32, _I32, _PI32, _PI32]),
+    "kvattn_kvstore_place_prefill": (_I32, [_P, _P, _PI32]),
+    "kvattn_kvstore_flush_plan": (_I32, [_P, _PI32, _I32, _PI32, _PI32]),
+    "kvattn_kvstore_flush": (_I32, [_P, _P, _PI32]),
+    "kvattn_kvstore_views": (_I32, [_P, _PI32, _PI32, _PI32, _PI32]),
     "kvattn_last_error": (ctypes.c_char_p, []),
     "kvattn_version": (ctypes.c_char_p, []),
 }

@@ -14,7 +14,7 @@ from ._lib import BF16, F32, KvattnError, check
 
 __all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets", "append_kv",
            "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
-           "ShareController", "KvattnError", "BF16", "F32"]
+           "ShareController", "KVStore", "KvattnError", "BF16", "F32"]
 
 
 def _i32p(arr):
@@ -306,6 +306,87 @@ class ShareController:
         s = _lib.ShareState()
         check(self._lib.kvattn_share_get_state(self._h, ctypes.byref(s)), "share_get_state")
         return {f: getattr(s, f) for f, _ in _lib.ShareState._fields_}
+
+
+class KVStore:
+    """Write-time placement of each sequence's KV across a device pool (GPU share and the
+    staging window) and a host pool (CPU share), routed by one share controller per sequence
+    (kvattn_kvstore_*).  `controllers` is a list of ShareController or None per sequence."""
+
+    def __init__(self, dev_pool, host_pool, batch, window_tokens, max_blocks, controllers=None):
+        self._lib = _lib.load()
+        self.batch, self.max_blocks = int(batch), int(max_blocks)
+        self._ctls = list(controllers) if controllers is not None else [None] * self.batch
+        if len(self._ctls) != self.batch:
+            raise ValueError("one controller (or None) per sequence")
+        arr = (ctypes.c_void_p * self.batch)(*[None if c is None else c._h.value for c in self._ctls])
+        h = ctypes.c_void_p()
+        check(self._lib.kvattn_kvstore_create(dev_pool.handle, host_pool.handle, self.batch,
+                                              int(window_tokens), self.max_blocks, arr,
+                                              ctypes.byref(h)), "kvstore_create")
+        self._pools = (dev_pool, host_pool)  # keep the pools alive as long as the store
+        self._h = h
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.kvattn_kvstore_free(h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _counts(self, n_new):
+        n = np.full(self.batch, n_new, np.int32) if np.isscalar(n_new) else _host_i32(n_new)
+        if n.shape != (self.batch,):
+            raise ValueError("n_new: a scalar or one count per sequence")
+        return n
+
+    def reserve(self, n_new):
+        n = self._counts(n_new)
+        changed = ctypes.c_int32()
+        check(self._lib.kvattn_kvstore_reserve(self._h, _i32p(n), ctypes.byref(changed)),
+              "kvstore_reserve")
+        return bool(changed.value)
+
+    def commit(self, n_new):
+        n = self._counts(n_new)
+        check(self._lib.kvattn_kvstore_commit(self._h, _i32p(n)), "kvstore_commit")
+
+    def _plan(self, fn, what):
+        cap = self.batch * self.max_blocks
+        copies = np.empty((cap, 2), np.int32)
+        n, changed = ctypes.c_int32(), ctypes.c_int32()
+        check(fn(self._h, _i32p(copies), cap, ctypes.byref(n), ctypes.byref(changed)), what)
+        return bool(changed.value), copies[:n.value].copy()
+
+    def place_prefill_plan(self):
+        """Bookkeeping only: returns (changed, copies [n, 2] of (device id, host id))."""
+        return self._plan(self._lib.kvattn_kvstore_place_prefill_plan, "kvstore_place_prefill")
+
+    def flush_plan(self):
+        return self._plan(self._lib.kvattn_kvstore_flush_plan, "kvstore_flush")
+
+    def place_prefill(self, stream=None):
+        changed = ctypes.c_int32()
+        check(self._lib.kvattn_kvstore_place_prefill(self._h, _stream(stream), ctypes.byref(changed)),
+              "kvstore_place_prefill")
+        return bool(changed.value)
+
+    def flush(self, stream=None):
+        changed = ctypes.c_int32()
+        check(self._lib.kvattn_kvstore_flush(self._h, _stream(stream), ctypes.byref(changed)),
+              "kvstore_flush")
+        return bool(changed.value)
+
+    def views(self):
+        """(gpu_table [B, max_blocks], gpu_len [B], cpu_table [B, max_blocks], cpu_len [B])."""
+        shape = (self.batch, self.max_blocks)
+        gt, ct = np.empty(shape, np.int32), np.empty(shape, np.int32)
+        gl, cl = np.empty(self.batch, np.int32), np.empty(self.batch, np.int32)
+        check(self._lib.kvattn_kvstore_views(self._h, _i32p(gt), _i32p(gl), _i32p(ct), _i32p(cl)),
+              "kvstore_views")
+        return gt, gl, ct, cl
 
 
 class DecodeStep:

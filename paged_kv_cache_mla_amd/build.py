@@ -30,6 +30,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # implicit contraction into FMA, so scalar double arithmetic (the share policy) rounds exactly
 # as written -- vector FMAs are spelled out where they are wanted
 HOST_CPU = ["-mavx2", "-mfma", "-fno-math-errno", "-ffp-contract=off"]
+# host files that enqueue copies use the HIP runtime API (no device code)
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HOST_HIP = ["-D__HIP_PLATFORM_AMD__", "-isystem", os.path.join(ROCM, "include")]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]
 
@@ -38,8 +41,8 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
         cmd = [HIPCC, *COMMON, *DEVICE, "-c", src, "-o", obj]
-    else:  # host-only C++ (pool, host attention); no HIP headers involved
-        cmd = [HIPCC, *COMMON, *HOST_CPU, "-x", "c++", "-c", src, "-o", obj]
+    else:  # host-only C++ (pool, host attention, share policy, placement store)
+        cmd = [HIPCC, *COMMON, *HOST_CPU, *HOST_HIP, "-x", "c++", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
