@@ -114,7 +114,9 @@ int64_t kvattn_block_bytes(const kvattn_layout* layout);
 kvattn_status kvattn_pool_alloc(const kvattn_layout* layout, const kvattn_region* regions,
                                 int32_t n_regions, uint64_t seed, kvattn_pool** out);
 
-/* Release the pool's host metadata; the regions stay the caller's.  NULL is ignored. */
+/* Release the pool's host metadata; the regions stay the caller's.  NULL is ignored.  While a
+ * kvattn_kvstore still holds the pool, the release is deferred until the last such store is
+ * freed (the pool must not be used by the caller after this call either way). */
 void kvattn_pool_free(kvattn_pool* pool);
 
 /*
@@ -450,7 +452,8 @@ kvattn_status kvattn_share_get_state(const kvattn_share_ctl* ctl, kvattn_share_s
  *    pairs.
  *  - views: host arrays gpu_table / cpu_table [batch][max_blocks] (ABSENT after the list),
  *    gpu_len / cpu_len [batch].
- *  - free: returns every block the store holds to its pool (the pools must still exist).
+ *  - free: returns every block the store holds to its pool; a pool whose kvattn_pool_free
+ *    came first is deleted then (the store holds both pools until it is freed).
  * The controllers (ctls[b], NULL for none; the array may be NULL; one distinct, not yet
  * admitted controller per sequence) and pools are borrowed and must outlive the store.  Not thread-safe.  Both pools must have the same layout.
  * Errors: E_INVAL (null pointers, batch < 1, max_blocks < 1, window_tokens not a positive

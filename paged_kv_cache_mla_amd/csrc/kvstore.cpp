@@ -161,6 +161,8 @@ kvattn_status kvattn_kvstore_create(kvattn_pool* dev_pool, kvattn_pool* host_poo
   if (ctls)
     for (int32_t b = 0; b < batch; ++b) s->ctl[(size_t)b] = ctls[b];
   s->seq.resize((size_t)batch);
+  kvattn::pool_borrow(dev_pool);
+  kvattn::pool_borrow(host_pool);
   *out = s;
   return KVATTN_OK;
 }
@@ -172,6 +174,8 @@ void kvattn_kvstore_free(kvattn_kvstore* s) {
     kvattn::release(s->dev, q.gpu.data(), (int32_t)q.gpu.size());
     kvattn::release(s->dev, q.win.data(), (int32_t)q.win.size());
   }
+  kvattn::pool_unborrow(s->dev);
+  kvattn::pool_unborrow(s->host);
   delete s;
 }
 

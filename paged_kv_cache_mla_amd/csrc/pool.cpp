@@ -26,6 +26,12 @@ namespace kvattn {
 
 static thread_local std::string g_last_error;
 
+void pool_borrow(kvattn_pool* p) { ++p->borrowers; }
+
+void pool_unborrow(kvattn_pool* p) {
+  if (--p->borrowers == 0 && p->free_requested) delete p;
+}
+
 kvattn_status set_error(kvattn_status code, const std::string& msg) {
   g_last_error = msg;
   return code;
@@ -120,7 +126,14 @@ kvattn_status kvattn_pool_alloc(const kvattn_layout* layout, const kvattn_region
   return KVATTN_OK;
 }
 
-void kvattn_pool_free(kvattn_pool* pool) { delete pool; }
+void kvattn_pool_free(kvattn_pool* pool) {
+  if (!pool) return;
+  if (pool->borrowers > 0) {  // a store still holds it: deleted when the last one is freed
+    pool->free_requested = true;
+    return;
+  }
+  delete pool;
+}
 
 int64_t kvattn_pool_num_free(const kvattn_pool* pool) {
   return pool ? (int64_t)pool->free_stack.size() : -1;

@@ -18,7 +18,16 @@ struct kvattn_pool {
   std::vector<int32_t> free_stack;  // next block handed out = back()
   std::vector<int32_t> refcount;
   int64_t shared_blocks = 0;        // blocks with refcount >= 2
+  int32_t borrowers = 0;            // placement stores holding this pool
+  bool free_requested = false;      // kvattn_pool_free called while borrowed
 };
+
+namespace kvattn {
+// A placement store takes / gives back a pool; giving back the last borrow of a pool whose
+// free was requested deletes it.
+void pool_borrow(kvattn_pool* p);
+void pool_unborrow(kvattn_pool* p);
+}  // namespace kvattn
 
 namespace kvattn {
 

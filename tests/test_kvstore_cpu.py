@@ -163,3 +163,17 @@ def test_store_create_validation():
     _expect(_lib.E_INVAL, KVStore, dev, host, 1, 32, 0)
     s = KVStore(dev, host, 2, 32, 4)
     _expect(_lib.E_INVAL, s.reserve, [-1, 0])
+
+
+def test_pool_freed_before_its_store_is_deferred():
+    """kvattn_pool_free on a pool a store still holds defers the deletion until the store is
+    freed (which still returns its blocks to that pool)."""
+    dev, host, _, _ = _pools(16, 16, 21)
+    store = KVStore(dev, host, 2, 32, 8)
+    store.reserve([40, 7])
+    store.commit([40, 7])
+    dev.close()
+    host.close()
+    gt, gl, ct, cl = store.views()
+    assert list(gl) == [40, 7]
+    store.close()
