@@ -132,3 +132,120 @@ def test_append_flags_absent_and_out_of_range_tokens_and_writes_the_rest():
             oracle.write_tokens(layout, regions, region_blocks, table[b], t, k[b, j:j + 1],
                                 v[b, j:j + 1])
     assert np.array_equal(_host(dev[0], np.uint16), regions[0])
+
+
+# ---------------------------------------------------------------- a decode session
+SESSIONS = {
+    # layout, hq, window D, prefill lengths, decode steps, check every
+    "gqa": (Layout(16, 2, 128, 128, "bf16", False), 8, 64, [100, 37, 0], 300, 60),
+    "mla": (Layout(64, 1, 576, 512, "bf16", True), 16, 128, [300, 64, 5], 300, 100),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SESSIONS))
+def test_decode_session_with_window_eviction_and_both_views(name):
+    """Prefill and decode tokens are appended into the staging window; D-token batches are
+    evicted to the GPU share or, copied to pinned host blocks, to the CPU share, as each
+    sequence's share controller routes them.  At checkpoints the GPU view is decoded on the
+    device and the CPU view on the host, and the merge matches the oracle's attention over
+    every token appended so far; the two views hold exactly the appended tokens."""
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.api import (DecodeStep, KVStore, Pool, ShareController,
+                                            append_kv, host_partial)
+    layout, hq, D, prefill, steps, every = SESSIONS[name]
+    _say(f"[session] {name}")
+    rng = np.random.default_rng(77)
+    B, bs = len(prefill), layout.block_size
+    hkv = 1 if layout.latent else layout.num_kv_heads
+    max_blocks = -(-(max(prefill) + steps) // bs) + D // bs + 2
+    nel = block_elems(layout)
+    dev_blocks, host_blocks = B * max_blocks + 3, B * max_blocks + 2
+    dev_region = torch.zeros(dev_blocks * nel, dtype=torch.int16, device="cuda")
+    host_region = torch.zeros(host_blocks * nel, dtype=torch.int16, pin_memory=True)
+    args = (bs, layout.num_kv_heads, layout.head_dim_k, layout.head_dim_v, "bf16", layout.latent)
+    dev_pool = Pool(*args, [(dev_region.data_ptr(), dev_blocks)], seed=5)
+    host_pool = Pool(*args, [(host_region.data_ptr(), host_blocks)], seed=6)
+    ctls = [ShareController(2.0, 1.0, 0.0, 0.0, window=4) for _ in range(B)]   # p = 1/3
+    store = KVStore(dev_pool, host_pool, B, D, max_blocks, ctls)
+    hist_k = [np.zeros((0, hkv, layout.head_dim_k), np.uint16) for _ in range(B)]
+    hist_v = [np.zeros((0, hkv, layout.head_dim_v), np.uint16) for _ in range(B)]
+
+    def tokens(n):
+        k = _random_storage(rng, (n, hkv, layout.head_dim_k), layout)
+        v = k[:, :, :layout.head_dim_v].copy() if layout.latent else \
+            _random_storage(rng, (n, hkv, layout.head_dim_v), layout)
+        return k, v
+
+    def upload_views():
+        gt, gl, ct, cl = store.views()
+        return _dev(gt), gl, ct, cl
+
+    def append(b_list, ks, vs, n, table_dev, gl):
+        for b, k, v in zip(b_list, ks, vs):
+            if n == 0:
+                continue
+            kd = _dev(k[None, :, 0, :] if layout.latent else k[None])
+            vd = None if layout.latent else _dev(v[None])
+            pos = torch.tensor([int(gl[b])], dtype=torch.int32, device="cuda")
+            append_kv(dev_pool, kd, vd, _lib.BF16, table_dev[b:b + 1], max_blocks, pos, err)
+            hist_k[b] = np.concatenate([hist_k[b], k])
+            hist_v[b] = np.concatenate([hist_v[b], v])
+
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # prefill: ragged lengths, one append per sequence, then placement
+    store.reserve(prefill)
+    table_dev, gl, ct, cl = upload_views()
+    for b in range(B):
+        k, v = tokens(prefill[b])
+        append([b], [k], [v], prefill[b], table_dev, gl)
+    store.commit(prefill)
+    store.place_prefill()
+    table_dev, gl, ct, cl = upload_views()
+    cpu_batches = 0
+    for step in range(1, steps + 1):
+        if store.reserve(1):
+            table_dev, gl, ct, cl = upload_views()
+        kv = [tokens(1) for _ in range(B)]
+        append(range(B), [k for k, _ in kv], [v for _, v in kv], 1, table_dev, gl)
+        store.commit(1)
+        if store.flush():
+            cpu_batches += 1
+        table_dev, gl, ct, cl = upload_views()
+        if step % every and step != steps:
+            continue
+        torch.cuda.synchronize()        # appends and copies to host blocks done
+        assert int(err.item()) == 0
+        assert np.array_equal(gl + cl, [len(h) for h in hist_k])
+        # the two views hold exactly the appended tokens (as a multiset of K rows)
+        dev_np = dev_region.cpu().numpy().view(np.uint16)
+        host_np = host_region.numpy().view(np.uint16)
+        gt_host = table_dev.cpu().numpy()
+        for b in range(B):
+            kg, _ = oracle.gather_sequence(layout, [dev_np], [dev_blocks], gt_host[b], 0, int(gl[b]))
+            kc, _ = oracle.gather_sequence(layout, [host_np], [host_blocks], ct[b], 0, int(cl[b]))
+            got = np.concatenate([kg, kc]).reshape(len(hist_k[b]), -1)
+            exp = oracle.bf16_bits_to_f64(hist_k[b]).reshape(len(hist_k[b]), -1)
+            assert np.array_equal(got[np.lexsort(got.T[::-1])], exp[np.lexsort(exp.T[::-1])])
+        # attention: GPU view on the device, CPU view on the host, merged on the device
+        q = _random_storage(rng, (B, hq, layout.head_dim_k), layout)
+        scale = 1.0 / np.sqrt(192.0 if layout.latent else layout.head_dim_k)
+        ds = DecodeStep(dev_pool, gt_host, gl, [bs * 4] * B, hq, layout.head_dim_v,
+                        group_parts=1)
+        o_h, l_h = host_partial(bs, layout.num_kv_heads, layout.head_dim_k, layout.head_dim_v,
+                                "bf16", layout.latent, [host_np], q, hq, scale, ct, cl,
+                                n_threads=4)
+        o, lse = ds.run(_dev(q), _lib.BF16, scale, torch.from_numpy(o_h).cuda(),
+                        torch.from_numpy(l_h).cuda())
+        torch.cuda.synchronize()
+        o, lse = o.cpu().numpy(), lse.cpu().numpy()
+        qf = oracle.bf16_bits_to_f64(q)
+        for b in range(B):
+            k64 = oracle.bf16_bits_to_f64(hist_k[b])
+            v64 = oracle.bf16_bits_to_f64(hist_v[b])
+            o_ref, lse_ref = oracle.attend(qf[b], k64, v64, scale)
+            err_o = np.max(np.abs(o[b] - o_ref)) / np.max(np.abs(o_ref))
+            assert err_o <= 2e-3, (step, b, err_o)
+            assert np.max(np.abs(lse[b] - lse_ref)) <= 2e-3
+        _say(f"[session] {name} step {step}: GPU view {list(gl)}, CPU view {list(cl)}")
+    assert sum(cl) > 0 and cpu_batches > 0     # the CPU side was exercised
+    store.close()
