@@ -434,6 +434,111 @@ def host_share_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def write_side_bench(args):
+    """The write side on the Qwen3-30B-A3B-shaped layer (16 sequences, 4 KV heads, head dim 128,
+    bf16, 16-token blocks): 32K-token prefills are appended and placed, then 2 * D decode steps
+    each append one token per sequence through the GPU view and flush the staging window
+    (D = 256).  Two routings: every batch to the GPU share (what the share policy picks on
+    MI355X, where a GPU position costs ~1/100 of a host one) and every batch to the CPU share
+    (device-to-host block copies, the most a flush can cost)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.api import (KVStore, Pool, ShareController, append_kv,
+                                            block_bytes)
+
+    _lib.load()
+    torch.cuda.set_device(0)
+    B, bs, hkv, d, D = 16, 16, 4, 128, 256
+    L0 = 32768 - D
+    steps = 2 * D
+    bb = block_bytes(bs, hkv, d, d, "bf16", False)
+    per_seq = (L0 + steps) // bs + 2 * (D // bs) + 2
+    timer = HipTimer()
+    out = {"mode": "write_side",
+           "workload": "Qwen3-30B-A3B-shaped layer: 16 x 32K, 4 KV heads, d 128, bf16, bs 16, D 256",
+           "append_bytes_per_step": B * hkv * 2 * d * 2}
+    for routing in ("gpu", "cpu"):
+        dev_region = torch.empty(B * per_seq * bb // 2, dtype=torch.int16, device="cuda")
+        host_blocks = B * (steps // bs + 2) + 8
+        host_region = torch.empty(host_blocks * bb // 2, dtype=torch.int16, pin_memory=True)
+        lay = (bs, hkv, d, d, "bf16", False)
+        dev_pool = Pool(*lay, [(dev_region.data_ptr(), B * per_seq)], seed=1)
+        host_pool = Pool(*lay, [(host_region.data_ptr(), host_blocks)], seed=2)
+        # the prefill stays on the GPU share in both cases; decode batches go where the
+        # routing under test sends them.  B = 0 gives r = 0 at every length (all GPU).
+        # A = 0 with C_CPU = L0 + 8 gives r(L0) = 0 but r(L) L = L - L0 - 8 afterwards, so
+        # every D-token batch after the prefill goes to the CPU.
+        if routing == "cpu":
+            ctls = [ShareController(0.0, 1.0, float(L0 + 8), 0.0) for _ in range(B)]
+        else:
+            ctls = [ShareController(1.0, 0.0, 0.0, 0.0) for _ in range(B)]
+        store = KVStore(dev_pool, host_pool, B, D, per_seq, ctls)
+        store.reserve([L0] * B)
+        gt, gl, _, _ = store.views()
+        table_dev = torch.from_numpy(gt).cuda()
+        log(f"[write] {routing}: appending {B} x {L0} prefill tokens")
+        for b in range(B):
+            k = torch.randn(1, L0, hkv, d, device="cuda", dtype=torch.bfloat16).view(torch.int16)
+            v = torch.randn(1, L0, hkv, d, device="cuda", dtype=torch.bfloat16).view(torch.int16)
+            pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+            append_kv(dev_pool, k, v, _lib.BF16, table_dev[b:b + 1], per_seq, pos)
+        store.commit([L0] * B)
+        store.place_prefill()
+        torch.cuda.synchronize()
+        gt, gl, _, _ = store.views()
+        table_dev.copy_(torch.from_numpy(gt))
+        pos_dev = torch.from_numpy(gl.copy()).cuda()
+        k1 = torch.randn(B, 1, hkv, d, device="cuda", dtype=torch.bfloat16).view(torch.int16)
+        v1 = torch.randn(B, 1, hkv, d, device="cuda", dtype=torch.bfloat16).view(torch.int16)
+        ones = np.ones(B, np.int32)
+        evs = [(timer.event(), timer.event()) for _ in range(steps)]
+        sp = torch.cuda.current_stream().cuda_stream
+        host_s, flush_s, n_flush = 0.0, [], 0
+        torch.cuda.synchronize()
+        t_all = time.perf_counter()
+        for i in range(steps):
+            t0 = time.perf_counter()
+            if store.reserve(ones):
+                gt, gl, _, _ = store.views()
+                table_dev.copy_(torch.from_numpy(gt))
+            timer.record(evs[i][0], sp)
+            append_kv(dev_pool, k1, v1, _lib.BF16, table_dev, per_seq, pos_dev)
+            timer.record(evs[i][1], sp)
+            store.commit(ones)
+            tf = time.perf_counter()
+            changed = store.flush()
+            if changed:
+                torch.cuda.synchronize()   # the copies of this flush, timed with it
+                flush_s.append(time.perf_counter() - tf)
+                n_flush += 1
+            gt, gl, _, _ = store.views()
+            if changed:
+                table_dev.copy_(torch.from_numpy(gt))
+            pos_dev.copy_(torch.from_numpy(gl))
+            host_s += time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_all
+        app_us = [timer.elapsed_ms(a, b_) * 1e3 for a, b_ in evs]
+        gt, gl, ct, cl = store.views()
+        res = {"steps": steps, "append_us": round(float(np.mean(app_us)), 2),
+               "wall_us_per_step": round(wall / steps * 1e6, 2),
+               "host_us_per_step": round(host_s / steps * 1e6, 2),
+               "gpu_view_tokens": int(gl.sum()), "cpu_view_tokens": int(cl.sum())}
+        if flush_s:
+            copied = B * D * hkv * 2 * d * 2
+            fl = float(np.median(flush_s))
+            res.update({"flushes_to_cpu": n_flush, "flush_us": round(fl * 1e6, 1),
+                        "flush_bytes": copied, "flush_GBps": round(copied / fl / 1e9, 2),
+                        "flush_us_amortized_per_step": round(fl * 1e6 / D, 2)})
+        out[routing + "_routing"] = res
+        log(f"[write] {routing}: {res}")
+        store.close()
+        del dev_region, host_region
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -447,6 +552,9 @@ def main():
     ap.add_argument("--host-share", choices=["off", "policy"], default="off",
                     help="policy: time the split workload with a native CPU share sized by the "
                          "share policy (prints its own JSON line instead of the bench line)")
+    ap.add_argument("--write-side", action="store_true",
+                    help="time appends and staging-window flushes on the 16 x 32K layer "
+                         "(prints its own JSON line instead of the bench line)")
     ap.add_argument("--host-threads", type=int, default=0,
                     help="host threads for --host-share (default: min(16, usable CPUs) - 1)")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
@@ -466,6 +574,9 @@ def main():
 
     if args.host_share == "policy":
         host_share_bench(args)
+        return
+    if args.write_side:
+        write_side_bench(args)
         return
 
     import numpy as np

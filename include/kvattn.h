@@ -445,11 +445,12 @@ kvattn_status kvattn_share_get_state(const kvattn_share_ctl* ctl, kvattn_share_s
  *    its copy must be enqueued (plan callers: performed) before any later write to it, which
  *    holds when appends go to the same stream.  The host must not read a CPU block before its
  *    copy has completed (synchronise the stream).
- *  - Before the host pool could run short, flush and place_prefill check that it has free
- *    blocks for the worst case (every pending batch to the CPU) and otherwise fail with
- *    E_POOL_EXHAUSTED, changing nothing; likewise E_INVAL if in that case a CPU view would
- *    exceed max_blocks, or if `copies` (host int32 [max_copies][2]) has fewer than that many
- *    pairs.
+ *  - Before anything changes, place_prefill checks that the host pool has free blocks for
+ *    what the controllers will admit (known in advance), and flush that it has them for the
+ *    worst case (every pending batch to the CPU); otherwise E_POOL_EXHAUSTED, changing
+ *    nothing.  Likewise E_INVAL if a CPU view would then exceed max_blocks, or if `copies`
+ *    (host int32 [max_copies][2]) has fewer pairs than that count; E_STATE if a controller
+ *    has already been admitted.
  *  - views: host arrays gpu_table / cpu_table [batch][max_blocks] (ABSENT after the list),
  *    gpu_len / cpu_len [batch].
  *  - free: returns every block the store holds to its pool; a pool whose kvattn_pool_free

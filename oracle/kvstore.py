@@ -19,10 +19,13 @@ Readings (the pages leave these open):
     to the CPU, the other whole blocks to the GPU share; a partial block stays in the window.
   * Blocks are claimed sequence by sequence from the allocator model (``oracle.alloc``), so
     every physical id is predictable; steps that could exhaust a pool or overflow a view fail
-    before changing anything.
+    before changing anything (prefill: for what the controllers will admit; flush: for every
+    pending batch going to the CPU).
 
 Steps follow the definitions in the order given, one sequence at a time.
 """
+
+import copy
 
 import numpy as np
 
@@ -93,7 +96,17 @@ class StoreModel:
     def place_prefill(self):
         if self.prefill_done or self.flushed:
             raise PoolError("state")
-        self._check_worst([w // self.bs for w in self.w])
+        # what each controller will admit is known beforehand (a copy of it admits)
+        need = []
+        for b in range(self.batch):
+            full = self.w[b] // self.bs
+            if self.ctl[b] is None:
+                need.append(0)
+                continue
+            if self.ctl[b].admitted:
+                raise PoolError("state")
+            need.append(copy.deepcopy(self.ctl[b]).admit(full * self.bs, self.bs) // self.bs)
+        self._check_worst(need)
         copies, changed = [], False
         for b in range(self.batch):
             full = self.w[b] // self.bs

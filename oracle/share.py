@@ -81,8 +81,10 @@ class Controller:
         self.cpu_batches = 0
         self.batches = 0
         self.decisions = []
+        self.admitted = False
 
     def admit(self, L0, block_tokens):
+        self.admitted = True
         c = 0
         if L0 > 0:
             r = optimum(self.A, self.B, self.C_cpu, self.C_gpu, float(L0))

@@ -228,8 +228,21 @@ kvattn_status kvattn_kvstore_place_prefill_plan(kvattn_kvstore* s, int32_t* copi
     return set_error(KVATTN_E_INVAL, "kvstore_place_prefill: null argument");
   if (s->prefill_done || s->flushed)
     return set_error(KVATTN_E_STATE, "kvstore_place_prefill: only once, before any flush");
+  // the admissions are known before anything changes, so the check is exact
+  std::vector<int64_t> ncpu_of((size_t)s->batch, 0);
+  for (int32_t b = 0; b < s->batch; ++b) {
+    const kvattn_share_ctl* c = s->ctl[(size_t)b];
+    if (!c) continue;
+    const int64_t full_tokens = (s->seq[(size_t)b].w / s->bs) * s->bs;
+    const int64_t t = kvattn::share_admit_tokens(c, full_tokens, s->bs);
+    if (t < 0)
+      return set_error(KVATTN_E_STATE, "kvstore_place_prefill: controller of sequence " +
+                                           std::to_string(b) + " already admitted");
+    ncpu_of[(size_t)b] = t / s->bs;
+  }
+  size_t idx = 0;
   kvattn_status st = kvattn::check_worst(
-      s, [&](const kvattn_kvstore::Seq& q) { return q.w / s->bs; }, copies, max_copies,
+      s, [&](const kvattn_kvstore::Seq&) { return ncpu_of[idx++]; }, copies, max_copies,
       "kvstore_place_prefill");
   if (st != KVATTN_OK) return st;
   *n_copies = 0;

@@ -27,6 +27,9 @@ namespace kvattn {
 // free was requested deletes it.
 void pool_borrow(kvattn_pool* p);
 void pool_unborrow(kvattn_pool* p);
+// CPU tokens kvattn_share_admit would give, without admitting (-1 if already admitted).
+int64_t share_admit_tokens(const kvattn_share_ctl* ctl, int64_t prefill_tokens,
+                           int64_t block_tokens);
 }  // namespace kvattn
 
 namespace kvattn {

@@ -44,6 +44,20 @@ double optimum(const kvattn_share_model& m, double L) {
 }
 
 }  // namespace
+
+// CPU tokens the admission of `prefill_tokens` gives (whole blocks, nearest, at most the
+// whole blocks of the prefill), without admitting: -1 if the controller is already admitted.
+int64_t share_admit_tokens(const kvattn_share_ctl* ctl, int64_t prefill_tokens,
+                           int64_t block_tokens) {
+  if (ctl->admitted) return -1;
+  if (prefill_tokens <= 0) return 0;
+  const double r = optimum(ctl->model, (double)prefill_tokens);
+  const int64_t whole = prefill_tokens / block_tokens;
+  int64_t blocks = (int64_t)std::llround(r * (double)prefill_tokens / (double)block_tokens);
+  if (blocks > whole) blocks = whole;
+  return blocks * block_tokens;
+}
+
 }  // namespace kvattn
 
 using kvattn::set_error;
@@ -112,14 +126,7 @@ kvattn_status kvattn_share_admit(kvattn_share_ctl* ctl, int64_t prefill_tokens,
   if (ctl->admitted) return set_error(KVATTN_E_STATE, "share_admit: already admitted");
   if (prefill_tokens < 0 || block_tokens < 1)
     return set_error(KVATTN_E_INVAL, "share_admit: prefill_tokens < 0 or block_tokens < 1");
-  int64_t c = 0;
-  if (prefill_tokens > 0) {
-    const double r = kvattn::optimum(ctl->model, (double)prefill_tokens);
-    const int64_t whole = prefill_tokens / block_tokens;
-    int64_t blocks = (int64_t)std::llround(r * (double)prefill_tokens / (double)block_tokens);
-    if (blocks > whole) blocks = whole;
-    c = blocks * block_tokens;
-  }
+  const int64_t c = kvattn::share_admit_tokens(ctl, prefill_tokens, block_tokens);
   ctl->admitted = true;
   ctl->placed = prefill_tokens;
   ctl->cpu = c;

@@ -144,14 +144,28 @@ def test_store_errors_leave_state_unchanged():
     assert dev.num_free == 10 and host.num_free == 4
 
 
-def test_store_host_pool_exhaustion_is_checked_for_the_worst_case():
+def test_host_pool_checks_exact_for_prefill_and_worst_case_for_flush():
+    # no controller: the prefill needs no host block, even with a tiny host pool
     dev, host, _, _ = _pools(40, 3, 9)
     store = KVStore(dev, host, 1, 32, 40)
     store.reserve([100])
     store.commit([100])
-    # without a controller nothing goes to the CPU, but the check is for the worst case
-    _expect(_lib.E_POOL_EXHAUSTED, store.place_prefill_plan)
+    store.place_prefill_plan()
     assert store.views()[1][0] == 100
+    # a flush of two pending batches could need 2 x 2 host blocks > 3
+    store.reserve([64])
+    store.commit([64])
+    _expect(_lib.E_POOL_EXHAUSTED, store.flush_plan)
+    assert store.views()[1][0] == 164
+    # a controller that admits more than the host pool holds: refused before any change
+    dev2, host2, _, _ = _pools(40, 3, 10)
+    ctl = ShareController(0.0, 1.0)               # r = 1: the whole prefill to the CPU
+    store2 = KVStore(dev2, host2, 1, 32, 40, [ctl])
+    store2.reserve([100])
+    store2.commit([100])
+    _expect(_lib.E_POOL_EXHAUSTED, store2.place_prefill_plan)
+    assert store2.views()[1][0] == 100 and host2.num_free == 3
+    assert ctl.state()["placed_tokens"] == 0      # not admitted by the refused call
 
 
 def test_store_create_validation():
