@@ -440,8 +440,10 @@ kvattn_status kvattn_share_get_state(const kvattn_share_ctl* ctl, kvattn_share_s
  *    GPU batch moves to the GPU share in place (no copy); a CPU batch is copied block by
  *    block into newly claimed host blocks and its device blocks are released.
  *  - The _plan forms do the bookkeeping only and return the copies as pairs (device id,
- *    host id) in copy order; the others then enqueue one hipMemcpyAsync (device to host) per
- *    pair on hip_stream.  A released device block may be claimed again by the next reserve:
+ *    host id) in copy order; the others then enqueue the copies on hip_stream: one kernel that
+ *    writes the blocks into the host regions over the host link when every host region is
+ *    pinned memory mapped for the device (hipHostGetDevicePointer succeeds), else one
+ *    hipMemcpyAsync (device to host) per pair.  A released device block may be claimed again by the next reserve:
  *    its copy must be enqueued (plan callers: performed) before any later write to it, which
  *    holds when appends go to the same stream.  The host must not read a CPU block before its
  *    copy has completed (synchronise the stream).

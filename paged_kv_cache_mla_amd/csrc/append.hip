@@ -11,6 +11,7 @@
 // dimensions); the kernel is bound by launch and store latency.
 
 #include "device_common.h"
+#include "launch_common.h"
 
 namespace kvattn {
 
@@ -86,6 +87,48 @@ hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const vo
   a.latent = L.latent;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)((int64_t)batch * n_new)), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// Eviction of staging blocks to host blocks: workgroup i copies device block src[i] of the
+// device pool to block dst[i] of the host pool, whose region table holds the device-mapped
+// addresses of pinned host regions; 16 bytes per lane, written over the host link.  The
+// list travels by value in the kernel arguments.
+constexpr int kMaxCopies = 240;
+
+struct CopyList {
+  int32_t n;
+  int32_t src[kMaxCopies];
+  int32_t dst[kMaxCopies];
+};
+
+__global__ void __launch_bounds__(256) copy_blocks_kernel(RegionTable src_rt, RegionTable dst_rt,
+                                                          CopyList list) {
+  const int i = blockIdx.x;
+  if (i >= list.n) return;
+  const uint4* s = reinterpret_cast<const uint4*>(block_ptr(src_rt, list.src[i]));
+  uint4* d = reinterpret_cast<uint4*>(const_cast<char*>(block_ptr(dst_rt, list.dst[i])));
+  for (int64_t j = threadIdx.x; j < src_rt.block_bytes / 16; j += blockDim.x) d[j] = s[j];
+}
+
+// pairs: [n][2] = (device id, host id); host_bases: device addresses of the host pool's regions
+hipError_t launch_copy_blocks(const kvattn_pool* dev, const kvattn_pool* host,
+                              void* const* host_bases, const int32_t* pairs, int n,
+                              hipStream_t st) {
+  const RegionTable src_rt = region_table(dev);
+  const RegionTable dst_rt = region_table(host, host_bases);
+  for (int first = 0; first < n; first += kMaxCopies) {
+    CopyList list{};
+    list.n = n - first < kMaxCopies ? n - first : kMaxCopies;
+    for (int i = 0; i < list.n; ++i) {
+      list.src[i] = pairs[2 * (first + i)];
+      list.dst[i] = pairs[2 * (first + i) + 1];
+    }
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)list.n), dim3(256), 0, st, src_rt, dst_rt,
+                       list);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kvattn

@@ -5,6 +5,7 @@
 #include <string>
 
 #include "device_common.h"
+#include "launch_common.h"
 #include "pool_internal.h"
 
 namespace kvattn {
@@ -22,22 +23,6 @@ hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const vo
                          int bs_shift, hipStream_t st);
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-static RegionTable region_table(const kvattn_pool* pool) {
-  RegionTable rt{};
-  for (int r = 0; r < KVATTN_MAX_REGIONS; ++r) {
-    rt.base[r] = static_cast<const char*>(r < pool->n_regions ? pool->base[r] : pool->base[0]);
-    rt.first[r] = pool->first_id[r];
-    rt.first32[r] = static_cast<int32_t>(pool->first_id[r]);
-    rt.adj[r] = reinterpret_cast<uint64_t>(rt.base[r]) -
-                static_cast<uint64_t>(pool->first_id[r]) * static_cast<uint64_t>(pool->block_bytes);
-  }
-  rt.first[KVATTN_MAX_REGIONS] = pool->first_id[KVATTN_MAX_REGIONS];
-  rt.block_bytes = pool->block_bytes;
-  rt.n = pool->n_regions;
-  rt.total = (int32_t)pool->total_blocks;
-  return rt;
-}
 
 static int log2_exact(int v) {
   int s = 0;

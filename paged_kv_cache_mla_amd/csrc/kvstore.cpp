@@ -11,7 +11,8 @@
 // to the GPU moves no data (its blocks change list); a batch routed to the CPU is copied block
 // by block into host blocks and its device blocks return to the pool.  Each engine then reads
 // its own blocks through a sub-table (its view).  Host bookkeeping; the only device work is
-// the copies, enqueued with hipMemcpyAsync on the caller's stream.
+// the copies, enqueued on the caller's stream: one kernel writing straight into the host
+// blocks when the host regions are mapped pinned memory, else one hipMemcpyAsync per block.
 
 #include <hip/hip_runtime_api.h>
 
@@ -33,9 +34,17 @@ struct kvattn_kvstore {
   std::vector<kvattn_share_ctl*> ctl;
   std::vector<Seq> seq;
   bool prefill_done = false, flushed = false;
+  // device addresses of the host pool's regions when they are mapped pinned memory (queried at
+  // the first enqueued copy): copies then run as one kernel writing over the host link
+  int mapped = -1;  // -1 unknown, 0 no, 1 yes
+  void* host_dev_base[KVATTN_MAX_REGIONS] = {};
 };
 
 namespace kvattn {
+
+hipError_t launch_copy_blocks(const kvattn_pool* dev, const kvattn_pool* host,
+                              void* const* host_bases, const int32_t* pairs, int n, hipStream_t st);
+
 namespace {
 
 // n fresh blocks of pool p appended to out (allocate mode of kvattn_block_table, one sequence)
@@ -113,9 +122,28 @@ kvattn_status place(kvattn_kvstore* s, kvattn_kvstore::Seq& q, int32_t n, bool t
   return KVATTN_OK;
 }
 
-kvattn_status enqueue_copies(const kvattn_kvstore* s, const std::vector<int32_t>& copies,
-                             int32_t n, void* hip_stream) {
+kvattn_status enqueue_copies(kvattn_kvstore* s, const std::vector<int32_t>& copies, int32_t n,
+                             void* hip_stream) {
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (n == 0) return KVATTN_OK;
+  if (s->mapped < 0) {
+    s->mapped = 1;
+    for (int r = 0; r < s->host->n_regions; ++r) {
+      void* d = nullptr;
+      if (hipHostGetDevicePointer(&d, s->host->base[r], 0) != hipSuccess || !d) {
+        (void)hipGetLastError();  // clear the sticky error of the failed query
+        s->mapped = 0;
+        break;
+      }
+      s->host_dev_base[r] = d;
+    }
+  }
+  if (s->mapped == 1) {
+    const hipError_t e = launch_copy_blocks(s->dev, s->host, s->host_dev_base, copies.data(), n, st);
+    if (e != hipSuccess)
+      return set_error(KVATTN_E_HIP, std::string("kvstore copy kernel: ") + hipGetErrorString(e));
+    return KVATTN_OK;
+  }
   for (int32_t i = 0; i < n; ++i) {
     const hipError_t e = hipMemcpyAsync(block_address(s->host, copies[2 * i + 1]),
                                         block_address(s->dev, copies[2 * i]),
