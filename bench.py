@@ -553,6 +553,89 @@ def write_side_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def sparse_bench(args):
+    """Block-level sparse decode on the Qwen3-30B-A3B-shaped layer (16 x 32K, 4 KV heads, d 128,
+    bf16): every sequence selects a seeded random `density` share of its 16-token blocks;
+    kvattn_select_blocks builds the sub-tables on the device, then decode_partial and the merge
+    run on them.  Reported against the selected KV bytes and next to the dense step."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.api import decode_partial, merge_lse, select_blocks
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    from synth import make_case
+
+    _lib.load()
+    torch.cuda.set_device(0)
+    density = args.sparse
+    case = make_case("gqa_32k", "full")
+    G = GROUP_PARTS["gqa_32k"]
+    dc = DeviceCase(case, group_parts=G)
+    B, bs = case.batch, case.block_size
+    nb = -(-int(case.ctx_lens.max()) // bs)
+    k = max(1, int(round(nb * density)))
+    rng = np.random.default_rng(3)
+    sel = np.stack([rng.choice(nb, k, replace=False) for _ in range(B)]).astype(np.int32)
+    dev = "cuda"
+    sel_dev = torch.from_numpy(sel).to(dev)
+    sub_table = torch.empty((B, k), dtype=torch.int32, device=dev)
+    seq_sub = torch.zeros((3, B), dtype=torch.int32, device=dev)
+    seq_sub[2] = int(case.part_tokens[0])
+    bound = np.full(B, k * bs, np.int32)
+    parts = -(-(k * bs) // int(case.part_tokens[0]))
+    g = min(G, max(1, parts // 2))          # keep at least two partials per (sequence, head)
+    max_parts = -(-parts // g)
+    o_part = torch.empty((B, case.num_q_heads, max_parts, case.head_dim_v), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((B, case.num_q_heads, max_parts), dtype=torch.float32, device=dev)
+    nparts = torch.empty(B, dtype=torch.int32, device=dev)
+    o = torch.empty((B, case.num_q_heads, case.head_dim_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, case.num_q_heads), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(evs=None):
+        sp = torch.cuda.current_stream().cuda_stream
+        if evs:
+            timer.record(evs[0], sp)
+        select_blocks(dc.step.table_dev, case.max_blocks, dc.step.seq_dev[0], bs, sel_dev,
+                      sub_table, seq_sub[0], err)
+        if evs:
+            timer.record(evs[1], sp)
+        decode_partial(dc.pool, dc.q, dc.q_dtype, case.num_q_heads, case.scale, sub_table, k,
+                       bound, None, case.part_tokens, seq_sub, max_parts, o_part, lse_part,
+                       nparts, err, None, g)
+        if evs:
+            timer.record(evs[2], sp)
+        merge_lse(o_part, lse_part, nparts, B, case.num_q_heads, max_parts, case.head_dim_v, o,
+                  None, None, lse)
+
+    timer = HipTimer()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"error flag {int(err.item())}")
+    evs = [(timer.event(), timer.event(), timer.event()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_sel = float(np.mean([timer.elapsed_ms(a, b_) for a, b_, _ in evs])) * 1e3
+    t_dec = float(np.mean([timer.elapsed_ms(b_, c) for _, b_, c in evs])) * 1e3
+    kv = B * k * bs * case.kv_bytes_per_token()
+    dense = _time_steps(torch, lambda: dc.step.run(dc.q, dc.q_dtype, case.scale), args.steps,
+                        args.warmup)
+    out = {"mode": "sparse", "workload": "Qwen3-30B-A3B-shaped layer: 16 x 32K, 4 KV heads, d 128, bf16, bs 16",
+           "density": density, "selected_blocks_per_seq": k, "selected_kv_bytes": kv,
+           "group_parts": g, "ms_per_step": round(ms, 5), "select_us": round(t_sel, 2),
+           "decode_partial_us": round(t_dec, 2),
+           "selected_kv_GBps": round(kv / (t_dec * 1e-6) / 1e9, 1),
+           "dense_ms_per_step": round(dense, 5),
+           "speedup_vs_dense": round(dense / ms, 2)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -569,6 +652,9 @@ def main():
     ap.add_argument("--write-side", action="store_true",
                     help="time appends and staging-window flushes on the 16 x 32K layer "
                          "(prints its own JSON line instead of the bench line)")
+    ap.add_argument("--sparse", type=float, default=0.0, metavar="DENSITY",
+                    help="time block-level sparse decode of the 16 x 32K layer at this block "
+                         "density (prints its own JSON line instead of the bench line)")
     ap.add_argument("--host-threads", type=int, default=0,
                     help="host threads for --host-share (default: min(16, usable CPUs) - 1)")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
@@ -591,6 +677,9 @@ def main():
         return
     if args.write_side:
         write_side_bench(args)
+        return
+    if args.sparse > 0:
+        sparse_bench(args)
         return
 
     import numpy as np

@@ -78,6 +78,7 @@ enum { KVATTN_F32 = 0, KVATTN_BF16 = 1 };
 /* Error bits a decode kernel may set in *err_dev (see kvattn_decode_partial). */
 #define KVATTN_ERR_BAD_BLOCK 1   /* a table entry inside a sequence's range is not a valid id */
 #define KVATTN_ERR_BAD_SEQ 2     /* device per-sequence values disagree with the host ones */
+#define KVATTN_ERR_BAD_SELECT 4  /* a selected block index outside the context, or repeated */
 
 typedef struct {
   int32_t block_size;   /* tokens per block bs; power of two in [1, 256] */
@@ -286,6 +287,36 @@ kvattn_status kvattn_append_kv(const kvattn_pool* pool, const void* k_new, const
                                int32_t kv_dtype, int32_t batch, int32_t n_new,
                                const int32_t* table_dev, int32_t max_blocks,
                                const int32_t* pos_dev, int32_t* err_dev, void* hip_stream);
+
+/*
+ * Block-level sparse selection ([InplaceKVCache] §4.2, sparse-selection compatibility: a
+ * block-level top-k selection yields a set of whole blocks, so sparsity needs no change to the
+ * block format).  For every sequence b, builds on the device the sub-table of the blocks whose
+ * logical indices sel_dev[b][0..k) name, so that the decode kernels attend exactly the tokens
+ * of those blocks:
+ *   sub_table_dev[b] = table[b][j] for the selected full blocks j in ascending order, then the
+ *                      partial last block (if ctx_len % bs != 0 and it is selected), then
+ *                      KVATTN_BLOCK_ABSENT up to max_sub;
+ *   sub_len_dev[b]   = bs * (selected full blocks) + (ctx_len - bs * (nb - 1) if the partial
+ *                      block is selected), nb = ceil(ctx_len / bs).
+ * Attention does not depend on the order of the cached tokens, so the order is a choice: the
+ * ascending one makes the result independent of the order of the selection.
+ *   table_dev [batch][max_blocks], ctx_lens_dev [batch], sel_dev [batch][k]: device int32;
+ *   negative entries of sel_dev are padding.  sub_table_dev [batch][max_sub], sub_len_dev
+ *   [batch]: device int32 (sub_len_dev may be row 0 of a decode's seq_dev).
+ *   err_dev (nullable): KVATTN_ERR_BAD_SELECT for an index >= nb or repeated (ignored),
+ *   KVATTN_ERR_BAD_SEQ for ctx_len < 0 or nb > max_blocks (the sequence gets length 0).
+ * To decode the selection, pass host upper bounds (k * bs per sequence) as ctx_lens of
+ * kvattn_decode_partial with table_dev = sub_table_dev and max_blocks = max_sub: the grid is
+ * sized by the bounds and the kernels use the device lengths.
+ * Errors: E_INVAL (null pointers, batch < 1, k < 1, max_sub < k, max_blocks outside
+ * [1, 65536], block_size not a power of two in [1, 256]), E_HIP.
+ */
+kvattn_status kvattn_select_blocks(const int32_t* table_dev, int32_t max_blocks,
+                                   const int32_t* ctx_lens_dev, int32_t block_size,
+                                   const int32_t* sel_dev, int32_t batch, int32_t k,
+                                   int32_t* sub_table_dev, int32_t max_sub, int32_t* sub_len_dev,
+                                   int32_t* err_dev, void* hip_stream);
 
 /*
  * CPU share of a decode step, computed on the host ([InplaceKVCache] §5.1: the engines take

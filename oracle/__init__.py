@@ -34,6 +34,7 @@ from .write import write_tokens
 from .decode import decode_reference, decode_partials_reference, resolve_offsets_reference
 from . import alloc
 from . import share
+from . import sparse
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -52,4 +53,5 @@ __all__ = [
     "resolve_offsets_reference",
     "alloc",
     "share",
+    "sparse",
 ]

@@ -23,6 +23,7 @@ MAX_REGIONS = 8
 MAX_GROUP_PARTS = 16
 ERR_BAD_BLOCK = 1
 ERR_BAD_SEQ = 2
+ERR_BAD_SELECT = 4
 
 STATUS_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_POOL_EXHAUSTED: "E_POOL_EXHAUSTED",
                 E_RANGE: "E_RANGE", E_STATE: "E_STATE", E_UNSUPPORTED: "E_UNSUPPORTED",
@@ -72,6 +73,7 @@ _SIGNATURES = {
                                      _PI32, _PI32, _PI32, _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_merge_lse": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_resolve_offsets": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
+    "kvattn_select_blocks": (_I32, [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
     "kvattn_append_kv": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P]),
     "kvattn_host_partial": (_I32, [ctypes.POINTER(Layout), ctypes.POINTER(Region), _I32, _P, _I32,
                                    _I32, _I32, ctypes.c_float, _PI32, _I32, _PI32, _P, _P, _I32]),

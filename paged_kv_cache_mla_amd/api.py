@@ -12,7 +12,7 @@ import numpy as np
 from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
-__all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets", "append_kv",
+__all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
            "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
            "ShareController", "KVStore", "KvattnError", "BF16", "F32"]
 
@@ -149,6 +149,20 @@ def merge_lse(o_part, lse_part, nparts, batch, num_q_heads, max_parts, dv, o_out
                               int(num_q_heads), int(max_parts), int(dv), _dptr(o_ext),
                               _dptr(lse_ext), _dptr(o_out), _dptr(lse_out), _stream(stream))
     check(st, "merge_lse")
+
+
+def select_blocks(table_dev, max_blocks, ctx_lens_dev, block_size, sel_dev, sub_table_dev,
+                  sub_len_dev, err=None, stream=None):
+    """Sub-table of the selected logical blocks of each sequence (kvattn_select_blocks):
+    sel_dev [B][k] device int32 (negative = padding), sub_table_dev [B][max_sub], sub_len_dev
+    [B] (may be row 0 of a decode step's seq_dev)."""
+    lib = _lib.load()
+    batch, k = int(sel_dev.shape[0]), int(sel_dev.shape[1])
+    st = lib.kvattn_select_blocks(_dptr(table_dev), int(max_blocks), _dptr(ctx_lens_dev),
+                                  int(block_size), _dptr(sel_dev), batch, k, _dptr(sub_table_dev),
+                                  int(sub_table_dev.shape[1]), _dptr(sub_len_dev), _dptr(err),
+                                  _stream(stream))
+    check(st, "select_blocks")
 
 
 def append_kv(pool, k_new, v_new, kv_dtype, table_dev, max_blocks, pos_dev, err=None,

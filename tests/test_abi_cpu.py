@@ -281,3 +281,23 @@ def test_append_validation_without_gpu(lib):
     assert call(gqa, b=0) == _lib.E_INVAL
     assert call(gqa, b=65536, n=65536) == _lib.E_INVAL        # 2^32 tokens in one launch
     assert call(gqa, t=None) == _lib.E_INVAL
+
+
+def test_select_blocks_validation_without_gpu(lib):
+    vp = ctypes.c_void_p
+
+    def call(**over):
+        a = dict(t=vp(FAKE), mb=64, c=vp(FAKE), bs=16, s=vp(FAKE), b=2, k=8, st=vp(FAKE), ms=8,
+                 sl=vp(FAKE))
+        a.update(over)
+        return lib.kvattn_select_blocks(a["t"], a["mb"], a["c"], a["bs"], a["s"], a["b"], a["k"],
+                                        a["st"], a["ms"], a["sl"], None, None)
+    assert call(t=None) == _lib.E_INVAL
+    assert call(sl=None) == _lib.E_INVAL
+    assert call(k=0) == _lib.E_INVAL
+    assert call(ms=7) == _lib.E_INVAL                         # sub-table narrower than k
+    assert call(mb=65537) == _lib.E_INVAL                     # bitmap beyond its LDS budget
+    assert call(mb=0) == _lib.E_INVAL
+    assert call(bs=24) == _lib.E_INVAL
+    assert call(bs=512) == _lib.E_INVAL
+    assert call(b=0) == _lib.E_INVAL
