@@ -639,6 +639,64 @@ def sparse_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def growth_bench(args):
+    """Run-time pool growth over HIP virtual memory: time to back a range with new pages, to
+    move pages from an "expert weights" range into the KV range (with and without the device
+    synchronisation that guards pages still in use), and to grow the pool over them; at the
+    step size of the pages' own controller (4 expert groups of 6 MiB) and at 1 GiB, in 2 MiB
+    chunks, on the layout of the 16 x 32K layer."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.api import Pool, VMMRange, block_bytes
+
+    _lib.load()
+    torch.cuda.set_device(0)
+    torch.zeros(1, device="cuda")
+    chunk = 2 << 20
+    bb = block_bytes(16, 4, 128, 128, "bf16", False)
+    out = {"mode": "growth", "chunk_bytes": chunk, "block_bytes": bb, "steps": []}
+    for size in (24 << 20, 1 << 30):
+        res = {"bytes": size}
+        for trial in range(4):   # the first trial takes one-time costs; the last three are kept
+            expert = VMMRange(2 * size, chunk)
+            kv = VMMRange(2 * size, chunk)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            expert.map_new(0, size)
+            t_map = time.perf_counter() - t
+            t = time.perf_counter()
+            expert.move_to(0, kv, 0, size, sync_device=True)
+            t_move = time.perf_counter() - t
+            t = time.perf_counter()
+            kv.move_to(0, expert, size, size, sync_device=False)   # idle device: no guard needed
+            t_move_ns = time.perf_counter() - t
+            base = torch.empty(bb // 2, dtype=torch.int16, device="cuda")
+            pool = Pool(16, 4, 128, 128, "bf16", False, [(base.data_ptr(), 1)])
+            expert.move_to(size, kv, 0, size, sync_device=False)
+            t = time.perf_counter()
+            pool.add_region(kv.base, size // bb)
+            st, _, _ = pool.block_table([16 * (size // bb)], size // bb)
+            t_pool = time.perf_counter() - t
+            assert st == _lib.OK
+            pool.close()
+            kv.close()
+            expert.close()
+            if trial:
+                for k_, v_ in (("map_new_us", t_map), ("move_sync_us", t_move),
+                               ("move_nosync_us", t_move_ns), ("pool_grow_and_claim_us", t_pool)):
+                    res.setdefault(k_, []).append(v_ * 1e6)
+        for k_ in list(res):
+            if isinstance(res[k_], list):
+                res[k_] = round(float(np.median(res[k_])), 1)
+        res["blocks"] = size // bb
+        res["move_us_per_chunk"] = round(res["move_nosync_us"] / (size // chunk), 2)
+        out["steps"].append(res)
+        log(f"[growth] {res}")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -658,6 +716,9 @@ def main():
     ap.add_argument("--sparse", type=float, default=0.0, metavar="DENSITY",
                     help="time block-level sparse decode of the 16 x 32K layer at this block "
                          "density (prints its own JSON line instead of the bench line)")
+    ap.add_argument("--growth", action="store_true",
+                    help="time run-time pool growth over moved virtual-memory pages (prints its own "
+                         "JSON line instead of the bench line)")
     ap.add_argument("--host-threads", type=int, default=0,
                     help="host threads for --host-share (default: min(16, usable CPUs) - 1)")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
@@ -683,6 +744,9 @@ def main():
         return
     if args.sparse > 0:
         sparse_bench(args)
+        return
+    if args.growth:
+        growth_bench(args)
         return
 
     import numpy as np

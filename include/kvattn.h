@@ -115,6 +115,68 @@ int64_t kvattn_block_bytes(const kvattn_layout* layout);
 kvattn_status kvattn_pool_alloc(const kvattn_layout* layout, const kvattn_region* regions,
                                 int32_t n_regions, uint64_t seed, kvattn_pool** out);
 
+/*
+ * Growth and shrinking of a pool at run time ([VAMP] §IV-C: physical HBM pages move between the
+ * expert weights and the KV pool; §V-A: reclaimed pages join the free-block pool at once, and
+ * the remapping primitive also runs in reverse; it moves a contiguous high-index region).
+ *  - kvattn_pool_add_region: appends a region (device address, 16-byte aligned, caller-owned)
+ *    of num_blocks blocks as region n_regions; its ids are [total, total + num_blocks), written
+ *    to *first_id, and go on top of the free list so that they are handed out first, in
+ *    ascending order.  E_INVAL: null pointers, misalignment, num_blocks < 1, already
+ *    KVATTN_MAX_REGIONS regions, more than 2^31-1 blocks.
+ *  - kvattn_pool_resize_last_region: sets the block count of the last region.  Growing appends
+ *    ids as above: the caller guarantees that the memory after the region's current end is
+ *    valid device memory (e.g. newly mapped pages of a reserved range).  Shrinking removes the
+ *    highest ids, which must all be free (E_STATE otherwise); 0 removes the region (E_INVAL if
+ *    it is the only one).  The removed ids leave the free list; other ids keep their order.
+ * Tables and kernels refer to blocks by id and each launch carries the region table it was
+ * given, so decodes enqueued before a change are unaffected; a shrink must not remove memory
+ * that work still in flight reads (the removed blocks are free, but synchronise before
+ * unmapping their pages).
+ */
+kvattn_status kvattn_pool_add_region(kvattn_pool* pool, void* base, int64_t num_blocks,
+                                     int64_t* first_id);
+kvattn_status kvattn_pool_resize_last_region(kvattn_pool* pool, int64_t num_blocks);
+/* Number of regions (-1 for NULL). */
+int32_t kvattn_pool_num_regions(const kvattn_pool* pool);
+
+/*
+ * Reserved device address ranges with movable physical pages ([VAMP] §IV-C: the physical pages
+ * behind expert weights are unmapped and remapped into the KV pool while the experts' address
+ * ranges stay reserved; §V-A: the remap unit is a multiple of the allocation granularity and the
+ * primitive also runs in reverse).
+ *  - create: reserves va_bytes (rounded up to the chunk size) of address space on `device`;
+ *    nothing is mapped.  Pages are created, mapped and moved in chunks of chunk_bytes (a
+ *    multiple of the device's minimum allocation granularity; 0 = the runtime's recommended
+ *    granularity), reported by kvattn_vmm_granularity.  E_UNSUPPORTED if the device has no
+ *    virtual memory management.
+ *  - map_new: backs [offset, offset + bytes) with new physical memory, granule by granule,
+ *    read-write for the device (E_STATE if part of it is mapped).  Contents are undefined.
+ *  - move: takes the physical granules behind src[src_offset, + bytes) and maps them at
+ *    dst[dst_offset, + bytes): the contents move with them, nothing is copied; the source
+ *    range stays reserved and becomes unmapped.  The source must be fully mapped and the
+ *    destination fully unmapped (E_STATE otherwise); both ranges on one device.  With
+ *    sync_device != 0 the device is synchronised first, so no work in flight can still read
+ *    the source; with 0 the caller guarantees that none does.
+ *  - free: synchronises the device, unmaps and releases every granule, frees the range.
+ * Offsets and sizes are multiples of the chunk size (E_INVAL otherwise).  Mapping new
+ * pages never disturbs work in flight; a pool grows over a moved or mapped range with
+ * kvattn_pool_add_region / kvattn_pool_resize_last_region.  Not thread-safe.
+ * Errors also: E_INVAL for null pointers or a zero size, E_HIP (the range may then be partly
+ * updated; kvattn_vmm_mapped_bytes tells how much is mapped).
+ */
+typedef struct kvattn_vmm kvattn_vmm;
+
+kvattn_status kvattn_vmm_create(int32_t device, uint64_t va_bytes, uint64_t chunk_bytes,
+                                kvattn_vmm** out);
+void kvattn_vmm_free(kvattn_vmm* vmm);
+uint64_t kvattn_vmm_granularity(const kvattn_vmm* vmm);
+void* kvattn_vmm_base(const kvattn_vmm* vmm);
+uint64_t kvattn_vmm_mapped_bytes(const kvattn_vmm* vmm);
+kvattn_status kvattn_vmm_map_new(kvattn_vmm* vmm, uint64_t offset, uint64_t bytes);
+kvattn_status kvattn_vmm_move(kvattn_vmm* src, uint64_t src_offset, kvattn_vmm* dst,
+                              uint64_t dst_offset, uint64_t bytes, int32_t sync_device);
+
 /* Release the pool's host metadata; the regions stay the caller's.  NULL is ignored.  While a
  * kvattn_kvstore still holds the pool, the release is deferred until the last such store is
  * freed (the pool must not be used by the caller after this call either way). */

@@ -158,3 +158,41 @@ class PoolModel:
             self.ref[pid] -= 1
             if self.ref[pid] == 0:
                 self.free.append(pid)
+
+
+def _push_new(model, first, n):
+    """New ids on top of the stack, handed out first and in ascending order."""
+    model.free += list(range(first + n - 1, first - 1, -1))
+    model.ref += [0] * n
+
+
+def add_region(model, n):
+    """Append n blocks as a new region ([VAMP] §V-A: reclaimed pages join the free-block pool
+    and are allocatable at once); returns their first id."""
+    first = model.total
+    model.total += n
+    _push_new(model, first, n)
+    model.region_sizes = getattr(model, "region_sizes", [first]) + [n]
+    return first
+
+
+def resize_last_region(model, n):
+    """Grow or shrink the last region ([VAMP] §V-A: the remap runs in reverse too); shrinking
+    needs the removed (highest) ids free."""
+    sizes = getattr(model, "region_sizes", [model.total])
+    cur = sizes[-1]
+    first = model.total - cur
+    if n < 0 or (n == 0 and len(sizes) == 1):
+        raise PoolError("inval")
+    if n >= cur:
+        _push_new(model, model.total, n - cur)
+        model.total = first + n
+    else:
+        cut = first + n
+        if any(model.ref[i] for i in range(cut, model.total)):
+            raise PoolError("state")
+        model.free = [i for i in model.free if i < cut]
+        model.ref = model.ref[:cut]
+        model.total = cut
+    sizes = sizes[:-1] + ([n] if n else [])
+    model.region_sizes = sizes

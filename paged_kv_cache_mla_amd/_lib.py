@@ -68,6 +68,16 @@ _SIGNATURES = {
     "kvattn_pool_num_free": (_I64, [_P]),
     "kvattn_pool_refcount": (_I32, [_P, _I32]),
     "kvattn_pool_shared_blocks": (_I64, [_P]),
+    "kvattn_pool_add_region": (_I32, [_P, _P, _I64, _PI64]),
+    "kvattn_pool_resize_last_region": (_I32, [_P, _I64]),
+    "kvattn_pool_num_regions": (_I32, [_P]),
+    "kvattn_vmm_create": (_I32, [_I32, ctypes.c_uint64, ctypes.c_uint64, ctypes.POINTER(_P)]),
+    "kvattn_vmm_free": (None, [_P]),
+    "kvattn_vmm_granularity": (ctypes.c_uint64, [_P]),
+    "kvattn_vmm_base": (_P, [_P]),
+    "kvattn_vmm_mapped_bytes": (ctypes.c_uint64, [_P]),
+    "kvattn_vmm_map_new": (_I32, [_P, ctypes.c_uint64, ctypes.c_uint64]),
+    "kvattn_vmm_move": (_I32, [_P, ctypes.c_uint64, _P, ctypes.c_uint64, ctypes.c_uint64, _I32]),
     "kvattn_partition_count": (_I32, [_I32, _I32, _I32]),
     "kvattn_decode_partial": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32,
                                      _PI32, _PI32, _PI32, _P, _I32, _I32, _P, _P, _P, _P, _P]),

@@ -14,7 +14,7 @@ from ._lib import BF16, F32, KvattnError, check
 
 __all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
            "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
-           "ShareController", "KVStore", "KvattnError", "BF16", "F32"]
+           "ShareController", "KVStore", "VMMRange", "KvattnError", "BF16", "F32"]
 
 
 def _i32p(arr):
@@ -104,6 +104,22 @@ class Pool:
     @property
     def shared_blocks(self):
         return int(self._lib.kvattn_pool_shared_blocks(self.handle))
+
+    @property
+    def num_regions(self):
+        return int(self._lib.kvattn_pool_num_regions(self.handle))
+
+    def add_region(self, addr, num_blocks):
+        """Append a region at run time; returns the first id of its blocks."""
+        first = ctypes.c_int64()
+        check(self._lib.kvattn_pool_add_region(self.handle, ctypes.c_void_p(int(addr)),
+                                               int(num_blocks), ctypes.byref(first)),
+              "pool_add_region")
+        return first.value
+
+    def resize_last_region(self, num_blocks):
+        check(self._lib.kvattn_pool_resize_last_region(self.handle, int(num_blocks)),
+              "pool_resize_last_region")
 
     def refcount(self, block_id):
         return int(self._lib.kvattn_pool_refcount(self.handle, int(block_id)))
@@ -320,6 +336,46 @@ class ShareController:
         s = _lib.ShareState()
         check(self._lib.kvattn_share_get_state(self._h, ctypes.byref(s)), "share_get_state")
         return {f: getattr(s, f) for f, _ in _lib.ShareState._fields_}
+
+
+class VMMRange:
+    """A reserved device address range with movable physical pages (kvattn_vmm_*)."""
+
+    def __init__(self, va_bytes, chunk_bytes=0, device=0):
+        self._lib = _lib.load()
+        h = ctypes.c_void_p()
+        check(self._lib.kvattn_vmm_create(int(device), int(va_bytes), int(chunk_bytes),
+                                          ctypes.byref(h)), "vmm_create")
+        self._h = h
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.kvattn_vmm_free(h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def granularity(self):
+        return int(self._lib.kvattn_vmm_granularity(self._h))
+
+    @property
+    def base(self):
+        return int(self._lib.kvattn_vmm_base(self._h))
+
+    @property
+    def mapped_bytes(self):
+        return int(self._lib.kvattn_vmm_mapped_bytes(self._h))
+
+    def map_new(self, offset, nbytes):
+        check(self._lib.kvattn_vmm_map_new(self._h, int(offset), int(nbytes)), "vmm_map_new")
+
+    def move_to(self, offset, dst, dst_offset, nbytes, sync_device=True):
+        """Move the pages behind [offset, offset + nbytes) of this range to `dst`."""
+        check(self._lib.kvattn_vmm_move(self._h, int(offset), dst._h, int(dst_offset), int(nbytes),
+                                        1 if sync_device else 0), "vmm_move")
 
 
 class KVStore:

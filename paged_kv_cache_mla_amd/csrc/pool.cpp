@@ -126,6 +126,75 @@ kvattn_status kvattn_pool_alloc(const kvattn_layout* layout, const kvattn_region
   return KVATTN_OK;
 }
 
+int32_t kvattn_pool_num_regions(const kvattn_pool* pool) { return pool ? pool->n_regions : -1; }
+
+// New ids [first, first + n) go on top of the free stack so that they are handed out first and
+// in ascending order.
+static void push_new_ids(kvattn_pool* p, int64_t first, int64_t n) {
+  for (int64_t i = first + n - 1; i >= first; --i) p->free_stack.push_back((int32_t)i);
+  p->refcount.resize((size_t)(first + n), 0);
+}
+
+kvattn_status kvattn_pool_add_region(kvattn_pool* pool, void* base, int64_t num_blocks,
+                                     int64_t* first_id) {
+  clear_error();
+  if (!pool || !base || !first_id) return set_error(KVATTN_E_INVAL, "pool_add_region: null argument");
+  if ((reinterpret_cast<uintptr_t>(base) & 15u) != 0 || num_blocks < 1)
+    return set_error(KVATTN_E_INVAL, "pool_add_region: base must be 16-byte aligned, num_blocks >= 1");
+  if (pool->n_regions >= KVATTN_MAX_REGIONS)
+    return set_error(KVATTN_E_INVAL, "pool_add_region: the pool already has KVATTN_MAX_REGIONS regions");
+  if (pool->total_blocks + num_blocks > INT32_MAX)
+    return set_error(KVATTN_E_INVAL, "pool_add_region: more than 2^31-1 blocks");
+  const int r = pool->n_regions;
+  const int64_t first = pool->total_blocks;
+  pool->base[r] = base;
+  pool->first_id[r] = first;
+  pool->n_regions = r + 1;
+  pool->total_blocks = first + num_blocks;
+  for (int i = r + 1; i <= KVATTN_MAX_REGIONS; ++i) pool->first_id[i] = pool->total_blocks;
+  push_new_ids(pool, first, num_blocks);
+  *first_id = first;
+  return KVATTN_OK;
+}
+
+kvattn_status kvattn_pool_resize_last_region(kvattn_pool* pool, int64_t num_blocks) {
+  clear_error();
+  if (!pool) return set_error(KVATTN_E_INVAL, "pool_resize_last_region: null pool");
+  const int r = pool->n_regions - 1;
+  const int64_t first = pool->first_id[r];
+  const int64_t cur = pool->total_blocks - first;
+  if (num_blocks < 0 || (num_blocks == 0 && pool->n_regions == 1))
+    return set_error(KVATTN_E_INVAL, "pool_resize_last_region: negative size, or removal of the only region");
+  if (first + num_blocks > INT32_MAX)
+    return set_error(KVATTN_E_INVAL, "pool_resize_last_region: more than 2^31-1 blocks");
+  if (num_blocks > cur) {
+    pool->total_blocks = first + num_blocks;
+    for (int i = r + 1; i <= KVATTN_MAX_REGIONS; ++i) pool->first_id[i] = pool->total_blocks;
+    push_new_ids(pool, first + cur, num_blocks - cur);
+    return KVATTN_OK;
+  }
+  if (num_blocks == cur) return KVATTN_OK;
+  // shrinking: every removed block must be free
+  const int64_t cut = first + num_blocks;
+  for (int64_t i = cut; i < pool->total_blocks; ++i)
+    if (pool->refcount[(size_t)i] != 0)
+      return set_error(KVATTN_E_STATE, "pool_resize_last_region: block " + std::to_string(i) +
+                                           " is in use");
+  std::vector<int32_t> kept;
+  kept.reserve(pool->free_stack.size());
+  for (const int32_t id : pool->free_stack)
+    if (id < cut) kept.push_back(id);
+  pool->free_stack.swap(kept);
+  pool->refcount.resize((size_t)cut);
+  pool->total_blocks = cut;
+  if (num_blocks == 0) {  // the region goes away
+    pool->base[r] = nullptr;
+    pool->n_regions = r;
+  }
+  for (int i = pool->n_regions; i <= KVATTN_MAX_REGIONS; ++i) pool->first_id[i] = pool->total_blocks;
+  return KVATTN_OK;
+}
+
 void kvattn_pool_free(kvattn_pool* pool) {
   if (!pool) return;
   if (pool->borrowers > 0) {  // a store still holds it: deleted when the last one is freed
