@@ -50,15 +50,16 @@ def log(msg):
 
 
 def kernel_hash(workload):
-    """Hash of the sources the workload's dominant kernel is built from (plus the build
-    flags): stored counter readings apply only while this hash is unchanged."""
+    """Hash of the sources the workload's dominant kernel is built from plus the device
+    compile flags: stored counter readings apply only while this hash is unchanged."""
+    from paged_kv_cache_mla_amd.build import ARCH, COMMON, DEVICE
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_mla_amd", "csrc")
     for f in KERNEL_SOURCES.get(workload, DEFAULT_KERNEL_SOURCES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
-    with open(os.path.join(ROOT, "paged_kv_cache_mla_amd", "build.py"), "rb") as fh:
-        h.update(fh.read())
+    flags = [f for f in COMMON + DEVICE if not f.startswith("-I")]  # include paths vary by host
+    h.update(" ".join([ARCH] + flags).encode())
     return h.hexdigest()[:16]
 
 
