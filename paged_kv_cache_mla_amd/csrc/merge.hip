@@ -7,14 +7,18 @@
 //     M = max_p lse_p,  T = sum_p exp(lse_p - M),  lse = M + ln T,
 //     o = sum_p exp(lse_p - M) o_p / T        (= sum_p exp(lse_p - lse) o_p).
 //
-// One 256-thread workgroup per (sequence, head).  Thread (g, c) of a [groups x dv/4]
-// arrangement owns 16-byte column c of partitions g, g + groups, ...  The merge is bound by
-// the latency of a few dependent steps, not by bandwidth, so the order is: issue the loads of
+// Two kernels.  The workgroup kernel: one 256-thread workgroup per (sequence, head); thread
+// (g, c) of a [groups x dv/4] arrangement owns 16-byte column c of partitions g, g + groups,
+// ...  The merge is bound by the latency of a few dependent steps, not by bandwidth, so the
+// order is: issue the loads of
 // the thread's first kR partial columns and of the first lse values at once, before the
 // partition count is known (bounded by max_parts), then take the block max, write the weights
 // to LDS while summing them, and only then consume the partial columns already in registers.
 // Partitions beyond kR * groups (long sequences, wide heads) follow in further chunks of
 // kR * groups.  Every sum runs in a fixed order, so the result is bitwise reproducible.
+
+#include <cstdlib>
+#include <cstring>
 
 #include "device_common.h"
 
@@ -129,9 +133,89 @@ __global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
   if (a.lse_out && tid == 0) a.lse_out[row] = big + logf(tot);
 }
 
+// One wave per (sequence, head) for narrow heads and few partials, the common case once the
+// decode kernels merge groups of partitions on chip: no barrier at all.  Lane (s, c) of a
+// [64 / cols x cols] arrangement owns 16-byte column c of partitions s, s + S, s + 2S, ...
+// (S = 64 / cols); lane p also holds lse_p.  The maximum and the sum of the weights are wave
+// reductions, each lane fetches the weight of its partitions from the lane holding them, and
+// the column sums are folded across the S lanes of a column with lane swaps.  All loads are
+// issued before the partition count is used.  Fixed order everywhere: bitwise reproducible.
+static constexpr int kWaveParts = 16;   // partitions per lane held in registers
+
+__global__ __launch_bounds__(kThreads) void merge_lse_wave_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.batch * a.hq) return;  // uniform per wave
+  const int b = (int)(row / a.hq);
+  const int cols = a.dv >> 2;
+  const int S = 64 / cols;
+  const int s = lane / cols;
+  const int c = lane - s * cols;
+  const float* lrow = a.lse_part + row * a.max_parts;
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.o_part + row * a.max_parts * a.dv);
+  const bool ext = a.o_ext != nullptr;
+  f32x4 ov[kWaveParts];
+#pragma unroll
+  for (int k = 0; k < kWaveParts; ++k) {
+    const int p = s + k * S;
+    ov[k] = p < a.max_parts ? orow[(int64_t)p * cols + c] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float l0 = lane < a.max_parts ? lrow[lane] : kNegInfG;
+  const float lx = ext ? a.lse_ext[row] : kNegInfG;
+  const int np_raw = a.nparts[b];
+  const int np = np_raw < 0 ? 0 : (np_raw > a.max_parts ? a.max_parts : np_raw);
+  const float big = fmaxf(wave_max(lane < np ? l0 : kNegInfG), lx);
+  f32x4* orow_out = reinterpret_cast<f32x4*>(a.o_out + row * a.dv);
+  if (big == kNegInfG) {
+    if (lane < cols) orow_out[lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.lse_out && lane == 0) a.lse_out[row] = kNegInfG;
+    return;
+  }
+  const float wl = lane < np ? expf(l0 - big) : 0.f;
+  const float wx = ext ? expf(lx - big) : 0.f;
+  const float tot = wave_sum(wl) + wx;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kWaveParts; ++k) {
+    const int p = s + k * S;
+    const float w = __shfl(wl, p < 64 ? p : 0);
+    if (p < np) acc += ov[k] * w;  // a select: stale slots never enter the sum
+  }
+  for (int o = cols; o < 64; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o);
+    acc.y += __shfl_xor(acc.y, o);
+    acc.z += __shfl_xor(acc.z, o);
+    acc.w += __shfl_xor(acc.w, o);
+  }
+  if (lane < cols) {
+    f32x4 o = acc;
+    if (ext) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[lane] * wx;
+    orow_out[lane] = o * (1.f / tot);
+  }
+  if (a.lse_out && lane == 0) a.lse_out[row] = big + logf(tot);
+}
+
+// The wave kernel takes heads of 4 .. 128 values (a power-of-two number of 16-byte columns)
+// with every partition slot in its registers; anything else goes to the workgroup kernel.
+// KVATTN_MERGE_KERNEL=block|wave overrides the choice (tuning and tests).
+bool merge_uses_wave(const MergeArgs& a) {
+  const int cols = a.dv >> 2;
+  const bool fits = (a.dv & 3) == 0 && cols >= 1 && cols <= 32 && (64 % cols) == 0 &&
+                    a.max_parts <= (64 / cols) * kWaveParts && a.max_parts <= 64;
+  const char* e = std::getenv("KVATTN_MERGE_KERNEL");
+  if (e && std::strcmp(e, "block") == 0) return false;
+  return fits;
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.batch * a.hq;
-  hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
+  if (merge_uses_wave(a)) {
+    const int64_t per = kThreads / 64;
+    hipLaunchKernelGGL(merge_lse_wave_kernel, dim3((unsigned)((rows + per - 1) / per)),
+                       dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -326,3 +326,54 @@ def test_split_step_with_native_host_share(variant, kw, seqs, group_parts):
         _say(f"[split-step] step {i} out error {err:.3e}")
         assert err <= oc.out_tol(case)
         assert float(np.max(np.abs(lse[sel] - lse_ref[sel]))) <= oc.lse_tol(case)
+
+
+# ---------------------------------------------------------------- the two merge kernels
+@pytest.mark.parametrize("dv,max_parts", [(64, 1), (64, 32), (128, 4), (128, 16), (128, 32),
+                                          (256, 8), (512, 40)])
+@pytest.mark.parametrize("ext", [False, True])
+def test_merge_kernels_match_oracle_and_each_other(dv, max_parts, ext):
+    """kvattn_merge_lse on random partials (counts from 0 to max_parts, -inf entries) against
+    the oracle's float64 merge; narrow heads with few partials take the wave kernel, the others
+    the workgroup kernel, and forcing the workgroup kernel gives the same result within
+    rounding."""
+    import os
+    from paged_kv_cache_mla_amd.api import merge_lse
+    rng = np.random.default_rng(dv * 100 + max_parts + ext)
+    B, hq = 5, 6
+    o_part = rng.standard_normal((B, hq, max_parts, dv)).astype(np.float32)
+    lse = (rng.standard_normal((B, hq, max_parts)) * 3).astype(np.float32)
+    lse[rng.random(lse.shape) < 0.15] = -np.inf
+    nparts = rng.integers(0, max_parts + 1, B).astype(np.int32)
+    nparts[0], nparts[-1] = max_parts, 0
+    o_x = rng.standard_normal((B, hq, dv)).astype(np.float32) if ext else None
+    l_x = (rng.standard_normal((B, hq)) * 3).astype(np.float32) if ext else None
+    if ext:
+        l_x[1, 2] = -np.inf
+    dev = lambda a: None if a is None else torch.from_numpy(a).cuda()  # noqa: E731
+    outs = {}
+    for kernel in ("auto", "block"):
+        if kernel == "block":
+            os.environ["KVATTN_MERGE_KERNEL"] = "block"
+        try:
+            o = torch.empty((B, hq, dv), dtype=torch.float32, device="cuda")
+            l = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+            merge_lse(dev(o_part), dev(lse), dev(nparts), B, hq, max_parts, dv, o, dev(o_x),
+                      dev(l_x), l)
+            torch.cuda.synchronize()
+            outs[kernel] = (o.cpu().numpy(), l.cpu().numpy())
+        finally:
+            os.environ.pop("KVATTN_MERGE_KERNEL", None)
+    for b in range(B):
+        parts_o = [o_part[b, :, p] for p in range(nparts[b])] + ([o_x[b]] if ext else [])
+        parts_l = [lse[b, :, p] for p in range(nparts[b])] + ([l_x[b]] if ext else [])
+        if not parts_o:
+            o_ref, l_ref = np.zeros((hq, dv)), np.full(hq, -np.inf)
+        else:
+            o_ref, l_ref = oracle.merge(parts_o, parts_l)
+        for kernel, (o, l) in outs.items():
+            assert np.max(np.abs(o[b] - o_ref)) <= 1e-5 * max(1.0, np.max(np.abs(o_ref))), (kernel, b)
+            fin = np.isfinite(l_ref)
+            assert np.array_equal(np.isneginf(l[b]), ~fin), (kernel, b)
+            assert np.max(np.abs(l[b][fin] - l_ref[fin]), initial=0.0) <= 1e-5, (kernel, b)
+    assert np.max(np.abs(outs["auto"][0] - outs["block"][0])) <= 1e-6
