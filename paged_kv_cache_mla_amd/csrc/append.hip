@@ -26,36 +26,79 @@ struct AppendArgs {
   int32_t hkv, dk, dv, bs, bs_shift, esize, latent;
 };
 
-__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+constexpr int kAppendThreads = 256;
+constexpr int kKPer = 4;  // K chunks per thread held in registers (heads * Dk / x <= 1024)
+constexpr int kVPer = 8;  // V elements per thread held in registers (Hkv * Dv <= 2048)
+
+__global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   const int b = blockIdx.x / a.n_new;
   const int j = blockIdx.x - b * a.n_new;
+  const int tid = threadIdx.x;
+  const int x = 16 / a.esize;          // elements per 16-byte chunk
+  const int kchunks = a.dk / x;        // chunks of one head's key
+  const int heads = a.latent ? 1 : a.hkv;
+  const int nk = heads * kchunks;
+  const int nv = a.latent ? 0 : a.hkv * a.dv;
+  const int64_t row = (int64_t)b * a.n_new + j;
+  const char* ksrc = a.k_new + row * heads * a.dk * a.esize;
+  const char* vsrc = a.latent ? nullptr : a.v_new + row * a.hkv * a.dv * a.esize;
+  // The source values do not depend on where they go: their loads are issued first, so their
+  // latency overlaps the dependent position -> table-entry lookups below.
+  const bool in_regs = nk <= kAppendThreads * kKPer && nv <= kAppendThreads * kVPer;
+  uint4 kreg[kKPer];
+  uint32_t vreg[kVPer];
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < kKPer; ++r) {
+      const int i = tid + r * kAppendThreads;
+      kreg[r] = i < nk ? *reinterpret_cast<const uint4*>(ksrc + (int64_t)i * 16) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < kVPer; ++r) {
+      const int i = tid + r * kAppendThreads;
+      vreg[r] = i >= nv ? 0u
+                : a.esize == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(vsrc)[i]
+                               : reinterpret_cast<const uint32_t*>(vsrc)[i];
+    }
+  }
   const int64_t t = (int64_t)a.pos[b] + j;
   if (t < 0 || (t >> a.bs_shift) >= a.max_blocks) {
-    if (threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    if (tid == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
     return;
   }
   const int32_t pid = a.table[(int64_t)b * a.max_blocks + (t >> a.bs_shift)];
   if (!valid_block(a.rt, pid)) {
-    if (threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+    if (tid == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
     return;
   }
   char* blk = const_cast<char*>(block_ptr(a.rt, pid));
   const int ts = (int)(t & (a.bs - 1));
-  const int x = 16 / a.esize;          // elements per 16-byte chunk
-  const int kchunks = a.dk / x;        // chunks of one head's key
-  const int heads = a.latent ? 1 : a.hkv;
-  const int64_t row = (int64_t)b * a.n_new + j;
-  // K (or the latent): chunk c of head h goes to chunk slot ((h * kchunks + c) * bs + ts)
-  const char* ksrc = a.k_new + row * heads * a.dk * a.esize;
-  for (int i = threadIdx.x; i < heads * kchunks; i += blockDim.x) {
+  // K (or the latent): chunk c of head h goes to chunk slot ((h * kchunks + c) * bs + ts);
+  // V: element (h, d) goes to element hkv * bs * dk + (h * dv + d) * bs + ts
+  char* vdst = blk + (int64_t)a.hkv * a.bs * a.dk * a.esize;
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < kKPer; ++r) {
+      const int i = tid + r * kAppendThreads;
+      if (i < nk) *reinterpret_cast<uint4*>(blk + (((int64_t)i * a.bs + ts) << 4)) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < kVPer; ++r) {
+      const int i = tid + r * kAppendThreads;
+      if (i >= nv) continue;
+      const int64_t off = ((int64_t)i * a.bs + ts) * a.esize;
+      if (a.esize == 2)
+        *reinterpret_cast<uint16_t*>(vdst + off) = (uint16_t)vreg[r];
+      else
+        *reinterpret_cast<uint32_t*>(vdst + off) = vreg[r];
+    }
+    return;
+  }
+  for (int i = tid; i < nk; i += kAppendThreads) {
     const uint4 v = *reinterpret_cast<const uint4*>(ksrc + (int64_t)i * 16);
     *reinterpret_cast<uint4*>(blk + (((int64_t)i * a.bs + ts) << 4)) = v;
   }
-  if (a.latent) return;
-  // V: element (h, d) goes to element hkv * bs * dk + (h * dv + d) * bs + ts
-  const char* vsrc = a.v_new + row * a.hkv * a.dv * a.esize;
-  char* vdst = blk + (int64_t)a.hkv * a.bs * a.dk * a.esize;
-  for (int i = threadIdx.x; i < a.hkv * a.dv; i += blockDim.x) {
+  for (int i = tid; i < nv; i += kAppendThreads) {
     const int64_t off = ((int64_t)i * a.bs + ts) * a.esize;
     if (a.esize == 2)
       *reinterpret_cast<uint16_t*>(vdst + off) = reinterpret_cast<const uint16_t*>(vsrc)[i];
@@ -85,7 +128,8 @@ hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const vo
   a.bs_shift = bs_shift;
   a.esize = L.kv_dtype == KVATTN_F32 ? 4 : 2;
   a.latent = L.latent;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((int64_t)batch * n_new)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((int64_t)batch * n_new)), dim3(kAppendThreads), 0,
+                     st, a);
   return hipGetLastError();
 }
 
