@@ -483,11 +483,18 @@ def write_side_bench(args):
         gt, gl, _, _ = store.views()
         table_dev = torch.from_numpy(gt).cuda()
         log(f"[write] {routing}: appending {B} x {L0} prefill tokens")
+        sp0 = torch.cuda.current_stream().cuda_stream
+        pre_ms = 0.0
+        pos = torch.zeros(1, dtype=torch.int32, device="cuda")
         for b in range(B):
             k = torch.randn(1, L0, hkv, d, device="cuda", dtype=torch.bfloat16).view(torch.int16)
             v = torch.randn(1, L0, hkv, d, device="cuda", dtype=torch.bfloat16).view(torch.int16)
-            pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+            e0, e1 = timer.event(), timer.event()
+            timer.record(e0, sp0)
             append_kv(dev_pool, k, v, _lib.BF16, table_dev[b:b + 1], per_seq, pos)
+            timer.record(e1, sp0)
+            torch.cuda.synchronize()
+            pre_ms += timer.elapsed_ms(e0, e1)
         store.commit([L0] * B)
         store.place_prefill()
         torch.cuda.synchronize()
@@ -535,7 +542,10 @@ def write_side_bench(args):
         wall = time.perf_counter() - t_all
         app_us = [timer.elapsed_ms(a, b_) * 1e3 for a, b_ in evs[warm:]]
         gt, gl, ct, cl = store.views()
-        res = {"steps": steps, "append_us": round(float(np.mean(app_us)), 2),
+        pre_bytes = B * L0 * hkv * 2 * d * 2
+        res = {"prefill_append_us_per_seq": round(pre_ms * 1e3 / B, 1),
+               "prefill_append_GBps": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+               "steps": steps, "append_us": round(float(np.mean(app_us)), 2),
                "wall_us_per_step": round(wall / steps * 1e6, 2),
                "host_us_per_step": round(host_s / steps * 1e6, 2),
                "store_calls_us_per_step": round(store_s / steps * 1e6, 2),

@@ -107,6 +107,99 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   }
 }
 
+// Appends of a tile or more per sequence (prefill): one workgroup per (sequence, touched tile
+// of T tokens, T a power of two dividing the block size, the largest whose K/V fit 64 KiB of
+// LDS).  The tokens of the tile are read from the source rows, which are contiguous, into
+// LDS, then written with consecutive lanes on consecutive token slots: K chunk slots of one
+// (head, chunk) are consecutive 16-byte slots, and V values of one (head, dim) are consecutive
+// elements, so both the reads and the writes coalesce (the per-token kernel writes V as
+// scattered 2-byte stores).  Tokens with an index below 0 or past the table, or in a block
+// whose entry is not a valid id, are flagged exactly as the per-token kernel flags them and
+// are not written: the two kernels leave the same bytes.
+__global__ void __launch_bounds__(kAppendThreads) append_blocks_kernel(AppendArgs a, int nt_max,
+                                                                       int tshift) {
+  extern __shared__ uint4 stage[];  // [T tokens][heads * Dk + Hkv * Dv] elements
+  const int b = blockIdx.x / nt_max;
+  const int i = blockIdx.x - b * nt_max;
+  const int tid = threadIdx.x;
+  const int64_t pos = a.pos[b];
+  // tile of T = 2^tshift tokens (T divides bs): [ti * T, (ti + 1) * T)
+  const int64_t ti = (pos >> tshift) + i;  // floor for negative positions too
+  const int64_t lo = max(pos, ti << tshift);
+  const int64_t hi = min(pos + a.n_new, (ti + 1) << tshift);
+  if (lo >= hi) return;  // past the appended range
+  const int64_t bi = ti >> (a.bs_shift - tshift);
+  if (bi < 0 || bi >= a.max_blocks) {
+    if (tid == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    return;
+  }
+  const int32_t pid = a.table[(int64_t)b * a.max_blocks + bi];
+  if (!valid_block(a.rt, pid)) {
+    if (tid == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+    return;
+  }
+  char* blk = const_cast<char*>(block_ptr(a.rt, pid));
+  const int x = 16 / a.esize;
+  const int kchunks = a.dk / x;
+  const int heads = a.latent ? 1 : a.hkv;
+  const int nk = heads * kchunks;                        // K chunks of one token
+  const int nvb = a.latent ? 0 : a.hkv * a.dv * a.esize; // V bytes of one token
+  const int ntok = (int)(hi - lo);
+  const int ts0 = (int)(lo - (bi << a.bs_shift));
+  const int64_t j0 = lo - pos;                           // first source row
+  // 1. source rows -> LDS, 16 bytes per lane, contiguous
+  const int kbytes = nk * 16;
+  char* sk = reinterpret_cast<char*>(stage);
+  char* sv = sk + (int64_t)ntok * kbytes;
+  const int64_t krow = (int64_t)heads * a.dk * a.esize;
+  const char* ksrc = a.k_new + ((int64_t)b * a.n_new + j0) * krow;
+  for (int q = tid; q < ntok * nk; q += kAppendThreads)
+    reinterpret_cast<uint4*>(sk)[q] = reinterpret_cast<const uint4*>(ksrc)[q];
+  if (nvb) {
+    const char* vsrc = a.v_new + ((int64_t)b * a.n_new + j0) * nvb;
+    if ((nvb & 15) == 0 && (reinterpret_cast<uintptr_t>(vsrc) & 15) == 0) {
+      for (int q = tid; q < ntok * nvb / 16; q += kAppendThreads)
+        reinterpret_cast<uint4*>(sv)[q] = reinterpret_cast<const uint4*>(vsrc)[q];
+    } else {
+      for (int q = tid; q < ntok * nvb / a.esize; q += kAppendThreads) {
+        if (a.esize == 2)
+          reinterpret_cast<uint16_t*>(sv)[q] = reinterpret_cast<const uint16_t*>(vsrc)[q];
+        else
+          reinterpret_cast<uint32_t*>(sv)[q] = reinterpret_cast<const uint32_t*>(vsrc)[q];
+      }
+    }
+  }
+  __syncthreads();
+  // 2. K: slot ((h * kchunks + c) * bs + ts) <- chunk c of head h of token ts; the token index
+  //    runs fastest over the lanes
+  for (int q = tid; q < nk * ntok; q += kAppendThreads) {
+    const int hc = q / ntok, tt = q - hc * ntok;
+    *reinterpret_cast<uint4*>(blk + (((int64_t)hc * a.bs + ts0 + tt) << 4)) =
+        *reinterpret_cast<const uint4*>(sk + (int64_t)tt * kbytes + hc * 16);
+  }
+  if (!nvb) return;
+  // 3. V: element hkv * bs * dk + (h * dv + d) * bs + ts, token index fastest
+  char* vdst = blk + (int64_t)a.hkv * a.bs * a.dk * a.esize;
+  const int nve = a.hkv * a.dv;
+  for (int q = tid; q < nve * ntok; q += kAppendThreads) {
+    const int e = q / ntok, tt = q - e * ntok;
+    const int64_t off = ((int64_t)e * a.bs + ts0 + tt) * a.esize;
+    if (a.esize == 2)
+      *reinterpret_cast<uint16_t*>(vdst + off) =
+          reinterpret_cast<const uint16_t*>(sv + (int64_t)tt * nvb)[e];
+    else
+      *reinterpret_cast<uint32_t*>(vdst + off) =
+          reinterpret_cast<const uint32_t*>(sv + (int64_t)tt * nvb)[e];
+  }
+}
+
+// Bytes of one token's K and V as the block kernel stages them
+static size_t append_token_bytes(const kvattn_layout& L) {
+  const int e = L.kv_dtype == KVATTN_F32 ? 4 : 2;
+  const int heads = L.latent ? 1 : L.num_kv_heads;
+  return ((size_t)heads * L.head_dim_k + (L.latent ? 0 : (size_t)L.num_kv_heads * L.head_dim_v)) * e;
+}
+
 hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const void* k_new,
                          const void* v_new, const int32_t* table, const int32_t* pos,
                          int32_t* err, int32_t batch, int32_t n_new, int32_t max_blocks,
@@ -128,8 +221,20 @@ hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const vo
   a.bs_shift = bs_shift;
   a.esize = L.kv_dtype == KVATTN_F32 ? 4 : 2;
   a.latent = L.latent;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((int64_t)batch * n_new)), dim3(kAppendThreads), 0,
-                     st, a);
+  // tile: the largest power of two dividing bs whose tokens fit 64 KiB of LDS
+  const size_t tok = append_token_bytes(L);
+  int tshift = bs_shift;
+  while (tshift > 0 && ((size_t)1 << tshift) * tok > 64 * 1024) --tshift;
+  const int T = 1 << tshift;
+  if (n_new >= T && (size_t)T * tok <= 64 * 1024 && T >= 8) {
+    // tiles touched by n_new tokens from any position: at most ceil(n_new / T) + 1
+    const int nt_max = (n_new + T - 1) / T + 1;
+    hipLaunchKernelGGL(append_blocks_kernel, dim3((unsigned)((int64_t)batch * nt_max)),
+                       dim3(kAppendThreads), (size_t)T * tok, st, a, nt_max, tshift);
+  } else {
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)((int64_t)batch * n_new)),
+                       dim3(kAppendThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

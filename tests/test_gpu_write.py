@@ -70,13 +70,16 @@ def _setup(layout, rng, batch, max_blocks, region_blocks):
 
 
 @pytest.mark.parametrize("name", sorted(LAYOUTS))
-@pytest.mark.parametrize("n_new", [1, 37])
+@pytest.mark.parametrize("n_new", [1, 37, 200])
 def test_append_matches_oracle_writer(name, n_new):
+    """One token per sequence takes the per-token kernel; 37 and 200 the tile kernel (tiles of
+    16 tokens for these GQA layouts, 32 for MLA); every byte must match the oracle's writer."""
     from paged_kv_cache_mla_amd.api import append_kv
     layout = LAYOUTS[name]
     _say(f"[append] {name} n_new={n_new}")
     rng = np.random.default_rng(100 * sorted(LAYOUTS).index(name) + n_new)
-    batch, max_blocks = 5, 6
+    batch = 5
+    max_blocks = max(6, -(-(n_new + layout.block_size) // layout.block_size) + 1)
     region_blocks = [13, batch * max_blocks + 4 - 13]
     regions, dev, pool, table = _setup(layout, rng, batch, max_blocks, region_blocks)
     cap = max_blocks * layout.block_size
@@ -104,30 +107,33 @@ def oracle_dtype(layout):
     return _lib.BF16 if layout.dtype == "bf16" else _lib.F32
 
 
-def test_append_flags_absent_and_out_of_range_tokens_and_writes_the_rest():
+@pytest.mark.parametrize("n_new", [4, 40])
+def test_append_flags_absent_and_out_of_range_tokens_and_writes_the_rest(n_new):
+    """Both kernels (4 tokens: per token; 40: tiles) flag and skip exactly the tokens whose
+    index is negative or past the table, or whose block entry is not a valid id."""
     from paged_kv_cache_mla_amd import _lib
     from paged_kv_cache_mla_amd.api import append_kv
     layout = LAYOUTS["gqa_bf16"]
     rng = np.random.default_rng(3)
-    batch, max_blocks = 3, 4
+    bs = layout.block_size
+    batch, max_blocks = 4, 8
     region_blocks = [batch * max_blocks]
     regions, dev, pool, table = _setup(layout, rng, batch, max_blocks, region_blocks)
     table = table.copy()
     table[1, 2] = -1                                   # ABSENT inside sequence 1's range
-    bs = layout.block_size
-    n_new = 4
-    pos = np.array([5, 2 * bs - 2, max_blocks * bs - 2], np.int32)  # seq 2 runs past the table
+    pos = np.array([5, 2 * bs - 2, max_blocks * bs - 2,  # seq 2 runs past the table
+                    -3], np.int32)                       # seq 3 starts before token 0
     k = _random_storage(rng, (batch, n_new, 4, 128), layout)
     v = _random_storage(rng, (batch, n_new, 4, 128), layout)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     append_kv(pool, _dev(k), _dev(v), _lib.BF16, _dev(table), max_blocks, _dev(pos), err)
     torch.cuda.synchronize()
     assert int(err.item()) == _lib.ERR_BAD_BLOCK | _lib.ERR_BAD_SEQ
-    # expected: every token whose block is valid is written, the others are not
+    # expected: every token with an index in the table and a valid block is written
     for b in range(batch):
         for j in range(n_new):
             t = int(pos[b]) + j
-            if t // bs >= max_blocks or table[b, t // bs] < 0:
+            if t < 0 or t // bs >= max_blocks or table[b, t // bs] < 0:
                 continue
             oracle.write_tokens(layout, regions, region_blocks, table[b], t, k[b, j:j + 1],
                                 v[b, j:j + 1])
