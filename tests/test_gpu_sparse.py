@@ -117,14 +117,16 @@ def test_sparse_selection_matches_oracle(name, density):
     _check(case, sel, *res, range(case.batch))
 
 
-def test_sparse_selection_full_size_sampled():
-    """The 16 x 32K layer at 1/8 block density, grouped as bench.py times it."""
-    from bench import GROUP_PARTS
+@pytest.mark.parametrize("name,density,group_parts,seqs", [
+    ("gqa_32k", 1 / 8, 4, [0, 9]), ("mla_16k", 1 / 4, 2, [0, 31])])
+def test_sparse_selection_full_size_sampled(name, density, group_parts, seqs):
+    """Full-size layers at a fraction of their blocks, grouped (the 16 x 32K GQA layer at 1/8,
+    the 32 x 16K MLA layer at 1/4)."""
     from paged_kv_cache_mla_amd.session import DeviceCase
-    _say("[sparse] gqa_32k full, density 1/8")
-    case = make_case("gqa_32k", "full")
+    _say(f"[sparse] {name} full, density {density}")
+    case = make_case(name, "full")
     dc = DeviceCase(case)
     rng = np.random.default_rng(8)
-    sel = _selection(rng, case, 1 / 8, extras=False)
-    res = _run_sparse(case, dc, sel, group_parts=GROUP_PARTS["gqa_32k"] // 4)
-    _check(case, sel, *res, [0, 9])
+    sel = _selection(rng, case, density, extras=False)
+    res = _run_sparse(case, dc, sel, group_parts=group_parts)
+    _check(case, sel, *res, seqs)
