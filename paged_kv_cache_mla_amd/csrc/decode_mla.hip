@@ -21,8 +21,9 @@
 //      write and for the transposed read below), and the scores to LDS;
 //   4. after one barrier every wave reads all 64 x 16 scores, updates the running max /
 //      normaliser and forms the bf16 P^T operands, then accumulates O^T for its 128 output
-//      dims, V^T P^T with v_mfma_f32_16x16x16_bf16, reading 4-token x 8-dim patches of the
-//      value part from LDS and regrouping them in registers with byte permutes.
+//      dims, V^T P^T with v_mfma_f32_16x16x32_bf16 (two 32-token k-steps per stage), reading
+//      8-token x 8-dim patches of the value part from LDS and regrouping them in registers
+//      with byte permutes.
 // The swizzle only touches the low 4 token bits, so all LDS addresses are a few per-lane bases
 // plus immediate offsets; computing those bases once keeps ~100 registers free for the ring.
 // LDS (values and scores) is double-buffered by stage parity, so one barrier per stage
@@ -43,6 +44,7 @@ static constexpr int kMlaVChunks = kMlaDv / 8;  // 64 chunks hold the value part
 static constexpr int kMlaKs = kMlaChunks / 4;   // 18 k-steps of the score product
 static constexpr int kMlaBs = 64;
 static constexpr int kRing = 3;                 // stages held in registers per wave
+static constexpr int kWin = 128;                // stages whose block ids a window holds
 
 __device__ __forceinline__ int lat_slot(int c, int t) { return c * kMlaBs + (t ^ (c & 15)); }
 
@@ -106,9 +108,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   // loads, the prefetch included); the prologue's loads past a short group re-read its last
   // block (clamped, harmless), the last round skips them.
   const uint32_t loff = (uint32_t)((g4 * kMlaBs + 16 * wv + n) * 16);
+  // The stages are walked in windows of up to kWin; the window's block ids are read once into
+  // two registers per lane (lane i: stages i and 64 + i of the window) and picked out with
+  // lane reads.  A table load per stage would make every stage wait for all outstanding
+  // loads (the load counter drains in order), prefetch included.
+  int w0 = 0, wn = 0, pid0 = 0, pid1 = 0;
   auto issue = [&](int slot, int s, bool guard) {
-    if (guard && s >= nst) return;
-    const int32_t pid = trow[st_lo + min(s, nst - 1)];
+    if (guard && s >= wn) return;
+    const int r = min(s, wn - 1);
+    const int32_t pa = __builtin_amdgcn_readlane(pid0, r & 63);
+    const int32_t pb = __builtin_amdgcn_readlane(pid1, r & 63);
+    const int32_t pid = r < 64 ? pa : pb;
     const bool ok = valid_block(a.rt, pid);
     vld[slot] = ok;
     gchar* base = block_addr(a.rt, ok ? pid : 0) + loff;
@@ -124,13 +134,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   bool bad = false;
   // LDS slots (16-byte units within a value buffer): the value-part write of chunk g4 + 4j
   // is wslot[j % 4] + (j / 4) * 1024, the transposed read of chunk 16 wv + n, token
-  // 16 ks + 4 g4 + i is rslot[i] + 16 ks (the swizzle only touches the low 4 token bits)
-  int wslot[4], rslot[4];
+  // 32 kk + 8 g4 + i is rslot[i] + 32 kk (the swizzle only touches the low 4 token bits)
+  int wslot[4], rslot[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    wslot[q] = lat_slot(g4 + 4 * q, 16 * wv + n);
-    rslot[q] = lat_slot(16 * wv + n, 4 * g4 + q);
-  }
+  for (int q = 0; q < 4; ++q) wslot[q] = lat_slot(g4 + 4 * q, 16 * wv + n);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rslot[i] = lat_slot(16 * wv + n, 8 * g4 + i);
 
   // One stage: refill the slot of stage s + kRing - 1, then compute stage s from slot r.
   auto stage = [&](int r, int s, bool guard) {
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < kMlaVChunks / 4; ++j)
       vbuf[(j >> 2) * 1024 + wslot[j & 3]] = __builtin_bit_cast(uint4, kb[r][j]);
-    const int tbase = (st_lo + s) << 6;
+    const int tbase = (st_lo + w0 + s) << 6;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tl = 16 * wv + 4 * g4 + i;
@@ -159,15 +168,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // 4a. softmax update over the 64 tokens, all waves alike
-    float sv[4][4];
+    // 4a. softmax update over the 64 tokens, all waves alike; lane (n, g4) takes head n's
+    //     scores of tokens 32*kk + 8*g4 + i (i < 8), the k-slots of the PV product below
+    float sv[2][8];
     float mx = kNegInfM;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[ks][i] = sx[buf][16 * ks + 4 * g4 + i][n];
-        mx = fmaxf(mx, sv[ks][i]);
+      for (int i = 0; i < 8; ++i) {
+        sv[kk][i] = sx[buf][32 * kk + 8 * g4 + i][n];
+        mx = fmaxf(mx, sv[kk][i]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -175,53 +185,65 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     const float mref = mnew == kNegInfM ? 0.f : mnew;
     const float alpha = __builtin_amdgcn_exp2f(m - mref);
     m = mnew;
-    i16x4 pop[4];
+    u32x4 pop[2];
     float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t p01 = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[ks][0] - mref), __builtin_amdgcn_exp2f(sv[ks][1] - mref));
-      const uint32_t p23 = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[ks][2] - mref), __builtin_amdgcn_exp2f(sv[ks][3] - mref));
-      // the normaliser sums the bf16 weights the PV product uses
-      part += (bf16_to_f32(p01 & 0xffffu) + bf16_to_f32(p01 >> 16)) +
-              (bf16_to_f32(p23 & 0xffffu) + bf16_to_f32(p23 >> 16));
-      pop[ks] = as_i16x4(make_uint2(p01, p23));
-    }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t p = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[kk][2 * j] - mref),
+                                       __builtin_amdgcn_exp2f(sv[kk][2 * j + 1] - mref));
+        // the normaliser sums the bf16 weights the PV product uses
+        part += bf16_to_f32(p & 0xffffu) + bf16_to_f32(p >> 16);
+        pop[kk][j] = p;
+      }
     lsum = lsum * alpha + part;
 
-    // 4b. O^T for dims 8*c + e, c = 16*wv + row (row = MFMA row), e = 0..7
+    // 4b. O^T for dims 8*c + e, c = 16*wv + row (row = MFMA row), e = 0..7: per 32-token
+    //     k-step, lane (row, g4) reads chunk c of its 8 tokens and regroups the 8 x 8 bf16
+    //     values dim-major with byte permutes, one v_mfma_f32_16x16x32_bf16 per e
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 r4[4];
+    for (int kk = 0; kk < 2; ++kk) {
+      uint4 r8[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r4[i] = vbuf[16 * ks + rslot[i]];
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r4[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r4[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r4[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r4[3]);
+      for (int i = 0; i < 8; ++i) r8[i] = vbuf[32 * kk + rslot[i]];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // dims 8c + 2q (low halves) and 8c + 2q + 1 (high halves) of the 4 tokens
-        const uint2 lo_op = make_uint2((w0[q] & 0xffffu) | (w1[q] << 16), (w2[q] & 0xffffu) | (w3[q] << 16));
-        const uint2 hi_op = make_uint2((w0[q] >> 16) | (w1[q] & 0xffff0000u), (w2[q] >> 16) | (w3[q] & 0xffff0000u));
-        acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(lo_op), pop[ks], acc[2 * q], 0, 0, 0);
-        acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(hi_op), pop[ks], acc[2 * q + 1], 0, 0, 0);
+        // dims 8c + 2q (low halves) and 8c + 2q + 1 (high halves) of the 8 tokens
+        u32x4 lo_op, hi_op;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x = reinterpret_cast<const uint32_t*>(&r8[2 * j])[q];
+          const uint32_t y = reinterpret_cast<const uint32_t*>(&r8[2 * j + 1])[q];
+          lo_op[j] = (x & 0xffffu) | (y << 16);
+          hi_op[j] = (x >> 16) | (y & 0xffff0000u);
+        }
+        acc[2 * q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo_op), as_bf16x8(pop[kk]), acc[2 * q], 0, 0, 0);
+        acc[2 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi_op), as_bf16x8(pop[kk]), acc[2 * q + 1], 0, 0, 0);
       }
     }
   };
 
+  // Each window fills the ring, runs, and drains it; kWin is even, so the LDS buffer parity
+  // s & 1 of a window's stage s is that of the group's stage w0 + s.
+  for (; w0 < nst; w0 += kWin) {
+    wn = min(kWin, nst - w0);
+    pid0 = trow[st_lo + w0 + min(lane, wn - 1)];
+    pid1 = trow[st_lo + w0 + min(64 + lane, wn - 1)];
 #pragma unroll
-  for (int r = 0; r < kRing - 1; ++r) issue(r, r, false);
-  int it = 0;
-  for (; it + 2 * kRing - 1 <= nst; it += kRing) {  // every refill inside the group
+    for (int r = 0; r < kRing - 1; ++r) issue(r, r, false);
+    int it = 0;
+    for (; it + 2 * kRing - 1 <= wn; it += kRing) {  // every refill inside the window
 #pragma unroll
-    for (int r = 0; r < kRing; ++r) stage(r, it + r, false);
-  }
-  for (; it < nst; it += kRing) {
+      for (int r = 0; r < kRing; ++r) stage(r, it + r, false);
+    }
+    for (; it < wn; it += kRing) {
 #pragma unroll
-    for (int r = 0; r < kRing; ++r)
-      if (it + r < nst) stage(r, it + r, true);  // uniform over the workgroup
+      for (int r = 0; r < kRing; ++r)
+        if (it + r < wn) stage(r, it + r, true);  // uniform over the workgroup
+    }
   }
   if (bad && lane == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 

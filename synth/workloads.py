@@ -275,6 +275,18 @@ def _mla_16k(variant):
                    1 / np.sqrt(192.0), [need], table, lens, None, [part] * len(lens), rq, rkv)
 
 
+def mla_case(lens, part_tokens, tok_begin=None, seed: int = 1006) -> Case:
+    """A latent-cache (MLA) case of the 16K layer's geometry (bs 64, Dk 576, Dv 512, 16 heads)
+    with the given context lengths, partition sizes and first tokens, over a pool of exactly
+    the blocks needed, in random order."""
+    rq, rkv, rtab, _ = _streams(seed)
+    bs = 64
+    max_blocks = _nblocks(max(lens), bs)
+    table, need = _permuted_tables(rtab, lens, bs, max_blocks)
+    return _finish("mla_custom", "small", seed, bs, 1, 576, 512, "bf16", True, 16,
+                   1 / np.sqrt(192.0), [need], table, lens, tok_begin, part_tokens, rq, rkv)
+
+
 def make_case(name: str, variant: str = "small", **kw) -> Case:
     """Build workload `name` ("tiny_fp32", "gqa_32k", "split_128k", "prefix_shared",
     "mla_16k") in variant "small" or "full"; split_128k takes r (default 0.5)."""

@@ -106,6 +106,24 @@ def test_grouped_partials_match_oracle(name, group_parts):
     _check_partials(case, dc, group_parts=group_parts)
 
 
+def test_long_mla_groups_cross_block_id_windows():
+    """Latent-cache groups longer than the 128 stages (64-token blocks) whose block ids the
+    kernel holds in registers at a time: a group of 257 stages starting mid-block (two full
+    windows and a one-stage window), a group of exactly 128 stages followed by a short one,
+    and a short sequence, each against the oracle."""
+    from synth import mla_case
+    case = mla_case([20000, 64 * 130 + 5, 777], [8192, 4096, 512], tok_begin=[37, 0, 100])
+    _say(f"[mla windows] L={case.ctx_lens.tolist()} P={case.part_tokens.tolist()} group_parts=2")
+    dc, o, lse = _run(case, None, 2)
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    _say(f"[mla windows] out error {err:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc, group_parts=2)
+
+
 @pytest.mark.parametrize("name", ["gqa_32k", "prefix_shared", "split_128k"])
 def test_generic_kernel_matches_oracle(name, monkeypatch):
     monkeypatch.setenv("KVATTN_FORCE_GENERIC", "1")
