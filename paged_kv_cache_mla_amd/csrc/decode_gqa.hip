@@ -155,20 +155,42 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
   bool bad = false;
   const float scale_log2 = a.scale_log2;
 
-  // scores of one tile, masked: lane (n, g4), register i = token 16*tile + 4*g4 + i, head n
-  auto scores = [&](int slot, int rel, float* sv) {
+  // scores of one tile, masked: lane (n, g4), register i = token 16*tile + 4*g4 + i, head n;
+  // bit i of the result is set when token i of the lane is inside the range
+  auto scores = [&](int slot, int rel, float* sv) -> uint32_t {
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KS; ++j)
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[slot][j]), qop[j], sacc, 0, 0, 0);
     const int tb = ((t_lo + rel) << 4) + 4 * g4;
+    uint32_t okbits = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tb + i;
       const bool ok = vld[slot] & (t >= lo) & (t < hi);  // bitwise: no short-circuit branches
       sv[i] = ok ? sacc[i] * scale_log2 : kNegInf;
+      okbits |= (uint32_t)ok << i;
     }
     bad |= !vld[slot] & (rel < ntiles);
+    return okbits;
+  };
+
+  // A tile not wholly inside the range (the range's first and last, the fully masked tiles of
+  // the last round, a tile of an invalid block) may hold anything in its outside token slots,
+  // NaN bit patterns included: a slot no token was ever written to, for instance.  A zero
+  // weight does not cancel a NaN in the PV product, so those V values are zeroed first.
+  auto edge_tile = [&](int slot, int rel) {
+    const int t0 = (t_lo + rel) << 4;
+    return !vld[slot] | (t0 < lo) | (t0 + 16 > hi);  // uniform
+  };
+  auto mask_v = [&](int slot, uint32_t okbits) {
+    const uint32_t m0 = ((okbits & 1u) ? 0xffffu : 0u) | ((okbits & 2u) ? 0xffff0000u : 0u);
+    const uint32_t m1 = ((okbits & 4u) ? 0xffffu : 0u) | ((okbits & 8u) ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      vb[slot][t][0] &= m0;
+      vb[slot][t][1] &= m1;
+    }
   };
 
   // One ring round: RING tiles starting at `it`, each pair's refill issued RING - 2 tiles
@@ -184,8 +206,10 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
       issue(fs, ra + RING - 2, guard);
       issue(fs + 1, ra + RING - 1, guard);
       float sva[4], svb[4];
-      scores(sa, ra, sva);
-      scores(sb, rb, svb);
+      const uint32_t oka = scores(sa, ra, sva);
+      const uint32_t okb = scores(sb, rb, svb);
+      if (edge_tile(sa, ra)) mask_v(sa, oka);
+      if (edge_tile(sb, rb)) mask_v(sb, okb);
       const float mx = rows_max(fmaxf(fmaxf(fmaxf(sva[0], sva[1]), fmaxf(sva[2], sva[3])),
                                       fmaxf(fmaxf(svb[0], svb[1]), fmaxf(svb[2], svb[3]))));
       if (__any(mx > m + kRescaleSlack)) {

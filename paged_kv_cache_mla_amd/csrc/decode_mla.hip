@@ -11,8 +11,9 @@
 // (sequence, group of partitions), walking the group's 64-token blocks ("stages") in order:
 //   1. wave w loads the latent rows of tokens 16w .. 16w+15 of a stage straight into
 //      registers with 16-byte non-temporal loads (the latent is read once per step) -- lane
-//      (n, g4) holds token n, 16-byte chunks g4 + 4j -- into a ring of kRing stages, so
-//      kRing - 1 stages (2 x 72 KiB per CU) are in flight while one is computed;
+//      (n, g4) holds token n, 16-byte chunks g4 + 4j -- into a ring of kRing stages; a slot
+//      is refilled as soon as its stage's rows are in LDS (step 3), so kRing stages
+//      (3 x 72 KiB per CU) are in flight through the softmax and PV of the current one;
 //   2. the same registers are the A operand of the scores S^T = C Q^T on the matrix cores
 //      (v_mfma_f32_16x16x32_bf16, 18 k-steps over the 576 dims, heads in the N columns; the
 //      Q^T operand is read from LDS, leaving the registers to the ring);
@@ -141,9 +142,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) rslot[i] = lat_slot(16 * wv + n, 8 * g4 + i);
 
-  // One stage: refill the slot of stage s + kRing - 1, then compute stage s from slot r.
+  // One stage: compute stage s from slot r; the slot is refilled with stage s + kRing as soon
+  // as its rows are in LDS, so kRing stages stay in flight through the softmax and PV.
   auto stage = [&](int r, int s, bool guard) {
-    issue((r + kRing - 1) % kRing, s + kRing - 1, guard);
     const int buf = s & 1;
     uint4* vbuf = vlat[buf];
     bad |= !vld[r];
@@ -154,17 +155,29 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     for (int j = 0; j < kMlaKs; ++j)
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[r][j]), as_bf16x8(qs[j * 64 + lane]), sacc, 0, 0, 0);
 
-    // 3. value part and scores to LDS
+    // 3. value part and scores to LDS.  In a stage not wholly inside the range (or of an
+    //    invalid block) the outside token slots may hold anything, NaN bit patterns included,
+    //    and a zero weight does not cancel a NaN in the PV product: their values are zeroed.
+    //    The zeros overwrite the lane's own slots just before the barrier, later in its
+    //    program order; in most stages no lane needs them and the branch skips them.
 #pragma unroll
     for (int j = 0; j < kMlaVChunks / 4; ++j)
       vbuf[(j >> 2) * 1024 + wslot[j & 3]] = __builtin_bit_cast(uint4, kb[r][j]);
     const int tbase = (st_lo + w0 + s) << 6;
+    const int tok = tbase + 16 * wv + n;
+    const bool zero_tok = !(vld[r] & (tok >= lo) & (tok < hi));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tl = 16 * wv + 4 * g4 + i;
       const int t = tbase + tl;
       const bool ok = vld[r] & (t >= lo) & (t < hi);
       sx[buf][tl][n] = ok ? sacc[i] * a.scale_log2 : kNegInfM;
+    }
+    issue(r, s + kRing, guard);
+    if (zero_tok) {
+#pragma unroll
+      for (int j = 0; j < kMlaVChunks / 4; ++j)
+        vbuf[(j >> 2) * 1024 + wslot[j & 3]] = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
@@ -233,9 +246,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     pid0 = trow[st_lo + w0 + min(lane, wn - 1)];
     pid1 = trow[st_lo + w0 + min(64 + lane, wn - 1)];
 #pragma unroll
-    for (int r = 0; r < kRing - 1; ++r) issue(r, r, false);
+    for (int r = 0; r < kRing; ++r) issue(r, r, false);
     int it = 0;
-    for (; it + 2 * kRing - 1 <= wn; it += kRing) {  // every refill inside the window
+    for (; it + 2 * kRing <= wn; it += kRing) {  // every refill inside the window
 #pragma unroll
       for (int r = 0; r < kRing; ++r) stage(r, it + r, false);
     }

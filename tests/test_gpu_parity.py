@@ -124,6 +124,56 @@ def test_long_mla_groups_cross_block_id_windows():
     _check_partials(case, dc, group_parts=2)
 
 
+def _poison_unused_slots(case):
+    """A copy of `case` whose pool holds NaN bit patterns in every token slot that no
+    sequence's range [tok_begin, L) uses: the tails of last blocks, the slots before
+    tok_begin, and blocks no table names.  The oracle never reads those slots."""
+    import dataclasses
+    lay = oc.layout_of(case)
+    bs, x = case.block_size, lay.chunk
+    total = sum(case.region_blocks)
+    used = np.zeros((total, bs), bool)
+    for b in range(case.batch):
+        beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
+        t = np.arange(beg, int(case.ctx_lens[b]))
+        used[case.table[b, t // bs], t % bs] = True
+    # token slot of every element of a block, from the block layout
+    if case.latent:
+        slot = np.broadcast_to(np.arange(bs)[None, :, None], (case.head_dim_k // x, bs, x)).ravel()
+    else:
+        hkv, dk, dv = case.num_kv_heads, case.head_dim_k, case.head_dim_v
+        slot = np.concatenate([
+            np.broadcast_to(np.arange(bs)[None, None, :, None], (hkv, dk // x, bs, x)).ravel(),
+            np.broadcast_to(np.arange(bs)[None, None, :], (hkv, dv, bs)).ravel()])
+    nan = np.uint16(0x7FC0) if case.dtype == "bf16" else np.float32(np.nan)
+    regions, first = [], 0
+    for reg, n in zip(case.regions, case.region_blocks):
+        r = reg.copy().reshape(n, -1)
+        for i in range(n):
+            r[i, ~used[first + i][slot]] = nan
+        regions.append(r.reshape(-1))
+        first += n
+    return dataclasses.replace(case, regions=regions)
+
+
+@pytest.mark.parametrize("name,group_parts", [("gqa_32k", 1), ("gqa_32k", 3), ("gqa_32k", 16),
+                                              ("mla_16k", 1), ("mla_16k", 3), ("split_128k", 4),
+                                              ("tiny_fp32", 1)])
+def test_nan_in_unused_token_slots_is_ignored(name, group_parts):
+    """Token slots outside every sequence's range may hold anything (a slot never written, a
+    stale block): NaN bit patterns there must not reach the output, although the kernels
+    read whole tiles and give those tokens zero weight."""
+    case = _poison_unused_slots(make_case(name, "small"))
+    _say(f"[poison] {name} group_parts={group_parts}")
+    ext = oc.external_partial(case) if case.ext_regions is not None else None
+    dc, o, lse = _run(case, ext, group_parts)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    o_ref, lse_ref = oc.full_reference(case)
+    assert oc.out_error(case, o, o_ref) <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+
+
 @pytest.mark.parametrize("name", ["gqa_32k", "prefix_shared", "split_128k"])
 def test_generic_kernel_matches_oracle(name, monkeypatch):
     monkeypatch.setenv("KVATTN_FORCE_GENERIC", "1")
