@@ -180,6 +180,42 @@ def summarize_profile(workload, fetch_dir, write_dir, stats_dir, out_path, comma
     return out_path
 
 
+def summarize_counters(workload, dirs, out_path, commands):
+    """Write the per-dispatch averages of the counters collected in `dirs` (one rocprofv3
+    --pmc run each) for this library's kernels, with the L2 hit rate derived from TCC_HIT_sum
+    and TCC_MISS_sum when both were collected."""
+    import glob
+    vals = {}   # kernel -> counter -> list of per-dispatch values
+    for d in dirs:
+        for r in _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0]):
+            if "kvattn::" not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    lines = [f"# rocprofv3 counters: {workload} ({DESCR[workload]})", "",
+             "Commands (from the repository root; rocprofv3 runs were started from /tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "Per-dispatch averages. MfmaUtil: percent of SIMD cycles with the matrix cores busy. "
+              "LdsBankConflict: bank-conflict cycles per LDS access cycle. MeanOccupancyPerCU: "
+              "resident waves per CU. L2 hit: TCC_HIT / (TCC_HIT + TCC_MISS).", "",
+              "| kernel | dispatches | " + " | ".join(names) + " | L2 hit |",
+              "|---|---|" + "---|" * len(names) + "---|"]
+    for k in sorted(vals, key=lambda k: -len(vals[k])):
+        v = vals[k]
+        n = max(len(x) for x in v.values())
+        avg = {c: sum(v[c]) / len(v[c]) for c in v}
+        cells = [f"{avg[c]:.4g}" if c in avg else "" for c in names]
+        hit = ""
+        if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg and avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"] > 0:
+            hit = f"{100 * avg['TCC_HIT_sum'] / (avg['TCC_HIT_sum'] + avg['TCC_MISS_sum']):.1f}%"
+        lines.append(f"| {_short(k)} | {n} | " + " | ".join(cells) + f" | {hit} |")
+    lines.append("")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines))
+    return out_path
+
+
 class HipTimer:
     """HIP timing events on an explicit stream, through the HIP runtime torch itself loaded,
     created with hipEventDisableSystemFence: recording them neither writes back nor
@@ -735,9 +771,17 @@ def main():
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "STATS_DIR"),
                     help="write profiles/decode_partial_and_merge.<workload>.md from rocprofv3 "
                          "output directories (no GPU needed) and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/counters.<workload>.md from rocprofv3 --pmc output "
+                         "directories (no GPU needed) and exit")
     ap.add_argument("--command", action="append", default=[],
-                    help="with --summarize: a command line to record in the summary")
+                    help="with --summarize / --summarize-counters: a command line to record")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(args.workload, args.summarize_counters,
+                                 os.path.join(ROOT, "profiles", f"counters.{args.workload}.md"),
+                                 args.command))
+        return
     if args.summarize:
         print(summarize_profile(args.workload, *args.summarize, profile_path(args.workload),
                                 args.command))

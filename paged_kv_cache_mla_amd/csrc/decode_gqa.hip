@@ -261,7 +261,8 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
 // One workgroup of W = group_parts / wave_parts waves per (sequence, KV head, group of
 // partitions); wave w takes the group's partitions [w * wave_parts, (w + 1) * wave_parts),
 // its online softmax continuing across their boundary.  Dynamic LDS (W > 1 only):
-// [W][group][D] partial outputs, then [W][group] lse values (log2 domain).
+// [W][group][row] partial outputs (row = gqa_merge_row(W, group, D), D padded), then
+// [W][group] lse values (log2 domain).
 template <int D, int BSL, int PAIRS, bool NT>
 __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kernel(DecodeArgs a) {
   constexpr int VT = D / 16;
@@ -314,12 +315,13 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
 
   // Exact LSE merge of the group's partials in LDS:
   //   M = max_w lse_w, s = sum_w 2^(lse_w - M), o = sum_w 2^(lse_w - M) o_w / s.
-  float* so = smem;                  // [G][grp][D]
-  float* sl = smem + G * grp * D;    // [G][grp]
+  const int rs = gqa_merge_row(G, grp, D);  // row stride
+  float* so = smem;                  // [G][grp][rs]
+  float* sl = smem + G * grp * rs;   // [G][grp]
   if (n < grp) {
     if (p < np) {
       const float inv = 1.f / lsum;
-      float* op = so + (wv * grp + n) * D;
+      float* op = so + (wv * grp + n) * rs;
 #pragma unroll
       for (int t = 0; t < VT; ++t)
         *reinterpret_cast<f32x4*>(op + 16 * t + 4 * g4) = acc[t] * inv;
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
       if (l != kNegInf) {  // idle waves wrote no output
         const float e = exp2f(l - mx);
         s += e;
-        o += e * so[(u * grp + h) * D + d];
+        o += e * so[(u * grp + h) * rs + d];
       }
     }
     const int64_t row = ((int64_t)b * a.hq + kvh * grp + h) * a.max_parts + k;
@@ -508,7 +510,7 @@ static hipError_t launch_mfma_d(const DecodeArgs& a, dim3 grid, size_t lds, bool
 }
 
 size_t gqa_mfma_lds_bytes(int waves, int group, int d) {
-  return waves > 1 ? (size_t)waves * group * (d + 1) * sizeof(float) : 0;
+  return waves > 1 ? (size_t)waves * group * (gqa_merge_row(waves, group, d) + 1) * sizeof(float) : 0;
 }
 
 // `stream`: non-temporal K/V loads (every block read once per step); otherwise

@@ -100,6 +100,14 @@ __device__ __forceinline__ void flag_error(int32_t* err, int32_t bit) {
 // Partition count of sequence b from the device copy of the per-sequence values, and in *ng
 // the number of partials written for it, ceil(np / group_parts).  Returns -1 (and *ng = -1)
 // if the values are inconsistent with the launch.
+// Row stride, in floats, of the partial outputs a matrix-core GQA workgroup merges in LDS:
+// padded by 4 so that the 16 rows one quarter of a wave writes at once start on different LDS
+// banks (an unpadded power-of-two stride puts them all on the same ones), unless the padding
+// would take the merge area (rows plus one lse per row) past 64 KiB.
+__host__ __device__ inline int gqa_merge_row(int waves, int group, int d) {
+  return (int64_t)waves * group * (d + 5) * 4 <= 65536 ? d + 4 : d;
+}
+
 __device__ __forceinline__ int seq_partitions(const DecodeArgs& a, int b, int* lo_tok, int* part,
                                               int* ng) {
   const int L = a.seq[b];
