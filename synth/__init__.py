@@ -5,6 +5,6 @@ attention, merge or address arithmetic, so both the oracle side and the HIP side
 consume its output without sharing any of the method's code.
 """
 
-from .workloads import Case, WORKLOADS, bf16_round_bits, make_case, mla_case
+from .workloads import Case, WORKLOADS, bf16_round_bits, make_case, gqa_case, mla_case
 
-__all__ = ["Case", "WORKLOADS", "bf16_round_bits", "make_case", "mla_case"]
+__all__ = ["Case", "WORKLOADS", "bf16_round_bits", "make_case", "gqa_case", "mla_case"]

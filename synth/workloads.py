@@ -275,6 +275,18 @@ def _mla_16k(variant):
                    1 / np.sqrt(192.0), [need], table, lens, None, [part] * len(lens), rq, rkv)
 
 
+def gqa_case(block_size, num_kv_heads, head_dim, num_q_heads, lens, part_tokens,
+             tok_begin=None, dtype: str = "bf16", seed: int = 1007) -> Case:
+    """A per-head K/V (GQA) case of any geometry with the given context lengths, partition
+    sizes and first tokens, over a pool of exactly the blocks needed, in random order."""
+    rq, rkv, rtab, _ = _streams(seed)
+    max_blocks = _nblocks(max(lens), block_size)
+    table, need = _permuted_tables(rtab, lens, block_size, max_blocks)
+    return _finish("gqa_custom", "small", seed, block_size, num_kv_heads, head_dim, head_dim,
+                   dtype, False, num_q_heads, 1 / np.sqrt(float(head_dim)), [need], table, lens,
+                   tok_begin, part_tokens, rq, rkv)
+
+
 def mla_case(lens, part_tokens, tok_begin=None, seed: int = 1006) -> Case:
     """A latent-cache (MLA) case of the 16K layer's geometry (bs 64, Dk 576, Dv 512, 16 heads)
     with the given context lengths, partition sizes and first tokens, over a pool of exactly

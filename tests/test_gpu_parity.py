@@ -106,6 +106,33 @@ def test_grouped_partials_match_oracle(name, group_parts):
     _check_partials(case, dc, group_parts=group_parts)
 
 
+GEOMETRIES = [  # block size, KV heads, head dim, q heads, partition blocks, group_parts
+    (32, 2, 128, 16, 2, 1), (32, 4, 64, 8, 3, 4), (64, 2, 64, 32, 2, 8),
+    (64, 1, 256, 4, 1, 2), (128, 2, 128, 8, 1, 4), (256, 1, 128, 16, 1, 2),
+    (256, 2, 256, 2, 1, 1), (16, 8, 64, 128, 4, 16)]
+
+
+@pytest.mark.parametrize("bs,hkv,d,hq,pblocks,group_parts", GEOMETRIES,
+                         ids=[f"bs{g[0]}-hkv{g[1]}-d{g[2]}-hq{g[3]}-g{g[5]}" for g in GEOMETRIES])
+def test_matrix_core_kernel_block_sizes_and_head_dims(bs, hkv, d, hq, pblocks, group_parts):
+    """The matrix-core GQA kernel at every block size it is built for (16 .. 256), head dims
+    64 / 128 / 256 and 1 .. 16 query heads per KV head, with ragged lengths (one token, a
+    partial last block, a start inside a block), against the oracle element by element."""
+    from synth import gqa_case
+    lens = [bs * 5 + 3, 1, bs * 11, 2 * bs - 1, bs * 3 + bs // 2]
+    begin = [0, 0, bs // 2 + 1, 0, bs]
+    case = gqa_case(bs, hkv, d, hq, lens, [bs * pblocks] * len(lens), tok_begin=begin)
+    _say(f"[geometry] bs={bs} hkv={hkv} d={d} hq={hq} P={bs * pblocks} group_parts={group_parts}")
+    dc, o, lse = _run(case, None, group_parts)
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    _say(f"[geometry] out error {err:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc, group_parts=group_parts)
+
+
 def test_long_mla_groups_cross_block_id_windows():
     """Latent-cache groups longer than the 128 stages (64-token blocks) whose block ids the
     kernel holds in registers at a time: a group of 257 stages starting mid-block (two full
