@@ -287,15 +287,15 @@ def gqa_case(block_size, num_kv_heads, head_dim, num_q_heads, lens, part_tokens,
                    tok_begin, part_tokens, rq, rkv)
 
 
-def mla_case(lens, part_tokens, tok_begin=None, seed: int = 1006) -> Case:
-    """A latent-cache (MLA) case of the 16K layer's geometry (bs 64, Dk 576, Dv 512, 16 heads)
-    with the given context lengths, partition sizes and first tokens, over a pool of exactly
-    the blocks needed, in random order."""
+def mla_case(lens, part_tokens, tok_begin=None, seed: int = 1006, num_q_heads: int = 16) -> Case:
+    """A latent-cache (MLA) case of the 16K layer's geometry (bs 64, Dk 576, Dv 512, up to 16
+    heads) with the given context lengths, partition sizes and first tokens, over a pool of
+    exactly the blocks needed, in random order."""
     rq, rkv, rtab, _ = _streams(seed)
     bs = 64
     max_blocks = _nblocks(max(lens), bs)
     table, need = _permuted_tables(rtab, lens, bs, max_blocks)
-    return _finish("mla_custom", "small", seed, bs, 1, 576, 512, "bf16", True, 16,
+    return _finish("mla_custom", "small", seed, bs, 1, 576, 512, "bf16", True, num_q_heads,
                    1 / np.sqrt(192.0), [need], table, lens, tok_begin, part_tokens, rq, rkv)
 
 

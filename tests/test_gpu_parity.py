@@ -133,6 +133,46 @@ def test_matrix_core_kernel_block_sizes_and_head_dims(bs, hkv, d, hq, pblocks, g
     _check_partials(case, dc, group_parts=group_parts)
 
 
+SMALL_BLOCKS = [  # block size, KV heads, head dim, q heads, dtype, group_parts
+    (1, 2, 64, 8, "f32", 1), (2, 1, 128, 4, "bf16", 3), (4, 2, 64, 4, "f32", 2),
+    (8, 4, 128, 16, "bf16", 4), (8, 1, 256, 16, "f32", 1), (64, 2, 64, 8, "f32", 2)]
+
+
+@pytest.mark.parametrize("bs,hkv,d,hq,dtype,group_parts", SMALL_BLOCKS,
+                         ids=[f"bs{g[0]}-d{g[2]}-{g[4]}-g{g[5]}" for g in SMALL_BLOCKS])
+def test_generic_kernel_block_sizes(bs, hkv, d, hq, dtype, group_parts):
+    """Block sizes below the matrix-core kernel's 16 tokens, and fp32 caches, go to the plain
+    VALU kernel: block sizes 1 .. 8 and 64, head dims 64 .. 256, fp32 and bf16, against the
+    oracle, partials included."""
+    from synth import gqa_case
+    lens = [37, 1, 130, 64 + 5]
+    begin = [0, 0, 3, 16]
+    pt = max(bs, 16) * 2
+    case = gqa_case(bs, hkv, d, hq, lens, [pt] * len(lens), tok_begin=begin, dtype=dtype)
+    _say(f"[generic] bs={bs} d={d} {dtype} hq={hq} hkv={hkv} group_parts={group_parts}")
+    dc, o, lse = _run(case, None, group_parts)
+    o_ref, lse_ref = oc.full_reference(case)
+    assert oc.out_error(case, o, o_ref) <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc, group_parts=group_parts)
+
+
+@pytest.mark.parametrize("hq", [1, 5, 8])
+def test_mla_fewer_heads(hq):
+    """Latent-cache decode with fewer than the 16 heads an MFMA tile holds: the unused head
+    columns are zero in the operands and never written."""
+    from synth import mla_case
+    case = mla_case([1000, 64, 333], [256] * 3, tok_begin=[0, 0, 70], num_q_heads=hq)
+    _say(f"[mla heads] hq={hq}")
+    dc, o, lse = _run(case, None, 2)
+    o_ref, lse_ref = oc.full_reference(case)
+    assert oc.out_error(case, o, o_ref) <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc, group_parts=2)
+
+
 def test_long_mla_groups_cross_block_id_windows():
     """Latent-cache groups longer than the 128 stages (64-token blocks) whose block ids the
     kernel holds in registers at a time: a group of 257 stages starting mid-block (two full
