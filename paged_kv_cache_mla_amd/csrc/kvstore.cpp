@@ -34,9 +34,12 @@ struct kvattn_kvstore {
   std::vector<kvattn_share_ctl*> ctl;
   std::vector<Seq> seq;
   bool prefill_done = false, flushed = false;
-  // device addresses of the host pool's regions when they are mapped pinned memory (queried at
-  // the first enqueued copy): copies then run as one kernel writing over the host link
+  // device addresses of the host pool's regions when they are mapped pinned memory: copies
+  // then run as one kernel writing over the host link.  Queried at the first enqueued copy
+  // and again whenever the host pool's regions have changed since (a region added, say).
   int mapped = -1;  // -1 unknown, 0 no, 1 yes
+  int mapped_regions = 0;                           // regions the query covered
+  void* mapped_host[KVATTN_MAX_REGIONS] = {};       // their host addresses
   void* host_dev_base[KVATTN_MAX_REGIONS] = {};
 };
 
@@ -126,8 +129,16 @@ kvattn_status enqueue_copies(kvattn_kvstore* s, const std::vector<int32_t>& copi
                              void* hip_stream) {
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (n == 0) return KVATTN_OK;
-  if (s->mapped < 0) {
+  bool stale = s->mapped < 0 || s->mapped_regions != s->host->n_regions;
+  for (int r = 0; r < s->host->n_regions && !stale; ++r)
+    stale = s->mapped_host[r] != s->host->base[r];
+  if (stale) {
     s->mapped = 1;
+    for (int r = 0; r < KVATTN_MAX_REGIONS; ++r) {
+      s->host_dev_base[r] = nullptr;
+      s->mapped_host[r] = r < s->host->n_regions ? s->host->base[r] : nullptr;
+    }
+    s->mapped_regions = s->host->n_regions;
     for (int r = 0; r < s->host->n_regions; ++r) {
       void* d = nullptr;
       if (hipHostGetDevicePointer(&d, s->host->base[r], 0) != hipSuccess || !d) {

@@ -257,6 +257,67 @@ def test_decode_session_with_window_eviction_and_both_views(name):
     store.close()
 
 
+def test_flush_into_a_host_region_added_after_the_first_flush():
+    """Every batch goes to the CPU share (p ~ 1).  The first flush fills the host pool's only
+    region; a second pinned region is then added to the host pool, and the next flush must copy
+    into it through the region's own device-mapped address.  The CPU view then holds exactly
+    the appended tokens, in order."""
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.api import KVStore, Pool, ShareController, append_kv
+    layout = Layout(16, 2, 64, 64, "bf16", False)
+    rng = np.random.default_rng(91)
+    B, bs, D, max_blocks = 2, 16, 32, 8
+    nb = D // bs
+    nel = block_elems(layout)
+    dev_region = torch.zeros(B * max_blocks * nel, dtype=torch.int16, device="cuda")
+    host_a = torch.zeros(B * nb * nel, dtype=torch.int16, pin_memory=True)   # one flush's room
+    host_b = torch.zeros(B * nb * nel, dtype=torch.int16, pin_memory=True)
+    args = (bs, 2, 64, 64, "bf16", False)
+    dev_pool = Pool(*args, [(dev_region.data_ptr(), B * max_blocks)], seed=3)
+    host_pool = Pool(*args, [(host_a.data_ptr(), B * nb)], seed=4)
+    ctls = [ShareController(1e-6, 1.0, 0.0, 0.0, window=4) for _ in range(B)]
+    store = KVStore(dev_pool, host_pool, B, D, max_blocks, ctls)
+    store.place_prefill()                       # admits the controllers; nothing to place
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hist = [[] for _ in range(B)]
+
+    def append_batch():
+        store.reserve([D] * B)
+        gt, gl, _, _ = store.views()
+        table = _dev(gt)
+        for b in range(B):
+            k = _random_storage(rng, (D, 2, 64), layout)
+            v = _random_storage(rng, (D, 2, 64), layout)
+            pos = torch.tensor([int(gl[b])], dtype=torch.int32, device="cuda")
+            append_kv(dev_pool, _dev(k[None]), _dev(v[None]), _lib.BF16, table[b:b + 1],
+                      max_blocks, pos, err)
+            hist[b].append((k, v))
+        store.commit([D] * B)
+
+    append_batch()
+    store.flush()
+    torch.cuda.synchronize()
+    assert host_pool.num_free == 0
+    first = host_pool.add_region(host_b.data_ptr(), B * nb)
+    _say(f"[kvstore] host region added at id {first}")
+    append_batch()
+    store.flush()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    _, gl, ct, cl = store.views()
+    regions = [host_a.numpy().view(np.uint16), host_b.numpy().view(np.uint16)]
+    for b in range(B):
+        assert cl[b] == 2 * D and gl[b] == 0
+        assert all(x >= first for x in ct[b, nb:2 * nb])     # the second batch is in the new region
+        k, v = oracle.gather_sequence(layout, regions, [B * nb, B * nb], ct[b], 0, 2 * D)
+        k_ref = np.concatenate([oracle.bf16_bits_to_f64(x[0]) for x in hist[b]])
+        v_ref = np.concatenate([oracle.bf16_bits_to_f64(x[1]) for x in hist[b]])
+        assert np.array_equal(k, k_ref) and np.array_equal(v, v_ref)
+    store.close()
+    host_pool.close()
+    dev_pool.close()
+
+
 def test_full_size_append_rebuilds_the_pool_byte_for_byte():
     """The 16 x 32K layer: every token of every sequence is read back out of the workload's
     pool, the device pool is cleared, and the tokens are appended again through the same
