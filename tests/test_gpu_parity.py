@@ -133,6 +133,29 @@ def test_matrix_core_kernel_block_sizes_and_head_dims(bs, hkv, d, hq, pblocks, g
     _check_partials(case, dc, group_parts=group_parts)
 
 
+EXTREMES = [  # lengths, tok_begin, group_parts
+    ([131072, 100001], [0, 777], 16),     # 256 and 194 partitions, groups of 16
+    ([512] * 255 + [7], None, 1),        # 256 sequences, one partition each
+]
+
+
+@pytest.mark.parametrize("lens,begin,group_parts", EXTREMES, ids=["long-128K-g16", "batch-256-g1"])
+def test_extreme_launch_shapes(lens, begin, group_parts):
+    """The Qwen3-30B-A3B GQA shape at the ends of its launch space: two 100K+ contexts in the
+    largest groups (grids of few workgroups, long on-chip merges), and 256 short sequences
+    (grids of many tiny workgroups), against the oracle."""
+    from synth import gqa_case
+    case = gqa_case(16, 4, 128, 32, lens, [512] * len(lens), tok_begin=begin, seed=1011)
+    _say(f"[extreme] B={case.batch} max L={max(lens)} group_parts={group_parts}")
+    dc, o, lse = _run(case, None, group_parts)
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    _say(f"[extreme] out error {err:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+
+
 SMALL_BLOCKS = [  # block size, KV heads, head dim, q heads, dtype, group_parts
     (1, 2, 64, 8, "f32", 1), (2, 1, 128, 4, "bf16", 3), (4, 2, 64, 4, "f32", 2),
     (8, 4, 128, 16, "bf16", 4), (8, 1, 256, 16, "f32", 1), (64, 2, 64, 8, "f32", 2)]
