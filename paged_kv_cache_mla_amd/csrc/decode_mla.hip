@@ -84,19 +84,6 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
   const int nst = ((hi + kMlaBs - 1) >> 6) - st_lo;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
 
-  // Q^T operand (B of the QK product): head n, dims 8*(g4+4j) .. +7.
-  if (wv == 0) {
-    const bool hv = n < a.hq;
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (hv ? n : 0)) * kMlaDk);
-#pragma unroll
-    for (int j = 0; j < kMlaKs; ++j) {
-      uint4 v = qrow[g4 + 4 * j];
-      if (!hv) v = make_uint4(0u, 0u, 0u, 0u);
-      qs[j * 64 + lane] = v;
-    }
-  }
-  __syncthreads();
 
   // The wave's latent rows of the team's next stage.  They start zeroed, so a stage never
   // loaded is finite; its scores are masked anyway.
@@ -156,15 +143,16 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
       vbuf[(j >> 2) * 1024 + wslot[j & 3]] = __builtin_bit_cast(uint4, kb[j]);
     const int tbase = (st_lo + w0 + s) << 6;
     const int tok = tbase + 16 * ww + n;
-    const bool zero_tok = !(vld & (tok >= lo) & (tok < hi));
+    const bool cur = vld;
+    const bool zero_tok = !(cur & (tok >= lo) & (tok < hi));
+    if (s + kTeams < wn) issue(s + kTeams);  // the registers are free once the rows are in LDS
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tl = 16 * ww + 4 * g4 + i;
       const int t = tbase + tl;
-      const bool ok = vld & (t >= lo) & (t < hi);
+      const bool ok = cur & (t >= lo) & (t < hi);
       sxt[tl][n] = ok ? sacc[i] * a.scale_log2 : kNegInfM;
     }
-    if (s + kTeams < wn) issue(s + kTeams);
     if (zero_tok) {
 #pragma unroll
       for (int j = 0; j < kMlaVChunks / 4; ++j)
@@ -235,11 +223,35 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
   // Step t of a window: team 0 runs phases 1-3 of its stage t/2 (t even) or phase 4 (t odd);
   // team 1 does the same one step later.  Every wave passes every barrier (the step count is
   // uniform over the workgroup).
-  for (; w0 < nst; w0 += kWin) {
+  // The first window's block ids and loads are issued before the barrier that publishes Q^T,
+  // so their latency overlaps the Q load.
+  auto open_window = [&]() {
     wn = min(kWin, nst - w0);
     pid0 = trow[st_lo + w0 + min(lane, wn - 1)];
     pid1 = trow[st_lo + w0 + min(64 + lane, wn - 1)];
     if (team < wn) issue(team);
+  };
+  // Q^T operand (B of the QK product): head n, dims 8*(g4+4j) .. +7.  The first wave of team 1
+  // loads it (team 1 scores its first stage one step after team 0, so the later start of its
+  // own loads costs nothing), into registers before its loads of the latent rows.
+  constexpr int kQWave = 4;
+  const bool hv = n < a.hq;
+  uint4 qv[kMlaKs];
+  if (wv == kQWave) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (hv ? n : 0)) * kMlaDk);
+#pragma unroll
+    for (int j = 0; j < kMlaKs; ++j) qv[j] = qrow[g4 + 4 * j];
+  }
+  open_window();
+  if (wv == kQWave) {
+#pragma unroll
+    for (int j = 0; j < kMlaKs; ++j) qs[j * 64 + lane] = hv ? qv[j] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+
+  for (; w0 < nst; w0 += kWin) {
+    if (w0 > 0) open_window();
     const int n0 = (wn + 1) >> 1, n1 = wn >> 1;  // stages of teams 0 and 1 in the window
     const int steps = max(2 * n0, 2 * n1 + 1);
     for (int t = 0; t < steps; ++t) {
