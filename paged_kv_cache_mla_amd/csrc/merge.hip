@@ -7,7 +7,7 @@
 //     M = max_p lse_p,  T = sum_p exp(lse_p - M),  lse = M + ln T,
 //     o = sum_p exp(lse_p - M) o_p / T        (= sum_p exp(lse_p - lse) o_p).
 //
-// Two kernels.  The workgroup kernel: one 256-thread workgroup per (sequence, head); thread
+// Three kernels.  The workgroup kernel: one 256-thread workgroup per (sequence, head); thread
 // (g, c) of a [groups x dv/4] arrangement owns 16-byte column c of partitions g, g + groups,
 // ...  The merge is bound by the latency of a few dependent steps, not by bandwidth, so the
 // order is: issue the loads of
@@ -16,6 +16,8 @@
 // to LDS while summing them, and only then consume the partial columns already in registers.
 // Partitions beyond kR * groups (long sequences, wide heads) follow in further chunks of
 // kR * groups.  Every sum runs in a fixed order, so the result is bitwise reproducible.
+// The two wave kernels below take one wave per (sequence, head) with every partial in
+// registers: narrow heads (up to 128 values), and wide heads (256 or 512) with few partials.
 
 #include <cstdlib>
 #include <cstring>
@@ -195,26 +197,98 @@ __global__ __launch_bounds__(kThreads) void merge_lse_wave_kernel(MergeArgs a) {
   if (a.lse_out && lane == 0) a.lse_out[row] = big + logf(tot);
 }
 
-// The wave kernel takes heads of 4 .. 128 values (a power-of-two number of 16-byte columns)
-// with every partition slot in its registers; anything else goes to the workgroup kernel.
-// KVATTN_MERGE_KERNEL=block|wave overrides the choice (tuning and tests).
-bool merge_uses_wave(const MergeArgs& a) {
-  const int cols = a.dv >> 2;
-  const bool fits = (a.dv & 3) == 0 && cols >= 1 && cols <= 32 && (64 % cols) == 0 &&
-                    a.max_parts <= (64 / cols) * kWaveParts && a.max_parts <= 64;
+// One wave per (sequence, head) for wide heads of 256 * C values (MLA's 512: C = 2) with at
+// most kWideParts partials: lane l owns 16-byte columns l, l + 64, ..., l + 64 (C - 1) of
+// every partition, and lane p holds lse_p.  The order of operations is the narrow wave
+// kernel's: all loads before the partition count is used, wave reductions for the maximum and
+// the weight sum, weights fetched from the lanes holding them, fixed summation order.
+static constexpr int kWideParts = 16;
+
+template <int C>
+__global__ __launch_bounds__(kThreads) void merge_lse_wide_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.batch * a.hq) return;  // uniform per wave
+  const int b = (int)(row / a.hq);
+  constexpr int cols = 64 * C;
+  const float* lrow = a.lse_part + row * a.max_parts;
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.o_part + row * a.max_parts * a.dv);
+  const bool ext = a.o_ext != nullptr;
+  f32x4 ov[kWideParts][C];
+#pragma unroll
+  for (int k = 0; k < kWideParts; ++k)
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      ov[k][u] = k < a.max_parts ? orow[(int64_t)k * cols + lane + 64 * u] : f32x4{0.f, 0.f, 0.f, 0.f};
+  const float l0 = lane < a.max_parts ? lrow[lane] : kNegInfG;
+  const float lx = ext ? a.lse_ext[row] : kNegInfG;
+  const int np_raw = a.nparts[b];
+  const int np = np_raw < 0 ? 0 : (np_raw > a.max_parts ? a.max_parts : np_raw);
+  const float big = fmaxf(wave_max(lane < np ? l0 : kNegInfG), lx);
+  f32x4* orow_out = reinterpret_cast<f32x4*>(a.o_out + row * a.dv);
+  if (big == kNegInfG) {
+#pragma unroll
+    for (int u = 0; u < C; ++u) orow_out[lane + 64 * u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.lse_out && lane == 0) a.lse_out[row] = kNegInfG;
+    return;
+  }
+  const float wl = lane < np ? expf(l0 - big) : 0.f;
+  const float wx = ext ? expf(lx - big) : 0.f;
+  const float tot = wave_sum(wl) + wx;
+  f32x4 acc[C];
+#pragma unroll
+  for (int u = 0; u < C; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kWideParts; ++k) {
+    const float w = __shfl(wl, k);
+    if (k < np) {  // a select: stale slots never enter the sum
+#pragma unroll
+      for (int u = 0; u < C; ++u) acc[u] += ov[k][u] * w;
+    }
+  }
+  const float inv = 1.f / tot;
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    f32x4 o = acc[u];
+    if (ext) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[lane + 64 * u] * wx;
+    orow_out[lane + 64 * u] = o * inv;
+  }
+  if (a.lse_out && lane == 0) a.lse_out[row] = big + logf(tot);
+}
+
+enum MergeKind { kMergeBlock, kMergeWave, kMergeWide };
+
+// The narrow wave kernel takes heads of 4 .. 128 values (a power-of-two number of 16-byte
+// columns) with every partition slot in its registers, the wide one heads of 256 or 512
+// values with at most 16 partials; anything else goes to the workgroup kernel.
+// KVATTN_MERGE_KERNEL=block overrides the choice (tuning and tests).
+static MergeKind merge_kind(const MergeArgs& a) {
   const char* e = std::getenv("KVATTN_MERGE_KERNEL");
-  if (e && std::strcmp(e, "block") == 0) return false;
-  return fits;
+  if (e && std::strcmp(e, "block") == 0) return kMergeBlock;
+  const int cols = a.dv >> 2;
+  if ((a.dv & 3) == 0 && cols >= 1 && cols <= 32 && (64 % cols) == 0 &&
+      a.max_parts <= (64 / cols) * kWaveParts && a.max_parts <= 64)
+    return kMergeWave;
+  if ((a.dv == 256 || a.dv == 512) && a.max_parts <= kWideParts) return kMergeWide;
+  return kMergeBlock;
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.batch * a.hq;
-  if (merge_uses_wave(a)) {
-    const int64_t per = kThreads / 64;
-    hipLaunchKernelGGL(merge_lse_wave_kernel, dim3((unsigned)((rows + per - 1) / per)),
-                       dim3(kThreads), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
+  const int64_t per = kThreads / 64;
+  const dim3 waves((unsigned)((rows + per - 1) / per));
+  switch (merge_kind(a)) {
+    case kMergeWave:
+      hipLaunchKernelGGL(merge_lse_wave_kernel, waves, dim3(kThreads), 0, st, a);
+      break;
+    case kMergeWide:
+      if (a.dv == 256)
+        hipLaunchKernelGGL(merge_lse_wide_kernel<1>, waves, dim3(kThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL(merge_lse_wide_kernel<2>, waves, dim3(kThreads), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }

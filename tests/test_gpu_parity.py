@@ -214,6 +214,27 @@ def test_long_mla_groups_cross_block_id_windows():
     _check_partials(case, dc, group_parts=2)
 
 
+@pytest.mark.parametrize("part,group_parts", [(640, 1), (192, 2), (128, 3)])
+def test_mla_team_split_over_stage_counts(part, group_parts):
+    """The latent-cache kernel gives a group's even 64-token stages to one team of waves and
+    the odd ones to the other, and merges the two teams at the end.  Groups of 1 to 10 stages
+    (so the second team has nothing, as many stages, or one fewer), starting at, just after
+    and just before block boundaries, against the oracle and partial by partial."""
+    from synth import mla_case
+    lens = [1, 67, 191, 256, 300, 400, 448, 512, 542, 640]     # 1 .. 10 stages
+    begin = [0, 3, 63, 10, 20, 100, 0, 0, 30, 0]
+    case = mla_case(lens, [part] * len(lens), tok_begin=begin)
+    _say(f"[mla teams] L={lens} begin={begin} P={part} group_parts={group_parts}")
+    dc, o, lse = _run(case, None, group_parts)
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    _say(f"[mla teams] out error {err:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc, group_parts=group_parts)
+
+
 def _poison_unused_slots(case):
     """A copy of `case` whose pool holds NaN bit patterns in every token slot that no
     sequence's range [tok_begin, L) uses: the tails of last blocks, the slots before
@@ -488,13 +509,14 @@ def test_split_step_with_native_host_share(variant, kw, seqs, group_parts):
 
 # ---------------------------------------------------------------- the two merge kernels
 @pytest.mark.parametrize("dv,max_parts", [(64, 1), (64, 32), (128, 4), (128, 16), (128, 32),
-                                          (256, 8), (512, 40)])
+                                          (256, 8), (256, 16), (256, 17), (512, 1), (512, 8),
+                                          (512, 16), (512, 40)])
 @pytest.mark.parametrize("ext", [False, True])
 def test_merge_kernels_match_oracle_and_each_other(dv, max_parts, ext):
     """kvattn_merge_lse on random partials (counts from 0 to max_parts, -inf entries) against
-    the oracle's float64 merge; narrow heads with few partials take the wave kernel, the others
-    the workgroup kernel, and forcing the workgroup kernel gives the same result within
-    rounding."""
+    the oracle's float64 merge; narrow heads, and heads of 256 or 512 values with at most 16
+    partials, take a wave kernel, the others the workgroup kernel, and forcing the workgroup
+    kernel gives the same result within rounding."""
     import os
     from paged_kv_cache_mla_amd.api import merge_lse
     rng = np.random.default_rng(dv * 100 + max_parts + ext)
