@@ -65,8 +65,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
   const int n = lane & 15;
   const int g4 = lane >> 4;
 
-  // one workgroup per (sequence, group of group_parts partitions); the group's partitions
-  // are walked in order, the online softmax continuing across their boundaries
+  // one workgroup per (sequence, group of group_parts partitions); each team walks its
+  // blocks of the group in order, its online softmax continuing across partition boundaries
   const int k = blockIdx.x % a.grid_ng;
   const int b = blockIdx.x / a.grid_ng;
   int beg, P, ng;
@@ -83,7 +83,6 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
   const int st_lo = lo >> 6;
   const int nst = ((hi + kMlaBs - 1) >> 6) - st_lo;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-
 
   // The wave's latent rows of the team's next stage.  They start zeroed, so a stage never
   // loaded is finite; its scores are masked anyway.
