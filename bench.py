@@ -12,7 +12,9 @@ goes to stderr.
 
 Fields beyond the contract: `roofline` (dominant kernel vs 8 TB/s, timed with HIP events on
 the launch stream), `cpu_baseline` (the float64 oracle on a bounded sample, on this host's
-cores), `copy_GBps` (a plain device-to-device copy on this GPU, for scale).
+cores), `copy_GBps` (a plain device-to-device copy on this GPU, for scale), `gather_ceiling`
+(the decode kernel's own loads with no arithmetic, timed after the steps: the access pattern's
+bandwidth ceiling on this GPU, and the decode kernel's fraction of it).
 """
 
 import argparse
@@ -855,6 +857,23 @@ def main():
     t_part = [timer.elapsed_ms(a, b) for a, b in evs]
     ms_step = wall * 1e3 / args.steps
 
+    # The access pattern's own ceiling, outside the timed region: the gather probe issues the
+    # decode kernel's loads (same grid, waves, table lookups and cache hints) with no arithmetic.
+    gather = None
+    try:
+        xsum = torch.zeros(case.batch * case.num_kv_heads, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            dc.step.probe(xsum)
+        pevs = [(timer.event(), timer.event()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            timer.record(pevs[i][0], sp)
+            dc.step.probe(xsum)
+            timer.record(pevs[i][1], sp)
+        torch.cuda.synchronize()
+        gather = float(np.mean([timer.elapsed_ms(a, b) for a, b in pevs]))
+    except _lib.KvattnError as e:  # layouts the probe does not serve (fp32, other block sizes)
+        log(f"[bench] no gather probe for this layout: {e}")
+
     kv_bytes = case.device_tokens() * case.kv_bytes_per_token()
     step = dc.step
     n_parts_total = int(dc.step.nparts.sum().item())
@@ -918,6 +937,13 @@ def main():
             "avg_launch_us": round(avg_part_ms * 1e3, 2),
         },
     }
+    if gather is not None:
+        out["gather_ceiling"] = {
+            "kernel": "gather probe: the decode kernel's loads, no arithmetic",
+            "avg_launch_us": round(gather * 1e3, 2),
+            "kv_GBps": round(kv_bytes / (gather * 1e-3) / 1e9, 1),
+            "decode_frac_of_probe": round(gather / avg_part_ms, 4),
+        }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(case)

@@ -302,6 +302,29 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
                                     void* hip_stream);
 
 /*
+ * Gather probe: the loads of kvattn_decode_partial's kernel for the same arguments -- the same
+ * grid, waves, block-table lookups, load widths, cache hints and order -- with no arithmetic.
+ * It measures the access pattern's own bandwidth ceiling on this device, which bounds what
+ * the decode kernel can reach. It also returns a checksum of exactly what the kernel reads:
+ *     xsum_dev[b][h] ^= XOR over the 16-bit elements of K(h, t, :) and V(h, t, :) of
+ *                       every token t in [tok_begin_b, ctx_len_b)
+ * (MLA: h = 0 and the 576-wide latent rows C(t, :), each element once).  The XOR is
+ * order-free, so the checksum is exact and reproducible, and it pins the block-table
+ * resolution bit for bit.
+ *   Arguments as for kvattn_decode_partial (no q, scale or partials).
+ *   xsum_dev  device uint32 [batch][num_kv_heads] (MLA: [batch]); the probe XORs into it, so
+ *             the caller zeroes it first; only the low 16 bits are used.
+ * Errors: those of kvattn_decode_partial's validation; E_INVAL for xsum_dev NULL;
+ * E_UNSUPPORTED unless the cache is bf16 GQA with block size 16 (matrix-core kernel), or MLA.
+ */
+kvattn_status kvattn_gather_probe(const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,
+                                  const int32_t* table_dev, int32_t max_blocks,
+                                  const int32_t* ctx_lens, const int32_t* tok_begin,
+                                  const int32_t* part_tokens, const int32_t* seq_dev,
+                                  int32_t group_parts, uint32_t* xsum_dev, int32_t* err_dev,
+                                  void* hip_stream);
+
+/*
  * Exact LSE merge of each (sequence, head)'s partials ([InplaceKVCache] §4.2, §5.1, §5.2:
  * the partial outputs and their normalisers are folded on the GPU, one join per step):
  *     M = max_p lse_p,  lse = M + ln sum_p exp(lse_p - M),  o = sum_p exp(lse_p - lse) o_p

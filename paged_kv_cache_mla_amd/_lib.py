@@ -82,6 +82,8 @@ _SIGNATURES = {
     "kvattn_decode_partial": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32,
                                      _PI32, _PI32, _PI32, _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_merge_lse": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "kvattn_gather_probe": (_I32, [_P, _I32, _I32, _P, _I32, _PI32, _PI32, _PI32, _P, _I32, _P,
+                                   _P, _P]),
     "kvattn_resolve_offsets": (_I32, [_P, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
     "kvattn_select_blocks": (_I32, [_P, _I32, _P, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _P]),
     "kvattn_append_kv": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P]),

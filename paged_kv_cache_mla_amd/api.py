@@ -158,6 +158,19 @@ def decode_partial(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, 
     check(st, "decode_partial")
 
 
+def gather_probe(pool, num_q_heads, table_dev, max_blocks, ctx_lens, tok_begin, part_tokens,
+                 seq_dev, xsum, err=None, stream=None, group_parts=1):
+    """kvattn_gather_probe: the decode kernel's loads without arithmetic; XORs a checksum of
+    the read K/V elements into `xsum` (int32 [batch][num_kv_heads], zeroed by the caller)."""
+    lib = _lib.load()
+    ctx, beg, part = _host_i32(ctx_lens), _host_i32(tok_begin), _host_i32(part_tokens)
+    st = lib.kvattn_gather_probe(pool.handle, int(ctx.shape[0]), int(num_q_heads),
+                                 _dptr(table_dev), int(max_blocks), _i32p(ctx), _i32p(beg),
+                                 _i32p(part), _dptr(seq_dev), int(group_parts), _dptr(xsum),
+                                 _dptr(err), _stream(stream))
+    check(st, "gather_probe")
+
+
 def merge_lse(o_part, lse_part, nparts, batch, num_q_heads, max_parts, dv, o_out,
               o_ext=None, lse_ext=None, lse_out=None, stream=None):
     lib = _lib.load()
@@ -500,6 +513,11 @@ class DecodeStep:
         decode_partial(self.pool, q, q_dtype, self.hq, scale, self.table_dev, self.max_blocks,
                        self.ctx, self.beg, self.part, self.seq_dev, self.max_parts, self.o_part,
                        self.lse_part, self.nparts, self.err, stream, self.group_parts)
+
+    def probe(self, xsum, stream=None):
+        """The gather probe over this step's ranges, in its launch configuration."""
+        gather_probe(self.pool, self.hq, self.table_dev, self.max_blocks, self.ctx, self.beg,
+                     self.part, self.seq_dev, xsum, self.err, stream, self.group_parts)
 
     def merge(self, o_ext=None, lse_ext=None, stream=None):
         merge_lse(self.o_part, self.lse_part, self.nparts, self.batch, self.hq, self.max_parts,

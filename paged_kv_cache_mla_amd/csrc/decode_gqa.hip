@@ -62,10 +62,12 @@ constexpr int mfma_max_group() { return D <= 64 ? 16 : 8; }
 // side by side, and the B operand the two tiles' score-layout weights side by side.  The
 // weights enter as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)), two MFMAs per
 // output tile, so P V is accurate to ~2^-16 relative rather than bf16's 2^-9.
-template <int D, int BSL, int PAIRS, bool NT>
+// PROBE: the same loads in the same order, with no arithmetic: the in-range 16-bit elements
+// of K and V are XOR-ed into `xs` (the gather's own bandwidth ceiling, and a checksum).
+template <int D, int BSL, int PAIRS, bool NT, bool PROBE = false>
 __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, int kvh, int lo,
                                                    int hi, int lane, f32x4 (&acc)[D / 16],
-                                                   float& m, float& lsum) {
+                                                   float& m, float& lsum, uint32_t& xs) {
   constexpr int BS = 1 << BSL;
   constexpr int KS = D / 32;       // k-steps of the QK product (32 dims each)
   constexpr int VT = D / 16;       // 16-dim output tiles of the PV product
@@ -85,7 +87,7 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
 
   // B operand of the QK product: Q^T, lane (n, g4) holds head n, dims 8*(g4+4j) .. +7.
   bf16x8 qop[KS];
-  {
+  if constexpr (!PROBE) {
     const bool hv = n < a.group;
     const uint4* qrow = reinterpret_cast<const uint4*>(
         static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + kvh * a.group + (hv ? n : 0)) * D);
@@ -196,6 +198,29 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
   // One ring round: RING tiles starting at `it`, each pair's refill issued RING - 2 tiles
   // ahead.  Tiles past the end of the range (the tail of the last round) are computed fully
   // masked: zero weight, max unchanged.
+  // PROBE: XOR of the tile's in-range elements (lane: token n's K chunks; V slices of tokens
+  // 4*g4 .. 4*g4+3, two per 32-bit word)
+  auto probe_tile = [&](int slot, int rel) -> uint32_t {
+    if (rel >= ntiles) return 0u;  // uniform
+    const int t0 = (t_lo + rel) << 4;
+    bad |= !vld[slot];
+    const bool okk = vld[slot] & (t0 + n >= lo) & (t0 + n < hi);
+    uint32_t x = 0u;
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      x ^= okk ? (kb[slot][j][0] ^ kb[slot][j][1] ^ kb[slot][j][2] ^ kb[slot][j][3]) : 0u;
+    uint32_t mk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g4 + i;
+      mk[i] = (vld[slot] & (t >= lo) & (t < hi)) ? 0xffffu : 0u;
+    }
+    const uint32_t m0 = mk[0] | (mk[1] << 16), m1 = mk[2] | (mk[3] << 16);
+#pragma unroll
+    for (int t = 0; t < VT; ++t) x ^= (vb[slot][t][0] & m0) ^ (vb[slot][t][1] & m1);
+    return x;
+  };
+
   auto round = [&](int it, bool guard) {
 #pragma unroll
     for (int ps = 0; ps < PAIRS; ++ps) {
@@ -205,6 +230,10 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
       const int fs = (sa + RING - 2) % RING;
       issue(fs, ra + RING - 2, guard);
       issue(fs + 1, ra + RING - 1, guard);
+      if constexpr (PROBE) {
+        xs ^= probe_tile(sa, ra) ^ probe_tile(sb, rb);
+        continue;
+      }
       float sva[4], svb[4];
       const uint32_t oka = scores(sa, ra, sva);
       const uint32_t okb = scores(sb, rb, svb);
@@ -294,8 +323,9 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
   float m = kNegInf, lsum = 0.f;
   if (p < np) {  // uniform over the wave: waves past the sequence's last partition idle
     const int lo = beg + p * P;
+    uint32_t unused = 0u;
     gqa_partition_mfma<D, BSL, PAIRS, NT>(a, b, kvh, lo, (int)min((int64_t)L, (int64_t)lo + S * P),
-                                      lane, acc, m, lsum);
+                                      lane, acc, m, lsum, unused);
   }
   lsum = rows_sum(lsum);
   const int grp = a.group;
@@ -347,6 +377,39 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
     a.o_part[row * D + d] = o / s;
     if (d == 0) a.lse_part[row] = (mx + log2f(s)) * kLn2;
   }
+}
+
+// Gather probe of the matrix-core kernel's access pattern: the same grid, waves and loads,
+// no arithmetic.  Each wave folds the XOR of its in-range 16-bit K/V elements into one 16-bit
+// value and XORs it into xsum[b][kvh] (zeroed by the caller).
+template <int D, int BSL, int PAIRS, bool NT>
+__global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_probe_kernel(DecodeArgs a,
+                                                                            uint32_t* xsum) {
+  const int S = a.wave_parts;
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  int w = blockIdx.x;
+  const int k = w % a.grid_ng;
+  w /= a.grid_ng;
+  const int kvh = w % a.hkv;
+  const int b = w / a.hkv;
+  int beg, P, ng;
+  const int np = seq_partitions(a, b, &beg, &P, &ng);
+  if (k == 0 && kvh == 0 && threadIdx.x == 0 && np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+  if (k >= ng) return;
+  const int p = k * a.group_parts + wv * S;
+  if (p >= np) return;  // uniform over the wave; no barrier follows
+  const int L = a.seq[b];
+  const int lo = beg + p * P;
+  f32x4 acc[D / 16];
+  float m = 0.f, lsum = 0.f;
+  uint32_t xs = 0u;
+  gqa_partition_mfma<D, BSL, PAIRS, NT, true>(a, b, kvh, lo,
+                                                (int)min((int64_t)L, (int64_t)lo + S * P), lane,
+                                                acc, m, lsum, xs);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) xs ^= __shfl_xor(xs, o);
+  if (lane == 0) atomicXor(xsum + (int64_t)b * a.hkv + kvh, (xs ^ (xs >> 16)) & 0xffffu);
 }
 
 template <typename T>
@@ -523,6 +586,28 @@ hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, bool stream, dim3 grid, h
     case 256: return launch_mfma_d<256>(a, grid, lds, stream, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The probe is built for the block size of 16 (the benchmark layers); other geometries
+// return hipErrorInvalidValue.  `stream` selects the decode kernel's cache hint.
+template <bool NT>
+static hipError_t launch_gqa_probe_nt(const DecodeArgs& a, int d, dim3 grid, uint32_t* xsum,
+                                      hipStream_t st) {
+  const dim3 block(64 * (a.group_parts / a.wave_parts));
+  switch (d) {
+    case 64: hipLaunchKernelGGL((gqa_probe_kernel<64, 4, 2, NT>), grid, block, 0, st, a, xsum); break;
+    case 128: hipLaunchKernelGGL((gqa_probe_kernel<128, 4, 2, NT>), grid, block, 0, st, a, xsum); break;
+    case 256: hipLaunchKernelGGL((gqa_probe_kernel<256, 4, 1, NT>), grid, block, 0, st, a, xsum); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gqa_probe(const DecodeArgs& a, int d, bool stream, dim3 grid, uint32_t* xsum,
+                            hipStream_t st) {
+  if (a.bs_shift != 4) return hipErrorInvalidValue;
+  return stream ? launch_gqa_probe_nt<true>(a, d, grid, xsum, st)
+                : launch_gqa_probe_nt<false>(a, d, grid, xsum, st);
 }
 
 template <typename T>

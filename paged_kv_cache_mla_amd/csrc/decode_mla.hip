@@ -53,7 +53,11 @@ static constexpr int kWin = 128;                // stages whose block ids a wind
 
 __device__ __forceinline__ int lat_slot(int c, int t) { return c * kMlaBs + (t ^ (c & 15)); }
 
-__global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
+// PROBE: the same grid, waves and loads with no arithmetic, LDS traffic or barriers: each wave
+// XORs the in-range 16-bit latent elements it loads and folds them into xsum[b] (the gather's
+// own bandwidth ceiling, and a checksum).
+template <bool PROBE>
+__global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a, uint32_t* xsum) {
   __shared__ uint4 vlat[kTeams][kMlaVChunks * kMlaBs];  // value part of a team's stage: 2 x 64 KiB
   __shared__ float sx[kTeams][kMlaBs][16];              // scores of a team's stage, [token][head]
   __shared__ uint4 qs[kMlaKs * 64];                     // Q^T operand, [k-step][lane]
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
   int beg, P, ng;
   const int np = seq_partitions(a, b, &beg, &P, &ng);
   if (k == 0 && tid == 0) {
-    a.nparts[b] = ng < 0 ? 0 : ng;
+    if (!PROBE) a.nparts[b] = ng < 0 ? 0 : ng;
     if (np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
   }
   if (k >= ng) return;
@@ -126,8 +130,17 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
 
   // Phases 1-3 of window-relative stage s: scores from the registers, value part and scores
   // to the team's tile, then the registers are refilled with the team's next stage.
+  uint32_t xs = 0u;
   auto score_stage = [&](int s) {
     bad |= !vld;
+    if constexpr (PROBE) {
+      const int tok = ((st_lo + w0 + s) << 6) + 16 * ww + n;
+      const bool ok = vld & (tok >= lo) & (tok < hi);
+#pragma unroll
+      for (int j = 0; j < kMlaKs; ++j) xs ^= ok ? (kb[j][0] ^ kb[j][1] ^ kb[j][2] ^ kb[j][3]) : 0u;
+      if (s + kTeams < wn) issue(s + kTeams);
+      return;
+    }
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kMlaKs; ++j)
@@ -161,6 +174,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
 
   // Phase 4: softmax update over the stage's 64 tokens and the PV product, from the team's tile.
   auto attend_stage = [&]() {
+    if constexpr (PROBE) return;
     // lane (n, g4) takes head n's scores of tokens 32*kk + 8*g4 + i (i < 8), the k-slots of
     // the PV product below
     float sv[2][8];
@@ -236,18 +250,18 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
   constexpr int kQWave = 4;
   const bool hv = n < a.hq;
   uint4 qv[kMlaKs];
-  if (wv == kQWave) {
+  if (wv == kQWave && !PROBE) {
     const uint4* qrow = reinterpret_cast<const uint4*>(
         static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + (hv ? n : 0)) * kMlaDk);
 #pragma unroll
     for (int j = 0; j < kMlaKs; ++j) qv[j] = qrow[g4 + 4 * j];
   }
   open_window();
-  if (wv == kQWave) {
+  if (wv == kQWave && !PROBE) {
 #pragma unroll
     for (int j = 0; j < kMlaKs; ++j) qs[j * 64 + lane] = hv ? qv[j] : make_uint4(0u, 0u, 0u, 0u);
   }
-  __syncthreads();
+  if (!PROBE) __syncthreads();
 
   for (; w0 < nst; w0 += kWin) {
     if (w0 > 0) open_window();
@@ -262,10 +276,16 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
         else
           attend_stage();
       }
-      __syncthreads();
+      if (!PROBE) __syncthreads();
     }
   }
   if (bad && lane == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+  if constexpr (PROBE) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) xs ^= __shfl_xor(xs, o);
+    if (lane == 0) atomicXor(xsum + b, (xs ^ (xs >> 16)) & 0xffffu);
+    return;
+  }
 
   // Exact merge of the two teams' states (log2 domain): team 1 hands its running max, sum and
   // unnormalised output through LDS (the value tiles are free after the last barrier); wave
@@ -315,7 +335,12 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_mla(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(512), 0, st, a);
+  hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(512), 0, st, a, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_probe(const DecodeArgs& a, dim3 grid, uint32_t* xsum, hipStream_t st) {
+  hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(512), 0, st, a, xsum);
   return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@ int gqa_mfma_max_group(int d);
 size_t gqa_mfma_lds_bytes(int group_parts, int group, int d);
 hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, hipStream_t st);
 hipError_t launch_mla(const DecodeArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_gqa_probe(const DecodeArgs& a, int d, bool stream, dim3 grid, uint32_t* xsum,
+                            hipStream_t st);
+hipError_t launch_mla_probe(const DecodeArgs& a, dim3 grid, uint32_t* xsum, hipStream_t st);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_append(const RegionTable& rt, const kvattn_layout& L, const void* k_new,
@@ -48,31 +51,24 @@ static kvattn_status hip_status(hipError_t e, const char* where) {
   return set_error(KVATTN_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
-}  // namespace kvattn
+enum Kind { K_MFMA, K_GENERIC, K_MLA };
 
-using namespace kvattn;
-
-extern "C" {
-
-kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int32_t q_dtype,
-                                    int32_t batch, int32_t num_q_heads, float scale,
-                                    const int32_t* table_dev, int32_t max_blocks,
-                                    const int32_t* ctx_lens, const int32_t* tok_begin,
-                                    const int32_t* part_tokens, const int32_t* seq_dev,
-                                    int32_t max_parts, int32_t group_parts, float* o_part,
-                                    float* lse_part, int32_t* nparts_dev, int32_t* err_dev,
-                                    void* hip_stream) {
-  clear_error();
-  if (!pool || !q || !table_dev || !ctx_lens || !part_tokens || !seq_dev || !o_part ||
-      !lse_part || !nparts_dev)
+// Validation, kernel choice and kernel arguments shared by kvattn_decode_partial and
+// kvattn_gather_probe (which checks its own pointers and passes no q or partials).
+static kvattn_status decode_prepare(const kvattn_pool* pool, int32_t q_dtype, int32_t batch,
+                                    int32_t num_q_heads, float scale, const int32_t* table_dev,
+                                    int32_t max_blocks, const int32_t* ctx_lens,
+                                    const int32_t* tok_begin, const int32_t* part_tokens,
+                                    const int32_t* seq_dev, int32_t max_parts,
+                                    int32_t group_parts, DecodeArgs* out, Kind* kind_out,
+                                    dim3* grid_out) {
+  if (!pool || !table_dev || !ctx_lens || !part_tokens || !seq_dev)
     return set_error(KVATTN_E_INVAL, "decode_partial: null argument");
   if (batch < 1 || num_q_heads < 1 || max_blocks < 1 || max_parts < 1)
     return set_error(KVATTN_E_INVAL, "decode_partial: batch, heads, max_blocks and max_parts must be >= 1");
   if (group_parts < 1 || group_parts > KVATTN_MAX_GROUP_PARTS)
     return set_error(KVATTN_E_INVAL, "decode_partial: group_parts must be in [1, KVATTN_MAX_GROUP_PARTS]");
   if (!std::isfinite(scale)) return set_error(KVATTN_E_INVAL, "decode_partial: scale must be finite");
-  if (!aligned16(q) || !aligned16(o_part))
-    return set_error(KVATTN_E_INVAL, "decode_partial: q and o_part must be 16-byte aligned");
   const kvattn_layout& L = pool->layout;
   if (q_dtype != L.kv_dtype)
     return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: q_dtype must equal the cache dtype");
@@ -83,7 +79,7 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
   const int bs = L.block_size;
 
   // kernel choice
-  enum { K_MFMA, K_GENERIC, K_MLA } kind;
+  Kind kind;
   int wave_parts = 1;
   if (L.latent) {
     if (L.kv_dtype != KVATTN_BF16 || L.head_dim_k != 576 || L.head_dim_v != 512 || bs != 64 ||
@@ -147,15 +143,11 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
   const int64_t items = (int64_t)batch * (kind == K_MLA ? 1 : hkv) * grid_ng;
   if (items > INT32_MAX) return set_error(KVATTN_E_INVAL, "decode_partial: launch too large");
 
-  DecodeArgs a{};
+  DecodeArgs& a = *out;
+  a = DecodeArgs{};
   a.rt = region_table(pool);
-  a.q = q;
   a.table = table_dev;
   a.seq = seq_dev;
-  a.o_part = o_part;
-  a.lse_part = lse_part;
-  a.nparts = nparts_dev;
-  a.err = err_dev;
   a.batch = batch;
   a.hq = num_q_heads;
   a.hkv = hkv;
@@ -169,9 +161,45 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
   a.bs_shift = log2_exact(bs);
   a.scale = scale;
   a.scale_log2 = scale * 1.44269504088896340736f;
+  *kind_out = kind;
+  *grid_out = dim3((unsigned)items);
+  return KVATTN_OK;
+}
 
+}  // namespace kvattn
+
+using namespace kvattn;
+
+extern "C" {
+
+kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int32_t q_dtype,
+                                    int32_t batch, int32_t num_q_heads, float scale,
+                                    const int32_t* table_dev, int32_t max_blocks,
+                                    const int32_t* ctx_lens, const int32_t* tok_begin,
+                                    const int32_t* part_tokens, const int32_t* seq_dev,
+                                    int32_t max_parts, int32_t group_parts, float* o_part,
+                                    float* lse_part, int32_t* nparts_dev, int32_t* err_dev,
+                                    void* hip_stream) {
+  clear_error();
+  if (!pool || !q || !table_dev || !ctx_lens || !part_tokens || !seq_dev || !o_part ||
+      !lse_part || !nparts_dev)
+    return set_error(KVATTN_E_INVAL, "decode_partial: null argument");
+  if (!aligned16(q) || !aligned16(o_part))
+    return set_error(KVATTN_E_INVAL, "decode_partial: q and o_part must be 16-byte aligned");
+  DecodeArgs a;
+  Kind kind;
+  dim3 grid;
+  const kvattn_status v = decode_prepare(pool, q_dtype, batch, num_q_heads, scale, table_dev,
+                                         max_blocks, ctx_lens, tok_begin, part_tokens, seq_dev,
+                                         max_parts, group_parts, &a, &kind, &grid);
+  if (v != KVATTN_OK) return v;
+  a.q = q;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.nparts = nparts_dev;
+  a.err = err_dev;
+  const kvattn_layout& L = pool->layout;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const dim3 grid((unsigned)items);
   hipError_t e;
   switch (kind) {
     case K_MLA: e = launch_mla(a, grid, st); break;
@@ -179,6 +207,33 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
     default: e = launch_gqa_generic(a, L.head_dim_k, L.kv_dtype == KVATTN_F32, grid, st); break;
   }
   return hip_status(e, "decode_partial launch");
+}
+
+kvattn_status kvattn_gather_probe(const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,
+                                  const int32_t* table_dev, int32_t max_blocks,
+                                  const int32_t* ctx_lens, const int32_t* tok_begin,
+                                  const int32_t* part_tokens, const int32_t* seq_dev,
+                                  int32_t group_parts, uint32_t* xsum_dev, int32_t* err_dev,
+                                  void* hip_stream) {
+  clear_error();
+  if (!pool || !xsum_dev) return set_error(KVATTN_E_INVAL, "gather_probe: null argument");
+  DecodeArgs a;
+  Kind kind;
+  dim3 grid;
+  const kvattn_status v = decode_prepare(pool, pool->layout.kv_dtype, batch, num_q_heads, 1.f,
+                                         table_dev, max_blocks, ctx_lens, tok_begin, part_tokens,
+                                         seq_dev, INT32_MAX, group_parts, &a, &kind, &grid);
+  if (v != KVATTN_OK) return v;
+  a.err = err_dev;
+  const kvattn_layout& L = pool->layout;
+  if (kind == K_GENERIC || (kind == K_MFMA && L.block_size != 16))
+    return set_error(KVATTN_E_UNSUPPORTED,
+                     "gather_probe: needs the matrix-core GQA kernel with block size 16, or MLA");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = kind == K_MLA ? launch_mla_probe(a, grid, xsum_dev, st)
+                                     : launch_gqa_probe(a, L.head_dim_k, pool->shared_blocks == 0,
+                                                        grid, xsum_dev, st);
+  return hip_status(e, "gather_probe launch");
 }
 
 kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,

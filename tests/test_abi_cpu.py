@@ -236,6 +236,27 @@ def test_decode_partial_validation_without_gpu(lib):
     assert "block" in lib.kvattn_last_error().decode()
 
 
+def test_gather_probe_validation_without_gpu(lib):
+    """kvattn_gather_probe validates like kvattn_decode_partial, and serves only the
+    matrix-core GQA layout with 16-token blocks and the MLA layout."""
+    vp = ctypes.c_void_p
+    p32 = lambda v: np.ascontiguousarray(np.asarray(v, np.int32)).ctypes.data_as(  # noqa: E731
+        ctypes.POINTER(ctypes.c_int32))
+
+    def call(pool, xsum=FAKE, part=(32, 32), ctx=(64, 50), hq=8, g=1):
+        return lib.kvattn_gather_probe(pool.handle, 2, hq, vp(FAKE), 4, p32(ctx), None,
+                                       p32(part), vp(FAKE), g, None if xsum is None else vp(xsum),
+                                       None, None)
+    ok = _pool(8, 0, bs=16, hkv=2, d=128)
+    assert call(ok, xsum=None) == _lib.E_INVAL
+    assert call(ok, part=(32, 24)) == _lib.E_INVAL                          # not a block multiple
+    assert call(ok, hq=7) == _lib.E_INVAL
+    assert call(ok, g=0) == _lib.E_INVAL
+    assert call(_pool(8, 0, bs=16, hkv=2, d=128, dtype="f32")) == _lib.E_UNSUPPORTED
+    assert call(_pool(8, 0, bs=32, hkv=2, d=128), ctx=(64, 50)) == _lib.E_UNSUPPORTED
+    assert "block size 16" in lib.kvattn_last_error().decode()
+
+
 def test_merge_validation_without_gpu(lib):
     vp = ctypes.c_void_p
     ok = dict(o=vp(FAKE), l=vp(FAKE), n=vp(FAKE), b=2, h=4, mp=3, dv=128, ox=None, lx=None,
