@@ -55,26 +55,31 @@ enum Kind { K_MFMA, K_GENERIC, K_MLA };
 
 // Validation, kernel choice and kernel arguments shared by kvattn_decode_partial and
 // kvattn_gather_probe (which checks its own pointers and passes no q or partials).
-static kvattn_status decode_prepare(const kvattn_pool* pool, int32_t q_dtype, int32_t batch,
-                                    int32_t num_q_heads, float scale, const int32_t* table_dev,
-                                    int32_t max_blocks, const int32_t* ctx_lens,
-                                    const int32_t* tok_begin, const int32_t* part_tokens,
-                                    const int32_t* seq_dev, int32_t max_parts,
-                                    int32_t group_parts, DecodeArgs* out, Kind* kind_out,
-                                    dim3* grid_out) {
+static kvattn_status decode_prepare(const char* what, const kvattn_pool* pool, int32_t q_dtype,
+                                    int32_t batch, int32_t num_q_heads, float scale,
+                                    const int32_t* table_dev, int32_t max_blocks,
+                                    const int32_t* ctx_lens, const int32_t* tok_begin,
+                                    const int32_t* part_tokens, const int32_t* seq_dev,
+                                    int32_t max_parts, int32_t group_parts, DecodeArgs* out,
+                                    Kind* kind_out, dim3* grid_out) {
   if (!pool || !table_dev || !ctx_lens || !part_tokens || !seq_dev)
-    return set_error(KVATTN_E_INVAL, "decode_partial: null argument");
+    return set_error(KVATTN_E_INVAL, std::string(what) + ": null argument");
   if (batch < 1 || num_q_heads < 1 || max_blocks < 1 || max_parts < 1)
-    return set_error(KVATTN_E_INVAL, "decode_partial: batch, heads, max_blocks and max_parts must be >= 1");
+    return set_error(KVATTN_E_INVAL,
+                     std::string(what) + ": batch, heads, max_blocks and max_parts must be >= 1");
   if (group_parts < 1 || group_parts > KVATTN_MAX_GROUP_PARTS)
-    return set_error(KVATTN_E_INVAL, "decode_partial: group_parts must be in [1, KVATTN_MAX_GROUP_PARTS]");
-  if (!std::isfinite(scale)) return set_error(KVATTN_E_INVAL, "decode_partial: scale must be finite");
+    return set_error(KVATTN_E_INVAL,
+                     std::string(what) + ": group_parts must be in [1, KVATTN_MAX_GROUP_PARTS]");
+  if (!std::isfinite(scale)) return set_error(KVATTN_E_INVAL,
+                                              std::string(what) + ": scale must be finite");
   const kvattn_layout& L = pool->layout;
   if (q_dtype != L.kv_dtype)
-    return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: q_dtype must equal the cache dtype");
+    return set_error(KVATTN_E_UNSUPPORTED,
+                     std::string(what) + ": q_dtype must equal the cache dtype");
   const int hkv = L.num_kv_heads;
   if (num_q_heads % hkv != 0)
-    return set_error(KVATTN_E_INVAL, "decode_partial: num_q_heads must be a multiple of num_kv_heads");
+    return set_error(KVATTN_E_INVAL,
+                     std::string(what) + ": num_q_heads must be a multiple of num_kv_heads");
   const int group = num_q_heads / hkv;
   const int bs = L.block_size;
 
@@ -85,14 +90,16 @@ static kvattn_status decode_prepare(const kvattn_pool* pool, int32_t q_dtype, in
     if (L.kv_dtype != KVATTN_BF16 || L.head_dim_k != 576 || L.head_dim_v != 512 || bs != 64 ||
         num_q_heads > 16)
       return set_error(KVATTN_E_UNSUPPORTED,
-                       "decode_partial: latent caches need bf16, Dk 576, Dv 512, block 64, <= 16 heads");
+                       std::string(what) + ": latent caches need bf16, Dk 576, Dv 512, block 64, <= 16 heads");
     kind = K_MLA;
   } else {
     const int d = L.head_dim_k;
     if (L.head_dim_v != d || (d != 64 && d != 128 && d != 256))
-      return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: GQA needs Dk == Dv in {64, 128, 256}");
+      return set_error(KVATTN_E_UNSUPPORTED,
+                       std::string(what) + ": GQA needs Dk == Dv in {64, 128, 256}");
     if (group > 16)
-      return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: at most 16 query heads per KV head");
+      return set_error(KVATTN_E_UNSUPPORTED,
+                       std::string(what) + ": at most 16 query heads per KV head");
     kind = (L.kv_dtype == KVATTN_BF16 && bs >= 16 && !force_generic()) ? K_MFMA : K_GENERIC;
     // Partitions per wave of the matrix-core kernel: two when the group splits evenly, so
     // that a long batch needs half the waves (at its register use a CU holds 8 waves of
@@ -109,12 +116,12 @@ static kvattn_status decode_prepare(const kvattn_pool* pool, int32_t q_dtype, in
       // waves of a group merge their partials in LDS
       const int waves = group_parts / wave_parts;
       if (waves > gqa_mfma_max_group(d))
-        return set_error(KVATTN_E_UNSUPPORTED, "decode_partial: group_parts above " +
+        return set_error(KVATTN_E_UNSUPPORTED, std::string(what) + ": group_parts above " +
                                                    std::to_string(gqa_mfma_max_group(d)) +
                                                    " for head dim " + std::to_string(d));
       if (gqa_mfma_lds_bytes(waves, group, d) > 65536)
         return set_error(KVATTN_E_UNSUPPORTED,
-                         "decode_partial: group_parts x heads per KV head x (head dim + 1) x 4 "
+                         std::string(what) + ": group_parts x heads per KV head x (head dim + 1) x 4 "
                          "bytes exceeds 64 KiB");
     }
   }
@@ -126,22 +133,23 @@ static kvattn_status decode_prepare(const kvattn_pool* pool, int32_t q_dtype, in
     const int beg = tok_begin ? tok_begin[b] : 0;
     const int P = part_tokens[b];
     if (beg < 0 || beg > len || (int64_t)len > (int64_t)max_blocks * bs)
-      return set_error(KVATTN_E_INVAL, "decode_partial: sequence " + std::to_string(b) +
+      return set_error(KVATTN_E_INVAL, std::string(what) + ": sequence " + std::to_string(b) +
                                            " needs 0 <= tok_begin <= ctx_len <= max_blocks * block_size");
     if (P <= 0 || P % bs != 0)
-      return set_error(KVATTN_E_INVAL, "decode_partial: part_tokens must be a positive multiple of block_size");
+      return set_error(KVATTN_E_INVAL,
+                       std::string(what) + ": part_tokens must be a positive multiple of block_size");
     const int np = kvattn_partition_count(len, beg, P);
     const int ng = (np + group_parts - 1) / group_parts;
     if (ng > max_parts)
-      return set_error(KVATTN_E_INVAL, "decode_partial: sequence " + std::to_string(b) +
+      return set_error(KVATTN_E_INVAL, std::string(what) + ": sequence " + std::to_string(b) +
                                            " writes more partials than max_parts");
     if (ng > max_ng) max_ng = ng;
   }
   if (max_ng > 0 && pool->total_blocks == 0)
-    return set_error(KVATTN_E_INVAL, "decode_partial: the pool holds no blocks");
+    return set_error(KVATTN_E_INVAL, std::string(what) + ": the pool holds no blocks");
   const int grid_ng = max_ng > 0 ? max_ng : 1;
   const int64_t items = (int64_t)batch * (kind == K_MLA ? 1 : hkv) * grid_ng;
-  if (items > INT32_MAX) return set_error(KVATTN_E_INVAL, "decode_partial: launch too large");
+  if (items > INT32_MAX) return set_error(KVATTN_E_INVAL, std::string(what) + ": launch too large");
 
   DecodeArgs& a = *out;
   a = DecodeArgs{};
@@ -189,9 +197,10 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
   DecodeArgs a;
   Kind kind;
   dim3 grid;
-  const kvattn_status v = decode_prepare(pool, q_dtype, batch, num_q_heads, scale, table_dev,
-                                         max_blocks, ctx_lens, tok_begin, part_tokens, seq_dev,
-                                         max_parts, group_parts, &a, &kind, &grid);
+  const kvattn_status v =
+      decode_prepare("decode_partial", pool, q_dtype, batch, num_q_heads, scale, table_dev,
+                     max_blocks, ctx_lens, tok_begin, part_tokens, seq_dev, max_parts,
+                     group_parts, &a, &kind, &grid);
   if (v != KVATTN_OK) return v;
   a.q = q;
   a.o_part = o_part;
@@ -220,9 +229,10 @@ kvattn_status kvattn_gather_probe(const kvattn_pool* pool, int32_t batch, int32_
   DecodeArgs a;
   Kind kind;
   dim3 grid;
-  const kvattn_status v = decode_prepare(pool, pool->layout.kv_dtype, batch, num_q_heads, 1.f,
-                                         table_dev, max_blocks, ctx_lens, tok_begin, part_tokens,
-                                         seq_dev, INT32_MAX, group_parts, &a, &kind, &grid);
+  const kvattn_status v =
+      decode_prepare("gather_probe", pool, pool->layout.kv_dtype, batch, num_q_heads, 1.f,
+                     table_dev, max_blocks, ctx_lens, tok_begin, part_tokens, seq_dev,
+                     INT32_MAX, group_parts, &a, &kind, &grid);
   if (v != KVATTN_OK) return v;
   a.err = err_dev;
   const kvattn_layout& L = pool->layout;
