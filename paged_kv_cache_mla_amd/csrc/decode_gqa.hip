@@ -413,6 +413,15 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_probe_kernel(Dec
 }
 
 template <typename T>
+__device__ __forceinline__ float load_elem_g(gchar* p) {
+  if constexpr (sizeof(T) == 4) {
+    return __uint_as_float(*reinterpret_cast<__attribute__((address_space(1))) const uint32_t*>(p));
+  } else {
+    return bf16_to_f32(*reinterpret_cast<__attribute__((address_space(1))) const uint16_t*>(p));
+  }
+}
+
+template <typename T>
 __device__ __forceinline__ float load_elem(const char* p) {
   if constexpr (sizeof(T) == 4) {
     return *reinterpret_cast<const float*>(p);
@@ -424,11 +433,18 @@ __device__ __forceinline__ float load_elem(const char* p) {
 // Plain VALU version: one token per lane for the scores, lanes over dims for P V.  One wave
 // per (sequence, KV head, group of partitions) walks the group's tokens in order; the online
 // softmax simply continues across the partition boundaries inside the group.
-template <typename T, int D>
+static constexpr int kCB = 8;  // K chunks per lane in flight (scores)
+static constexpr int kVB = 8;  // tokens' V loads in flight (P V)
+
+// GP: the query heads per KV head rounded up to a power of two, a compile-time bound (the
+// head loops then carry no per-head branches, which keeps the code small enough for the
+// instruction cache); heads G .. GP-1 get zero queries, are computed and never written.
+template <typename T, int D, int GP>
 __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   constexpr int R = D / 64;                // dims per lane in the output
   constexpr int X = 16 / (int)sizeof(T);   // elements per 16-byte chunk
-  __shared__ float qs[16][D];
+  static_assert((D / X) % kCB == 0, "K chunks per token must be a multiple of kCB");
+  __shared__ float qs[GP][D];
   const int lane = threadIdx.x;
 
   int w = blockIdx.x;
@@ -450,18 +466,18 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   const int hi = (int)min((int64_t)L, lo + span);
   const int G = a.group;
 
-  for (int h = 0; h < G; ++h) {
-    const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.hq + kvh * G + h) * D;
+  for (int h = 0; h < GP; ++h) {
+    const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.hq + kvh * G + min(h, G - 1)) * D;
     for (int d = lane; d < D; d += 64)
-      qs[h][d] = load_elem<T>(reinterpret_cast<const char*>(qrow + d));
+      qs[h][d] = h < G ? load_elem<T>(reinterpret_cast<const char*>(qrow + d)) : 0.f;
   }
   __syncthreads();
 
   const int64_t kpart_bytes = (int64_t)a.hkv * a.bs * D * (int64_t)sizeof(T);
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-  float m[16], l[16], acc[16][R], pr[16];
+  float m[GP], l[GP], acc[GP][R], pr[GP];
 #pragma unroll
-  for (int h = 0; h < 16; ++h) {
+  for (int h = 0; h < GP; ++h) {
     m[h] = kNegInf;
     l[h] = 0.f;
 #pragma unroll
@@ -475,25 +491,42 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
     const int32_t pid = in ? trow[t >> a.bs_shift] : 0;
     const bool ok = in && valid_block(a.rt, pid);
     bad |= in && !ok;
-    const char* base = block_ptr(a.rt, pid);
+    // global-address-space pointers: global loads count against the vector-memory counter
+    // only, so the shuffles and LDS reads below do not wait for them (flat loads would)
+    const int32_t vpid = ok ? pid : 0;  // id 0 exists: the launcher checked the pool
+    gchar* base = block_addr(a.rt, vpid);
     const int tt = t & (a.bs - 1);
-    float s[16];
+    float s[GP];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) s[h] = 0.f;
+    for (int h = 0; h < GP; ++h) s[h] = 0.f;
     if (ok) {
-      for (int c = 0; c < D / X; ++c) {
-        const char* kp = base + ((((int64_t)kvh * (D / X) + c) << a.bs_shift) + tt) * 16;
-        for (int u = 0; u < X; ++u) {
-          const float kv = load_elem<T>(kp + u * (int)sizeof(T));
+      // the token's K chunks, kCB 16-byte loads in flight at a time
+      for (int c0 = 0; c0 < D / X; c0 += kCB) {
+        uint4 kc[kCB];
 #pragma unroll
-          for (int h = 0; h < 16; ++h)
-            if (h < G) s[h] += qs[h][c * X + u] * kv;
+        for (int u = 0; u < kCB; ++u) {
+          const u32x4 v = *reinterpret_cast<gu32x4*>(
+              base + ((((int64_t)kvh * (D / X) + c0 + u) << a.bs_shift) + tt) * 16);
+          kc[u] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+#pragma unroll
+        for (int u = 0; u < kCB; ++u) {
+          const uint32_t w[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+#pragma unroll
+          for (int e = 0; e < X; ++e) {
+            const float kv = sizeof(T) == 4 ? __uint_as_float(w[e])
+                                            : bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+            for (int h = 0; h < GP; ++h) s[h] += qs[h][(c0 + u) * X + e] * kv;
+          }
+          // keeps the next chunk's q reads from LDS below this point: hoisting all of them
+          // (a fully unrolled 64-dim bf16 token) would exhaust the registers
+          asm volatile("" ::: "memory");
         }
       }
     }
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      if (h >= G) continue;
+    for (int h = 0; h < GP; ++h) {
       const float sc = ok ? s[h] * a.scale : kNegInf;
       const float mnew = fmaxf(m[h], wave_max(sc));
       const float mref = mnew == kNegInf ? 0.f : mnew;
@@ -504,30 +537,45 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[h][r] *= alpha;
     }
+    // P V over the chunk's tokens, kVB tokens' V loads in flight at a time.  Tokens outside
+    // the range or in an invalid block are left out by a select (their slots may hold NaN bit
+    // patterns, which a zero weight would not cancel); loads past the chunk's end repeat its
+    // last token and are left out the same way.
     const int cnt = min(64, hi - c0);
-    for (int j = 0; j < cnt; ++j) {
-      const bool okj = __shfl(ok ? 1 : 0, j) != 0;
-      if (!okj) continue;
-      const int32_t pidj = __shfl(pid, j);
-      const int ttj = __shfl(tt, j);
-      const char* vbase = block_ptr(a.rt, pidj) + kpart_bytes;
-      float vv[R];
+    for (int j0 = 0; j0 < cnt; j0 += kVB) {
+      // every shuffle first, then every load
+      int32_t pidj[kVB], ttj[kVB];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        vv[r] = load_elem<T>(vbase + ((((int64_t)kvh * D + lane + 64 * r) << a.bs_shift) + ttj) * (int64_t)sizeof(T));
+      for (int u = 0; u < kVB; ++u) {
+        const int j = min(j0 + u, cnt - 1);
+        pidj[u] = __shfl(vpid, j);
+        ttj[u] = __shfl(tt, j);
+      }
+      float vv[kVB][R];
 #pragma unroll
-      for (int h = 0; h < 16; ++h) {
-        if (h >= G) continue;
-        const float pj = __shfl(pr[h], j);
+      for (int u = 0; u < kVB; ++u) {
+        gchar* vbase = block_addr(a.rt, pidj[u]) + kpart_bytes;
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[h][r] += pj * vv[r];
+        for (int r = 0; r < R; ++r)
+          vv[u][r] = load_elem_g<T>(vbase + ((((int64_t)kvh * D + lane + 64 * r) << a.bs_shift) + ttj[u]) * (int64_t)sizeof(T));
+      }
+#pragma unroll
+      for (int u = 0; u < kVB; ++u) {
+        const int j = min(j0 + u, 63);
+        const bool use = (j0 + u < cnt) && __shfl(ok ? 1 : 0, j) != 0;  // uniform
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          const float pj = __shfl(pr[h], j);
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[h][r] = use ? acc[h][r] + pj * vv[u][r] : acc[h][r];
+        }
       }
     }
   }
   if (__any(bad) && lane == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 
 #pragma unroll
-  for (int h = 0; h < 16; ++h) {
+  for (int h = 0; h < GP; ++h) {
     if (h >= G) continue;
     const int64_t row = ((int64_t)b * a.hq + kvh * G + h) * a.max_parts + k;
     float* op = a.o_part + row * D;
@@ -610,15 +658,24 @@ hipError_t launch_gqa_probe(const DecodeArgs& a, int d, bool stream, dim3 grid, 
                 : launch_gqa_probe_nt<false>(a, d, grid, xsum, st);
 }
 
-template <typename T>
-static hipError_t launch_generic_t(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {
+template <typename T, int GP>
+static hipError_t launch_generic_tg(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {
   switch (d) {
-    case 64: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 64>), grid, dim3(64), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 128>), grid, dim3(64), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 256>), grid, dim3(64), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 64, GP>), grid, dim3(64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 128, GP>), grid, dim3(64), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 256, GP>), grid, dim3(64), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_generic_t(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {
+  if (a.group <= 1) return launch_generic_tg<T, 1>(a, d, grid, st);
+  if (a.group <= 2) return launch_generic_tg<T, 2>(a, d, grid, st);
+  if (a.group <= 4) return launch_generic_tg<T, 4>(a, d, grid, st);
+  if (a.group <= 8) return launch_generic_tg<T, 8>(a, d, grid, st);
+  return launch_generic_tg<T, 16>(a, d, grid, st);
 }
 
 hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, hipStream_t st) {
