@@ -433,8 +433,8 @@ __device__ __forceinline__ float load_elem(const char* p) {
 // Plain VALU version: one token per lane for the scores, lanes over dims for P V.  One wave
 // per (sequence, KV head, group of partitions) walks the group's tokens in order; the online
 // softmax simply continues across the partition boundaries inside the group.
-static constexpr int kCB = 8;  // K chunks per lane in flight (scores)
-static constexpr int kVB = 8;  // tokens' V loads in flight (P V)
+static constexpr int kCB = 16;  // at most this many K chunks per lane in flight (scores)
+static constexpr int kVB = 32;  // V loads per lane in flight (P V, dims 64 and up)
 
 // GP: the query heads per KV head rounded up to a power of two, a compile-time bound (the
 // head loops then carry no per-head branches, which keeps the code small enough for the
@@ -443,8 +443,15 @@ template <typename T, int D, int GP>
 __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   constexpr int R = D / 64;                // dims per lane in the output
   constexpr int X = 16 / (int)sizeof(T);   // elements per 16-byte chunk
-  static_assert((D / X) % kCB == 0, "K chunks per token must be a multiple of kCB");
+  constexpr int CB = (D / X) < kCB ? (D / X) : kCB;  // K chunks in flight
+  static_assert((D / X) % CB == 0, "K chunks per token must be a multiple of CB");
   __shared__ float qs[GP][D];
+  // P V operands, staged through LDS: the chunk's weights [head][token], and 64 dims of its V
+  // values transposed, [dim][token] (row padded by one word: conflict-free both ways).  V is
+  // stored token-fastest, so loads with lane = token coalesce (16 consecutive slots of a
+  // block), where lane = dim would touch a cache line per lane and token.
+  __shared__ float sp[GP][64];
+  __shared__ float sv[64][65];
   const int lane = threadIdx.x;
 
   int w = blockIdx.x;
@@ -492,32 +499,40 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
     const bool ok = in && valid_block(a.rt, pid);
     bad |= in && !ok;
     // global-address-space pointers: global loads count against the vector-memory counter
-    // only, so the shuffles and LDS reads below do not wait for them (flat loads would)
+    // only, so the shuffles and LDS accesses below do not wait for them (flat loads would)
     const int32_t vpid = ok ? pid : 0;  // id 0 exists: the launcher checked the pool
     gchar* base = block_addr(a.rt, vpid);
     const int tt = t & (a.bs - 1);
+    // the token's V values of output dims 0..63, loaded now, with the K chunks, since they
+    // depend only on the block id (zeros for a token that takes no part)
+    gchar* vtok = base + kpart_bytes + (int64_t)tt * (int64_t)sizeof(T);
+    float v0[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+      v0[j] = ok ? load_elem_g<T>(vtok + ((((int64_t)kvh * D + j) << a.bs_shift) * (int64_t)sizeof(T)))
+                 : 0.f;
     float s[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) s[h] = 0.f;
     if (ok) {
-      // the token's K chunks, kCB 16-byte loads in flight at a time
-      for (int c0 = 0; c0 < D / X; c0 += kCB) {
-        uint4 kc[kCB];
+      // the token's K chunks, CB 16-byte loads in flight at a time
+      for (int k0 = 0; k0 < D / X; k0 += CB) {
+        uint4 kc[CB];
 #pragma unroll
-        for (int u = 0; u < kCB; ++u) {
+        for (int u = 0; u < CB; ++u) {
           const u32x4 v = *reinterpret_cast<gu32x4*>(
-              base + ((((int64_t)kvh * (D / X) + c0 + u) << a.bs_shift) + tt) * 16);
+              base + ((((int64_t)kvh * (D / X) + k0 + u) << a.bs_shift) + tt) * 16);
           kc[u] = make_uint4(v[0], v[1], v[2], v[3]);
         }
 #pragma unroll
-        for (int u = 0; u < kCB; ++u) {
+        for (int u = 0; u < CB; ++u) {
           const uint32_t w[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
 #pragma unroll
           for (int e = 0; e < X; ++e) {
             const float kv = sizeof(T) == 4 ? __uint_as_float(w[e])
                                             : bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
 #pragma unroll
-            for (int h = 0; h < GP; ++h) s[h] += qs[h][(c0 + u) * X + e] * kv;
+            for (int h = 0; h < GP; ++h) s[h] += qs[h][(k0 + u) * X + e] * kv;
           }
           // keeps the next chunk's q reads from LDS below this point: hoisting all of them
           // (a fully unrolled 64-dim bf16 token) would exhaust the registers
@@ -537,38 +552,36 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[h][r] *= alpha;
     }
-    // P V over the chunk's tokens, kVB tokens' V loads in flight at a time.  Tokens outside
-    // the range or in an invalid block are left out by a select (their slots may hold NaN bit
-    // patterns, which a zero weight would not cancel); loads past the chunk's end repeat its
-    // last token and are left out the same way.
+    // P V over the chunk's tokens, 64 output dims at a time.  A token outside the range or in
+    // an invalid block stages zeros (its slots may hold NaN bit patterns, which a zero weight
+    // would not cancel) and has weight zero.
     const int cnt = min(64, hi - c0);
-    for (int j0 = 0; j0 < cnt; j0 += kVB) {
-      // every shuffle first, then every load
-      int32_t pidj[kVB], ttj[kVB];
+    __syncthreads();  // the previous chunk's reads of sp are done
 #pragma unroll
-      for (int u = 0; u < kVB; ++u) {
-        const int j = min(j0 + u, cnt - 1);
-        pidj[u] = __shfl(vpid, j);
-        ttj[u] = __shfl(tt, j);
-      }
-      float vv[kVB][R];
+    for (int h = 0; h < GP; ++h) sp[h][lane] = pr[h];
 #pragma unroll
-      for (int u = 0; u < kVB; ++u) {
-        gchar* vbase = block_addr(a.rt, pidj[u]) + kpart_bytes;
+    for (int r = 0; r < R; ++r) {
+      __syncthreads();  // the previous slice's reads of sv are done
+      if (r == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          vv[u][r] = load_elem_g<T>(vbase + ((((int64_t)kvh * D + lane + 64 * r) << a.bs_shift) + ttj[u]) * (int64_t)sizeof(T));
-      }
+        for (int j = 0; j < 64; ++j) sv[j][lane] = v0[j];
+      } else {
+        for (int j0 = 0; j0 < 64; j0 += kVB) {
+          float v[kVB];
 #pragma unroll
-      for (int u = 0; u < kVB; ++u) {
-        const int j = min(j0 + u, 63);
-        const bool use = (j0 + u < cnt) && __shfl(ok ? 1 : 0, j) != 0;  // uniform
+          for (int u = 0; u < kVB; ++u)
+            v[u] = ok ? load_elem_g<T>(vtok + ((((int64_t)kvh * D + 64 * r + j0 + u) << a.bs_shift) *
+                                               (int64_t)sizeof(T)))
+                      : 0.f;
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-          const float pj = __shfl(pr[h], j);
-#pragma unroll
-          for (int r = 0; r < R; ++r) acc[h][r] = use ? acc[h][r] + pj * vv[u][r] : acc[h][r];
+          for (int u = 0; u < kVB; ++u) sv[j0 + u][lane] = v[u];
         }
+      }
+      __syncthreads();
+      for (int j = 0; j < cnt; ++j) {
+        const float vj = sv[lane][j];
+#pragma unroll
+        for (int h = 0; h < GP; ++h) acc[h][r] += sp[h][j] * vj;
       }
     }
   }

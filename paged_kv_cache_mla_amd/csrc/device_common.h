@@ -176,16 +176,33 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
+// Wave-wide max / sum on the VALU (no LDS round trips), for a wave with every lane active.
+// Within each row of 16 lanes, DPP moves pair lane l with l^1 and l^2 (quad_perm), then with
+// its mirror in the half row (l^7: the other quad, whose lanes agree by then) and in the row
+// (l^15: the other half); the rows are then combined by rows_max / rows_sum.  Every lane
+// combines the same two values at every step, so all lanes end with the same bits.
+__device__ __forceinline__ float dpp_move(float v, int ctrl_sel) {
+  const int x = __float_as_int(v);
+  int y;
+  switch (ctrl_sel) {  // the control must be a constant
+    case 0: y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return __int_as_float(y);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  for (int c = 0; c < 4; ++c) v = fmaxf(v, dpp_move(v, c));
+  return rows_max(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  for (int c = 0; c < 4; ++c) v = v + dpp_move(v, c);
+  return rows_sum(v);
 }
 
 }  // namespace kvattn
