@@ -472,6 +472,10 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   const int lo = (int)(beg + k * span);
   const int hi = (int)min((int64_t)L, lo + span);
   const int G = a.group;
+  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  // block ids are read one chunk ahead (the first chunk's before q), so that a chunk's K / V
+  // loads need not wait for a table read of their own
+  int32_t pid_next = lo + lane < hi ? trow[(lo + lane) >> a.bs_shift] : 0;
 
   for (int h = 0; h < GP; ++h) {
     const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.hq + kvh * G + min(h, G - 1)) * D;
@@ -481,7 +485,6 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int64_t kpart_bytes = (int64_t)a.hkv * a.bs * D * (int64_t)sizeof(T);
-  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
   float m[GP], l[GP], acc[GP][R], pr[GP];
 #pragma unroll
   for (int h = 0; h < GP; ++h) {
@@ -495,7 +498,9 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   for (int c0 = lo; c0 < hi; c0 += 64) {
     const int t = c0 + lane;
     const bool in = t < hi;
-    const int32_t pid = in ? trow[t >> a.bs_shift] : 0;
+    const int32_t pid = pid_next;
+    const int tn = t + 64;
+    pid_next = tn < hi ? trow[tn >> a.bs_shift] : 0;
     const bool ok = in && valid_block(a.rt, pid);
     bad |= in && !ok;
     // global-address-space pointers: global loads count against the vector-memory counter
