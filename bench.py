@@ -40,6 +40,17 @@ DESCR = {
 # Partitions merged on chip into each written partial, per workload (the launch configuration
 # the full-size parity tests use too): fewer partial writes next to the K/V read stream.
 GROUP_PARTS = {"gqa_32k": 16, "split_128k": 8, "prefix_shared": 2, "mla_16k": 4, "tiny_fp32": 1}
+# The split layer's device share shrinks with the host fraction r (1024-token partitions: 96,
+# 64 and 32 per sequence at r = 0.25, 0.5, 0.75), and with it the grid: measured best
+# group_parts per r (at r = 0.75, group_parts 8 would leave 128 workgroups for 256 CUs).
+SPLIT_GROUP_PARTS = {0.25: 4, 0.5: 8, 0.75: 1}
+
+
+def default_group_parts(workload, r=0.5):
+    """Partitions merged on chip per written partial in the launch configuration timed here."""
+    if workload == "split_128k" and r in SPLIT_GROUP_PARTS:
+        return SPLIT_GROUP_PARTS[r]
+    return GROUP_PARTS[workload]
 
 KERNEL_SOURCES = {
     "mla_16k": ["decode_mla.hip", "device_common.h"],
@@ -823,7 +834,7 @@ def main():
     log(f"[bench] generating {args.workload} (full)")
     kw = {"r": args.r} if args.workload == "split_128k" else {}
     case = make_case(args.workload, "full" if args.workload != "tiny_fp32" else "small", **kw)
-    group_parts = args.group_parts or GROUP_PARTS[args.workload]
+    group_parts = args.group_parts or default_group_parts(args.workload, args.r)
     log(f"[bench] uploading (group_parts {group_parts})")
     dc = DeviceCase(case, group_parts=group_parts)
     o_ext = lse_ext = None

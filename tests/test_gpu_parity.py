@@ -432,8 +432,8 @@ FULL = [("gqa_32k", {}, [0, 7, 15]), ("mla_16k", {}, [0, 31]),
 @pytest.mark.parametrize("name,kw,seqs", FULL, ids=[f"{n}-{k.get('r', '')}" for n, k, _ in FULL])
 def test_full_size_sampled_sequences(name, kw, seqs):
     """Full-size workloads in the launch configuration bench.py times (its group_parts)."""
-    from bench import GROUP_PARTS
-    group_parts = GROUP_PARTS[name]
+    from bench import default_group_parts
+    group_parts = default_group_parts(name, kw.get("r", 0.5))
     _say(f"[full] generating {name} {kw} group_parts={group_parts}")
     case = make_case(name, "full", **kw)
     ext = oc.external_partial(case, seqs) if case.ext_regions is not None else None
