@@ -62,15 +62,40 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace runs collapsed (string and character
+    literals kept as they are), so that editing a comment does not void stored readings."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # a literal: copy through its closing quote
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash(workload):
-    """Hash of the sources the workload's dominant kernel is built from plus the device
-    compile flags: stored counter readings apply only while this hash is unchanged."""
+    """Hash of the code (comments and whitespace aside) of the sources the workload's dominant
+    kernel is built from, plus the device compile flags: stored counter readings apply only
+    while this hash is unchanged."""
     from paged_kv_cache_mla_amd.build import ARCH, COMMON, DEVICE
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_mla_amd", "csrc")
     for f in KERNEL_SOURCES.get(workload, DEFAULT_KERNEL_SOURCES):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     flags = [f for f in COMMON + DEVICE if not f.startswith("-I")]  # include paths vary by host
     h.update(" ".join([ARCH] + flags).encode())
     return h.hexdigest()[:16]

@@ -430,9 +430,11 @@ __device__ __forceinline__ float load_elem(const char* p) {
   }
 }
 
-// Plain VALU version: one token per lane for the scores, lanes over dims for P V.  One wave
-// per (sequence, KV head, group of partitions) walks the group's tokens in order; the online
-// softmax simply continues across the partition boundaries inside the group.
+// Plain VALU version: one token per lane for the scores, lanes over dims for P V (the chunk's
+// V values transposed through LDS, so that both the loads and the P V reads are coalesced).
+// One wave per (sequence, KV head, group of partitions) walks the group's tokens in 64-token
+// chunks, in order; the online softmax simply continues across the partition boundaries
+// inside the group.
 static constexpr int kCB = 16;  // at most this many K chunks per lane in flight (scores)
 static constexpr int kVB = 32;  // V loads per lane in flight (P V, dims 64 and up)
 
