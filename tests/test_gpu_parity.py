@@ -181,6 +181,30 @@ def test_generic_kernel_block_sizes(bs, hkv, d, hq, dtype, group_parts):
     _check_partials(case, dc, group_parts=group_parts)
 
 
+HEAD_COUNTS = [(1, "f32", 64), (3, "f32", 128), (5, "bf16", 64), (12, "f32", 256), (7, "bf16", 128)]
+
+
+@pytest.mark.parametrize("group,dtype,d", HEAD_COUNTS, ids=[f"g{g}-{t}-d{d}" for g, t, d in HEAD_COUNTS])
+def test_generic_kernel_head_counts(group, dtype, d):
+    """The VALU kernel is built for 1, 2, 4, 8 or 16 query heads per KV head; other counts run
+    in the next size up, with zero queries in the padding heads, which are never written.
+    Counts 1, 3, 5, 7 and 12 (block size 8 for bf16, so that the VALU kernel serves it) against
+    the oracle, partials included, with ragged lengths over a full 64-token chunk."""
+    from synth import gqa_case
+    bs = 16 if dtype == "f32" else 8
+    hkv = 2
+    lens = [37, 1, 200, 64 + 5]
+    begin = [0, 0, 3, 16]
+    case = gqa_case(bs, hkv, d, hkv * group, lens, [96] * len(lens), tok_begin=begin, dtype=dtype)
+    _say(f"[generic heads] group={group} {dtype} d={d}")
+    dc, o, lse = _run(case, None, 2)
+    o_ref, lse_ref = oc.full_reference(case)
+    assert oc.out_error(case, o, o_ref) <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+    _check_partials(case, dc, group_parts=2)
+
+
 @pytest.mark.parametrize("hq", [1, 5, 8])
 def test_mla_fewer_heads(hq):
     """Latent-cache decode with fewer than the 16 heads an MFMA tile holds: the unused head
