@@ -432,29 +432,42 @@ __device__ __forceinline__ float load_elem(const char* p) {
 
 // Plain VALU version: one token per lane for the scores, lanes over dims for P V (the chunk's
 // V values transposed through LDS, so that both the loads and the P V reads are coalesced).
-// One wave per (sequence, KV head, group of partitions) walks the group's tokens in 64-token
-// chunks, in order; the online softmax simply continues across the partition boundaries
-// inside the group.
+// One workgroup of kGW waves per (sequence, KV head, group of partitions): wave w takes the
+// group's 64-token chunks w, w + kGW, ..., each wave with its own online softmax and its own
+// LDS staging area, and the waves' states are merged exactly at the end (the LSE rescaling of
+// the merge kernel), so a group's chunks are read in parallel.
 static constexpr int kCB = 16;  // at most this many K chunks per lane in flight (scores)
 static constexpr int kVB = 32;  // V loads per lane in flight (P V, dims 64 and up)
+static constexpr int kGW = 4;   // waves per workgroup
+
+// Orders a wave's LDS writes before its own later reads by other lanes (and its reads before
+// later writes): a wave's LDS operations complete in order, this keeps the compiler's too.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
 
 // GP: the query heads per KV head rounded up to a power of two, a compile-time bound (the
 // head loops then carry no per-head branches, which keeps the code small enough for the
 // instruction cache); heads G .. GP-1 get zero queries, are computed and never written.
 template <typename T, int D, int GP>
-__global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kGW) void gqa_decode_generic_kernel(DecodeArgs a) {
   constexpr int R = D / 64;                // dims per lane in the output
   constexpr int X = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   constexpr int CB = (D / X) < kCB ? (D / X) : kCB;  // K chunks in flight
   static_assert((D / X) % CB == 0, "K chunks per token must be a multiple of CB");
+  static_assert(GP * D <= 64 * 65, "the wave merge reuses a wave's V staging area");
   __shared__ float qs[GP][D];
-  // P V operands, staged through LDS: the chunk's weights [head][token], and 64 dims of its V
-  // values transposed, [dim][token] (row padded by one word: conflict-free both ways).  V is
-  // stored token-fastest, so loads with lane = token coalesce (16 consecutive slots of a
-  // block), where lane = dim would touch a cache line per lane and token.
-  __shared__ float sp[GP][64];
-  __shared__ float sv[64][65];
-  const int lane = threadIdx.x;
+  // P V operands of each wave, staged through LDS: the chunk's weights [head][token], and 64
+  // dims of its V values transposed, [dim][token] (row padded by one word: conflict-free both
+  // ways).  V is stored token-fastest, so loads with lane = token coalesce (16 consecutive
+  // slots of a block), where lane = dim would touch a cache line per lane and token.  At the
+  // end the V areas hold the waves' unnormalised outputs for the merge.
+  __shared__ float sp[kGW][GP][64];
+  __shared__ float sv[kGW][64][65];
+  __shared__ float sml[kGW][2][GP];  // each wave's running max and sum per head
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
 
   int w = blockIdx.x;
   const int k = w % a.grid_ng;
@@ -464,11 +477,11 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
 
   int beg, P, ng;
   const int np = seq_partitions(a, b, &beg, &P, &ng);
-  if (k == 0 && kvh == 0 && lane == 0) {
+  if (k == 0 && kvh == 0 && threadIdx.x == 0) {
     a.nparts[b] = ng < 0 ? 0 : ng;
     if (np < 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
   }
-  if (k >= ng) return;
+  if (k >= ng) return;  // uniform over the workgroup
   const int L = a.seq[b];
   const int64_t span = (int64_t)P * a.group_parts;
   const int lo = (int)(beg + k * span);
@@ -477,12 +490,13 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
   // block ids are read one chunk ahead (the first chunk's before q), so that a chunk's K / V
   // loads need not wait for a table read of their own
-  int32_t pid_next = lo + lane < hi ? trow[(lo + lane) >> a.bs_shift] : 0;
+  const int first = lo + 64 * wv;
+  int32_t pid_next = first + lane < hi ? trow[(first + lane) >> a.bs_shift] : 0;
 
-  for (int h = 0; h < GP; ++h) {
+  for (int i = threadIdx.x; i < GP * D; i += 64 * kGW) {
+    const int h = i / D, d = i - (i / D) * D;
     const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.hq + kvh * G + min(h, G - 1)) * D;
-    for (int d = lane; d < D; d += 64)
-      qs[h][d] = h < G ? load_elem<T>(reinterpret_cast<const char*>(qrow + d)) : 0.f;
+    qs[h][d] = h < G ? load_elem<T>(reinterpret_cast<const char*>(qrow + d)) : 0.f;
   }
   __syncthreads();
 
@@ -496,12 +510,14 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
     for (int r = 0; r < R; ++r) acc[h][r] = 0.f;
   }
   bool bad = false;
+  float (*spw)[64] = sp[wv];
+  float (*svw)[65] = sv[wv];
 
-  for (int c0 = lo; c0 < hi; c0 += 64) {
+  for (int c0 = first; c0 < hi; c0 += 64 * kGW) {  // uniform over the wave
     const int t = c0 + lane;
     const bool in = t < hi;
     const int32_t pid = pid_next;
-    const int tn = t + 64;
+    const int tn = t + 64 * kGW;
     pid_next = tn < hi ? trow[tn >> a.bs_shift] : 0;
     const bool ok = in && valid_block(a.rt, pid);
     bad |= in && !ok;
@@ -533,11 +549,11 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
-          const uint32_t w[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+          const uint32_t wd[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
 #pragma unroll
           for (int e = 0; e < X; ++e) {
-            const float kv = sizeof(T) == 4 ? __uint_as_float(w[e])
-                                            : bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+            const float kv = sizeof(T) == 4 ? __uint_as_float(wd[e])
+                                            : bf16_to_f32((uint16_t)(wd[e >> 1] >> (16 * (e & 1))));
 #pragma unroll
             for (int h = 0; h < GP; ++h) s[h] += qs[h][(k0 + u) * X + e] * kv;
           }
@@ -563,15 +579,15 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
     // an invalid block stages zeros (its slots may hold NaN bit patterns, which a zero weight
     // would not cancel) and has weight zero.
     const int cnt = min(64, hi - c0);
-    __syncthreads();  // the previous chunk's reads of sp are done
+    wave_lds_sync();  // the previous chunk's reads of sp are done
 #pragma unroll
-    for (int h = 0; h < GP; ++h) sp[h][lane] = pr[h];
+    for (int h = 0; h < GP; ++h) spw[h][lane] = pr[h];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      __syncthreads();  // the previous slice's reads of sv are done
+      wave_lds_sync();  // the previous slice's reads of sv are done
       if (r == 0) {
 #pragma unroll
-        for (int j = 0; j < 64; ++j) sv[j][lane] = v0[j];
+        for (int j = 0; j < 64; ++j) svw[j][lane] = v0[j];
       } else {
         for (int j0 = 0; j0 < 64; j0 += kVB) {
           float v[kVB];
@@ -581,27 +597,49 @@ __global__ __launch_bounds__(64) void gqa_decode_generic_kernel(DecodeArgs a) {
                                                (int64_t)sizeof(T)))
                       : 0.f;
 #pragma unroll
-          for (int u = 0; u < kVB; ++u) sv[j0 + u][lane] = v[u];
+          for (int u = 0; u < kVB; ++u) svw[j0 + u][lane] = v[u];
         }
       }
-      __syncthreads();
+      wave_lds_sync();
       for (int j = 0; j < cnt; ++j) {
-        const float vj = sv[lane][j];
+        const float vj = svw[lane][j];
 #pragma unroll
-        for (int h = 0; h < GP; ++h) acc[h][r] += sp[h][j] * vj;
+        for (int h = 0; h < GP; ++h) acc[h][r] += spw[h][j] * vj;
       }
     }
   }
   if (__any(bad) && lane == 0) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 
+  // Exact merge of the waves' states: M = max_w m_w, l = sum_w l_w e^(m_w - M),
+  // o = sum_w acc_w e^(m_w - M) / l, lse = M + ln l (waves without a chunk: m = -inf, weight 0).
+  __syncthreads();  // every wave's staging reads are done: the V areas take the outputs
+  float* so = &sv[wv][0][0];  // [GP][D] unnormalised output of this wave
 #pragma unroll
   for (int h = 0; h < GP; ++h) {
-    if (h >= G) continue;
-    const int64_t row = ((int64_t)b * a.hq + kvh * G + h) * a.max_parts + k;
-    float* op = a.o_part + row * D;
 #pragma unroll
-    for (int r = 0; r < R; ++r) op[lane + 64 * r] = acc[h][r] / l[h];
-    if (lane == 0) a.lse_part[row] = m[h] + logf(l[h]);
+    for (int r = 0; r < R; ++r) so[h * D + lane + 64 * r] = acc[h][r];
+    if (lane == 0) {
+      sml[wv][0][h] = m[h];
+      sml[wv][1][h] = l[h];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += 64 * kGW) {
+    const int h = i / D, d = i - (i / D) * D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kGW; ++u) mx = fmaxf(mx, sml[u][0][h]);
+    const float mref = mx == kNegInf ? 0.f : mx;
+    float ls = 0.f, o = 0.f;
+#pragma unroll
+    for (int u = 0; u < kGW; ++u) {
+      const float e = expf(sml[u][0][h] - mref);  // 0 for a wave without tokens
+      ls += sml[u][1][h] * e;
+      o += (&sv[u][0][0])[h * D + d] * e;
+    }
+    const int64_t row = ((int64_t)b * a.hq + kvh * G + h) * a.max_parts + k;
+    a.o_part[row * D + d] = o / ls;
+    if (d == 0) a.lse_part[row] = mx + logf(ls);
   }
 }
 
@@ -681,9 +719,9 @@ hipError_t launch_gqa_probe(const DecodeArgs& a, int d, bool stream, dim3 grid, 
 template <typename T, int GP>
 static hipError_t launch_generic_tg(const DecodeArgs& a, int d, dim3 grid, hipStream_t st) {
   switch (d) {
-    case 64: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 64, GP>), grid, dim3(64), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 128, GP>), grid, dim3(64), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 256, GP>), grid, dim3(64), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 64, GP>), grid, dim3(64 * kGW), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 128, GP>), grid, dim3(64 * kGW), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((gqa_decode_generic_kernel<T, 256, GP>), grid, dim3(64 * kGW), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
