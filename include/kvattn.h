@@ -262,7 +262,8 @@ int32_t kvattn_partition_count(int32_t ctx_len, int32_t tok_begin, int32_t part_
  * and at least 4 and two partitions span at most 127 blocks, else one) and merges the waves'
  * partials on chip, exactly, by the LSE rescaling of kvattn_merge_lse; the latent (MLA)
  * kernel gives the group's even and odd blocks to two teams of waves and merges the two the
- * same way; the VALU kernel walks the group's tokens in order.  group_parts = 1
+ * same way; the VALU kernel gives the group's 64-token chunks to four waves in turn and merges
+ * them the same way.  group_parts = 1
  * writes one partial per partition; larger groups write fewer partials, which is faster on
  * long contexts (partial writes compete with the K/V read stream).  Logical token t of
  * sequence b lives at offset t % bs of physical block table_dev[b][t / bs].

@@ -29,9 +29,10 @@
 //    partial outputs are expensive while the read stream is running (on MI355X, 16.9 MB of
 //    partials written next to the 1 GiB of 16 x 32K K/V cost ~16 us, ~8% of the step), and
 //    the group merge divides them by group_parts.
-//  * gqa_decode_generic_kernel (fp32 or bf16, any block size): a plain VALU version, one wave
-//    per group walking its tokens in order, used for fp32 caches and as an independent
-//    cross-check of the MFMA kernel.
+//  * gqa_decode_generic_kernel (fp32 or bf16, any block size): a plain VALU version, four
+//    waves per group taking its 64-token chunks in turn, merged exactly at the end; used for
+//    fp32 caches and block sizes below 16, and as an independent cross-check of the MFMA
+//    kernel.
 
 #include "device_common.h"
 
