@@ -220,6 +220,34 @@ def test_mla_fewer_heads(hq):
     _check_partials(case, dc, group_parts=2)
 
 
+@pytest.mark.parametrize("group_parts", [1, 3])
+def test_mla_split_with_external_partial(group_parts):
+    """A latent-cache layer split as the pages split a sequence between engines: the oldest
+    tokens [0, begin) are a partial computed elsewhere (the oracle's, here), the device decodes
+    [begin, L) and the merge folds the external partial in (the 512-wide wave merge with an
+    external term).  Split points on and inside block boundaries; the result must be the
+    unsplit attention over [0, L)."""
+    from synth import mla_case
+    lens = [3000, 1000, 64 * 20 + 7, 700]
+    begins = [1024, 512, 64 * 7 + 5, 699]
+    case = mla_case(lens, [256] * len(lens))
+    o_ref, lse_ref = oc.full_reference(case)            # the whole context, unsplit
+    lay, qf = oc.layout_of(case), oc.q_f64(case)
+    o_x = np.zeros((case.batch, case.num_q_heads, case.head_dim_v))
+    l_x = np.zeros((case.batch, case.num_q_heads))
+    for b, beg in enumerate(begins):
+        k, v = oracle.gather_sequence(lay, case.regions, case.region_blocks, case.table[b], 0, beg)
+        o_x[b], l_x[b] = oracle.attend(qf[b], k, v, case.scale)
+    case.tok_begin = np.array(begins, np.int32)
+    _say(f"[mla split] L={lens} begin={begins} group_parts={group_parts}")
+    dc, o, lse = _run(case, (o_x, l_x), group_parts)
+    err = oc.out_error(case, o, o_ref)
+    _say(f"[mla split] out error {err:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+    assert int(dc.step.err.item()) == 0
+
+
 def test_long_mla_groups_cross_block_id_windows():
     """Latent-cache groups longer than the 128 stages (64-token blocks) whose block ids the
     kernel holds in registers at a time: a group of 257 stages starting mid-block (two full
