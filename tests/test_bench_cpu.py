@@ -48,3 +48,43 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _write_csv(path, header, rows):
+    with open(path, "w") as fh:
+        fh.write(",".join(f'"{h}"' for h in header) + "\n")
+        for r in rows:
+            fh.write(",".join(f'"{v}"' for v in r) + "\n")
+
+
+def test_profile_summary_picks_the_decode_kernel_not_the_probe(tmp_path):
+    """The gather probe is timed next to the decode kernel and may run longer in total; the
+    summary's stored values must still be the decode kernel's, with the HBM bytes scaled by
+    the copy calibration (FETCH_SIZE reads half a copy's bytes, WRITE_SIZE all of them)."""
+    dec = "kvattn::gqa_decode_mfma_kernel<128, 4, 2, true>(kvattn::DecodeArgs)"
+    probe = "void kvattn::gqa_probe_kernel<128, 4, 2, true>(kvattn::DecodeArgs, unsigned int*)"
+    copy = bench.COPY_KERNEL
+    stats, fetch, write = tmp_path / "stats", tmp_path / "fetch", tmp_path / "write"
+    for d in (stats, fetch, write):
+        d.mkdir()
+    _write_csv(stats / "run_kernel_stats.csv",
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+               [[probe, 22, 22 * 171000, 171000, 40, 168000, 180000, 1],
+                [dec, 20, 20 * 163000, 163000, 38, 157000, 170000, 1],
+                [copy, 12, 12 * 700000, 700000, 20, 600000, 800000, 1]])
+    big = 2 << 30
+    hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    _write_csv(fetch / "run_counter_collection.csv", hdr,
+               [[copy, 1 << 20, "FETCH_SIZE", big / 2 / 1024], [dec, 4096, "FETCH_SIZE", 524800.0],
+                [probe, 4096, "FETCH_SIZE", 524300.0]])
+    _write_csv(write / "run_counter_collection.csv", hdr,
+               [[copy, 1 << 20, "WRITE_SIZE", big / 1024], [dec, 4096, "WRITE_SIZE", 1056.0],
+                [probe, 4096, "WRITE_SIZE", 1.0]])
+    out = tmp_path / "summary.md"
+    bench.summarize_profile("gqa_32k", str(fetch), str(write), str(stats), str(out), ["cmd"])
+    vals = bench.read_profile_values(str(out))
+    assert vals["kernel"] == "kvattn::gqa_decode_mfma_kernel<128, 4, 2, true>"
+    assert vals["avg_duration_us"] == "163.00"
+    assert abs(float(vals["fetch_factor"]) - 2.0) < 1e-9 and abs(float(vals["write_factor"]) - 1.0) < 1e-9
+    assert int(vals["hbm_bytes_per_launch"]) == round(524800.0 * 1024 * 2 + 1056.0 * 1024)
+    assert vals["kernel_hash"] == bench.kernel_hash("gqa_32k")
