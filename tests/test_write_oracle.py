@@ -67,6 +67,9 @@ def test_writes_in_pieces_equal_elementwise_scatter(layout):
     assert np.array_equal(kk, _widen(k, layout)) and np.array_equal(vv, _widen(v, layout))
 
 
+# the random region bytes include signalling-NaN bf16 patterns outside the written tokens;
+# widening them to float64 is exact (NaN stays NaN) but numpy reports the cast as invalid
+@pytest.mark.filterwarnings("ignore:invalid value encountered in cast:RuntimeWarning")
 def test_write_touches_only_its_tokens():
     layout = Layout(16, 2, 16, 16, "bf16", False)
     rng = np.random.default_rng(5)
