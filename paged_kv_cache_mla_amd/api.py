@@ -508,11 +508,31 @@ class DecodeStep:
         self.o_out = torch.empty((self.batch, self.hq, self.dv), dtype=f32, device=device)
         self.lse_out = torch.empty((self.batch, self.hq), dtype=f32, device=device)
         self.err = torch.zeros(1, dtype=torch.int32, device=device)
+        self._fixed = None
+
+    def _marshal(self):
+        """The arguments of the two calls that do not change between steps, converted once
+        (the per-call conversions are most of a small step's host time).  The tensors and host
+        rows they point to stay referenced here, so the addresses stay valid while this object
+        lives."""
+        self._lib = _lib.load()
+        part = (_dptr(self.table_dev), self.max_blocks, _i32p(self.ctx), _i32p(self.beg),
+                _i32p(self.part), _dptr(self.seq_dev), self.max_parts, self.group_parts,
+                _dptr(self.o_part), _dptr(self.lse_part), _dptr(self.nparts), _dptr(self.err))
+        merge = (_dptr(self.o_part), _dptr(self.lse_part), _dptr(self.nparts), self.batch,
+                 self.hq, self.max_parts, self.dv)
+        out = (_dptr(self.o_out), _dptr(self.lse_out))
+        keep = (self.table_dev, self.seq_dev, self.o_part, self.lse_part, self.nparts, self.err,
+                self.o_out, self.lse_out, self.ctx, self.beg, self.part)
+        self._fixed = (part, merge, out, keep)
 
     def partial(self, q, q_dtype, scale, stream=None):
-        decode_partial(self.pool, q, q_dtype, self.hq, scale, self.table_dev, self.max_blocks,
-                       self.ctx, self.beg, self.part, self.seq_dev, self.max_parts, self.o_part,
-                       self.lse_part, self.nparts, self.err, stream, self.group_parts)
+        if self._fixed is None:
+            self._marshal()
+        st = self._lib.kvattn_decode_partial(self.pool.handle, _dptr(q), int(q_dtype), self.batch,
+                                             self.hq, ctypes.c_float(scale), *self._fixed[0],
+                                             _stream(stream))
+        check(st, "decode_partial")
 
     def probe(self, xsum, stream=None):
         """The gather probe over this step's ranges, in its launch configuration."""
@@ -520,8 +540,11 @@ class DecodeStep:
                      self.part, self.seq_dev, xsum, self.err, stream, self.group_parts)
 
     def merge(self, o_ext=None, lse_ext=None, stream=None):
-        merge_lse(self.o_part, self.lse_part, self.nparts, self.batch, self.hq, self.max_parts,
-                  self.dv, self.o_out, o_ext, lse_ext, self.lse_out, stream)
+        if self._fixed is None:
+            self._marshal()
+        st = self._lib.kvattn_merge_lse(*self._fixed[1], _dptr(o_ext), _dptr(lse_ext),
+                                        *self._fixed[2], _stream(stream))
+        check(st, "merge_lse")
 
     def run(self, q, q_dtype, scale, o_ext=None, lse_ext=None, stream=None):
         self.partial(q, q_dtype, scale, stream)
