@@ -359,6 +359,42 @@ def test_deterministic_bitwise(name):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_interleaved_steps_keep_their_own_buffers():
+    """Two decode steps alive at once, their calls interleaved, with q passed as fresh tensors
+    and changed in place between calls: each step reads and writes only its own buffers (the
+    step object converts its fixed arguments once), and each result equals the oracle's for
+    the q it was given."""
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    ca, cb = make_case("gqa_32k", "small"), make_case("mla_16k", "small")
+    da, db = DeviceCase(ca), DeviceCase(cb)
+    ref_a = oc.full_reference(ca)
+    ref_b = oc.full_reference(cb)
+    qa0 = da.q.clone()
+    qa_rev = da.q.flip(0).contiguous()
+    ref_a_rev = oc.full_reference(_with_q(ca, np.ascontiguousarray(ca.q[::-1])))
+    for i in range(3):
+        if i == 0:
+            q = qa0.clone()            # a fresh tensor
+        else:
+            da.q.copy_(qa_rev if i == 1 else qa0)   # the same tensor, changed in place
+            q = da.q
+        da.step.partial(q, da.q_dtype, ca.scale)
+        db.run()
+        da.step.merge()
+        torch.cuda.synchronize()
+        want_a = ref_a_rev if i == 1 else ref_a
+        assert oc.out_error(ca, da.step.o_out.cpu().numpy(), want_a[0]) <= oc.out_tol(ca), i
+        assert oc.out_error(cb, db.step.o_out.cpu().numpy(), ref_b[0]) <= oc.out_tol(cb), i
+    assert int(da.step.err.item()) == 0 and int(db.step.err.item()) == 0
+
+
+def _with_q(case, q):
+    import copy
+    c2 = copy.copy(case)
+    c2.q = q
+    return c2
+
+
 def _relabelled(case, seed):
     """Same logical content, every physical block moved to a new random slot (across
     regions), tables rewritten accordingly."""
