@@ -20,7 +20,9 @@ Sources (cited by tag):
                    reclaimed pages joining the free-block pool.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
-invariants, brute force at 50 digits, a library special case) or, for the allocator model,
+invariants, brute force at 50 digits, a library special case; the per-partition partials
+against attention over element-wise-written dense slices; the address resolution against
+the element found at each returned offset, with planted mistakes that must fail) or, for the allocator model,
 by ``tests/test_alloc_oracle.py`` (published SplitMix64 outputs, exhaustive permutation
 counts), or, for the share policy, by ``tests/test_share_policy.py`` (brute-force minimum of
 Eq. 1's step time, balance, limits, exact cost recovery, a library line fit).  None is "parity unpinned".
@@ -28,7 +30,7 @@ Eq. 1's step time, balance, limits, exact cost recovery, a library line fit).  N
 
 from .bf16 import bf16_bits_to_f64
 from .layout import Layout, block_elems, gather_sequence, token_k_offset
-from .attention import attend, merge, partial_over_range
+from .attention import attend, merge
 from .partition import partition_count, partition_ranges
 from .write import write_tokens
 from .decode import decode_reference, decode_partials_reference, resolve_offsets_reference
@@ -44,7 +46,6 @@ __all__ = [
     "token_k_offset",
     "attend",
     "merge",
-    "partial_over_range",
     "partition_count",
     "partition_ranges",
     "write_tokens",

@@ -48,11 +48,6 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     return o, lse
 
 
-def partial_over_range(q, k, v, scale):
-    """Partial (o, lse) of the tokens in k/v; identical to `attend` by definition."""
-    return attend(q, k, v, scale)
-
-
 def merge(os_, lses):
     """Exact LSE merge of partials.
 

@@ -57,18 +57,6 @@ def decode_partials_reference(layout: Layout, regions, region_blocks, table, ctx
     return out
 
 
-def merge_partials(o_parts, lse_parts, o_ext=None, lse_ext=None):
-    """Merge one sequence's partials [np, Hq, Dv] / [np, Hq] plus an optional external one."""
-    os_ = list(o_parts)
-    ls_ = list(lse_parts)
-    if o_ext is not None:
-        os_.append(o_ext)
-        ls_.append(lse_ext)
-    if not os_:
-        raise ValueError("nothing to merge")
-    return merge(os_, ls_)
-
-
 def resolve_offsets_reference(layout: Layout, region_blocks, table, ctx_lens, max_tokens):
     """(region index, byte offset of K(h=0, t, 0)) for every (b, t); -1 where not resident."""
     from .layout import block_elems

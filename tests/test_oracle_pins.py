@@ -166,13 +166,13 @@ def test_matches_torch_sdpa_float64(shape):
 
 
 # ---------------------------------------------------------------- block layout
-def _write_pool_elementwise(layout, dense_k, dense_v, table_row, region_blocks, dtype):
-    """Scatter dense K/V into regions with the per-element offsets of the documented layout
-    (a second, loop-based statement of it; the oracle reads with reshapes/transposes)."""
+def _scatter_elementwise(layout, regions, region_blocks, dense_k, dense_v, table_row):
+    """Write one sequence's dense K/V into `regions` with the per-element offsets of the
+    documented layout (a second, loop-based statement of it; the oracle reads with
+    reshapes/transposes).  Values are stored as given (float32, or uint16 bf16 bits)."""
     bs, hkv, dk, dv, x = (layout.block_size, layout.num_kv_heads, layout.head_dim_k,
                           layout.head_dim_v, layout.chunk)
     nel = block_elems(layout)
-    regions = [np.full(n * nel, np.nan, dtype) for n in region_blocks]
     starts = np.cumsum([0] + list(region_blocks))
     for t in range(dense_k.shape[0]):
         pid = int(table_row[t // bs])
@@ -189,6 +189,14 @@ def _write_pool_elementwise(layout, dense_k, dense_v, table_row, region_blocks, 
             if not layout.latent:
                 for j in range(dv):
                     regions[r][base + hkv * bs * dk + (h * dv + j) * bs + tt] = dense_v[t, h, j]
+
+
+def _write_pool_elementwise(layout, dense_k, dense_v, table_row, region_blocks, dtype):
+    nel = block_elems(layout)
+    # NaN (or NaN bf16 bit patterns) in every slot no token is written to
+    fill = np.nan if np.issubdtype(np.dtype(dtype), np.floating) else 0x7FC1
+    regions = [np.full(n * nel, fill, dtype) for n in region_blocks]
+    _scatter_elementwise(layout, regions, region_blocks, dense_k, dense_v, table_row)
     return regions
 
 
@@ -270,3 +278,181 @@ def test_kv_bytes_per_token_match_page_tables():
         assert abs(got - (t2["unpinned"][model] + t2["pinned"][model])) <= 0.011
         assert round(256 * 32 * per_tok * layers / 1e6) == t2["all_layers_256_entries_mb"][model]
         assert abs(1024 * 32 * per_tok / 1e6 - t2["one_layer_1024_entries_mb"][model]) <= 0.06
+
+
+# ---------------------------------------------------------------- per-partition partials
+def _pool_with_dense(layout, lens, region_blocks, rng, unique=False):
+    """A pool over two regions holding `len(lens)` sequences written element by element, with
+    the dense float64 K/V each sequence holds and its table (entries past the sequence ABSENT).
+    With `unique`, every stored element is a distinct value (distinct bit pattern)."""
+    bs, hkv, dk, dv = (layout.block_size, layout.num_kv_heads, layout.head_dim_k,
+                       layout.head_dim_v)
+    nbs = [-(-L // bs) for L in lens]
+    max_blocks = max(nbs) + 2
+    total = sum(region_blocks)
+    ids = rng.permutation(total).astype(np.int32)
+    table = np.full((len(lens), max_blocks), oracle.layout.ABSENT, np.int32)
+    pos = 0
+    for b, nb in enumerate(nbs):
+        table[b, :nb] = ids[pos:pos + nb]
+        pos += nb
+    store = np.uint16 if layout.dtype == "bf16" else np.float32
+    nel = block_elems(layout)
+    regions = [np.full(n * nel, 0x7FC1 if store == np.uint16 else np.nan, store)
+               for n in region_blocks]
+    n_k = [L * hkv * dk for L in lens]
+    n_v = [0 if layout.latent else L * hkv * dv for L in lens]
+    need = sum(n_k) + sum(n_v)
+    if layout.dtype == "bf16":
+        # distinct finite positive and negative bf16 patterns (exponents 2^-61 .. 2^63)
+        pool_bits = np.concatenate([np.arange(0x2100, 0x5F00), np.arange(0xA100, 0xDF00)])
+        vals = (rng.choice(pool_bits, need, replace=False) if unique
+                else rng.choice(pool_bits, need)).astype(np.uint16)
+        widen = oracle.bf16_bits_to_f64
+    else:
+        vals = rng.standard_normal(need).astype(np.float32)
+        if unique:
+            assert len(np.unique(vals)) == need
+        widen = lambda a: a.astype(np.float64)  # noqa: E731
+    dense = []
+    off = 0
+    for b, L in enumerate(lens):
+        k = vals[off:off + n_k[b]].reshape(L, hkv, dk)
+        off += n_k[b]
+        if layout.latent:
+            v = k[:, :, :dv]
+        else:
+            v = vals[off:off + n_v[b]].reshape(L, hkv, dv)
+            off += n_v[b]
+        _scatter_elementwise(layout, regions, region_blocks, k, v, table[b])
+        dense.append((k, widen(k), widen(v)))
+    return regions, table, dense
+
+
+PARTIAL_LAYOUTS = [Layout(4, 2, 8, 8, "f32", False), Layout(8, 1, 16, 16, "bf16", False),
+                   Layout(8, 1, 24, 16, "bf16", True), Layout(4, 1, 32, 16, "f32", True)]
+
+
+def _check_partials_against_dense(layout, partials, dense, q, scale, lens, begins, parts):
+    """Each partition p of sequence b covers [beg + p*P, min(L, beg + (p+1)*P)) and its
+    partial is the attention over exactly those dense tokens."""
+    for b, (o_b, l_b) in enumerate(partials):
+        L, beg, P = lens[b], begins[b], parts[b]
+        count = -(-(L - beg) // P)
+        assert o_b.shape[0] == count and l_b.shape[0] == count, b
+        for p in range(count):
+            lo, hi = beg + p * P, min(L, beg + (p + 1) * P)
+            o_ref, l_ref = oracle.attend(q[b], dense[b][1][lo:hi], dense[b][2][lo:hi], scale)
+            assert np.array_equal(o_b[p], o_ref), (b, p)
+            assert np.array_equal(l_b[p], l_ref), (b, p)
+
+
+@pytest.mark.parametrize("layout", PARTIAL_LAYOUTS,
+                         ids=lambda l: f"{l.dtype}-{'mla' if l.latent else 'gqa'}")
+def test_partials_are_attention_over_their_token_ranges(layout):
+    """decode_partials_reference against attention over element-wise-written dense slices:
+    a start inside the context (tok_begin != 0), short last partitions, a one-token range and
+    an empty one; the merge of every sequence's partials equals the unsplit attention over
+    [tok_begin, L) to 1e-12 ([InplaceKVCache] §5.1: the split is exact)."""
+    rng = np.random.default_rng(600 + layout.block_size + 7 * layout.latent)
+    bs = layout.block_size
+    lens = [5 * bs + 3, 4 * bs, 2 * bs + 1, 3 * bs, 7]
+    begins = [bs + 2, 0, 2 * bs, 3 * bs, 7]          # mid-block start, 0, one token, empty
+    parts = [2 * bs, bs, bs, 2 * bs, bs]
+    regions, table, dense = _pool_with_dense(layout, lens, [6, 40], rng)
+    hq = 4 if not layout.latent else 3
+    q = rng.standard_normal((len(lens), hq, layout.head_dim_k)).astype(np.float32)
+    scale = 0.31
+    partials = oracle.decode_partials_reference(layout, regions, [6, 40], table, lens, q, scale,
+                                                parts, tok_begin=begins)
+    qf = q.astype(np.float64)
+    _check_partials_against_dense(layout, partials, dense, qf, scale, lens, begins, parts)
+    unsplit = oracle.decode_reference(layout, regions, [6, 40], table, lens, q, scale,
+                                      tok_begin=begins)
+    for b, (o_b, l_b) in enumerate(partials):
+        o_m, l_m = (oracle.merge(list(o_b), list(l_b)) if o_b.shape[0] else
+                    (np.zeros_like(unsplit[0][b]), np.full(hq, -np.inf)))
+        o_d, l_d = oracle.attend(qf[b], dense[b][1][begins[b]:], dense[b][2][begins[b]:], scale)
+        assert np.max(np.abs(o_m - unsplit[0][b])) <= 1e-12
+        assert np.max(np.abs(o_m - o_d)) <= 1e-12
+        fin = np.isfinite(l_d)
+        assert np.array_equal(np.isfinite(l_m), fin) and np.array_equal(np.isfinite(unsplit[1][b]), fin)
+        assert np.max(np.abs(l_m[fin] - l_d[fin]), initial=0.0) <= 1e-12
+
+
+def test_partials_pin_catches_a_dropped_begin():
+    """A partial reference that ignored tok_begin (every range starting at 0) fails the pin."""
+    layout = PARTIAL_LAYOUTS[0]
+    rng = np.random.default_rng(610)
+    lens, begins, parts = [23, 17], [5, 4], [8, 4]
+    regions, table, dense = _pool_with_dense(layout, lens, [6, 40], rng)
+    q = rng.standard_normal((2, 4, layout.head_dim_k)).astype(np.float32)
+    wrong = oracle.decode_partials_reference(layout, regions, [6, 40], table, lens, q, 0.5, parts)
+    with pytest.raises(AssertionError):
+        _check_partials_against_dense(layout, wrong, dense, q.astype(np.float64), 0.5, lens,
+                                      begins, parts)
+
+
+# ---------------------------------------------------------------- address resolution
+def _check_resolution(layout, regions, region_blocks, table, lens, dense, max_tokens,
+                      resolve=None):
+    """Every (b, t) of a resident block resolves to the region and byte offset at which the
+    stored element K(h=0, t, 0) (MLA: C(t, 0)) sits; every other (b, t) gives -1 / -1."""
+    resolve = resolve or oracle.resolve_offsets_reference
+    region, offset = resolve(layout, region_blocks, table, lens, max_tokens)
+    starts = np.cumsum([0] + list(region_blocks))
+    e = layout.elem_bytes
+    for b in range(len(lens)):
+        for t in range(max_tokens):
+            pid = int(table[b][t // layout.block_size]) if t // layout.block_size < table.shape[1] else -1
+            resident = t < lens[b] and 0 <= pid < starts[-1]
+            if not resident:
+                assert region[b, t] == -1 and offset[b, t] == -1, (b, t)
+                continue
+            r = int(np.searchsorted(starts, pid, side="right") - 1)
+            assert region[b, t] == r, (b, t)
+            off = int(offset[b, t])
+            assert off % e == 0 and 0 <= off < regions[r].nbytes, (b, t)
+            got = regions[r].view(np.uint8)[off:off + e].view(regions[r].dtype)[0]
+            want = dense[b][0][t, 0, 0]
+            assert got.tobytes() == np.asarray(want, regions[r].dtype).tobytes(), (b, t)
+
+
+RESOLVE_LAYOUTS = [Layout(4, 2, 8, 8, "f32", False), Layout(4, 3, 16, 16, "bf16", False),
+                   Layout(8, 1, 24, 16, "bf16", True), Layout(2, 1, 8, 4, "f32", True),
+                   Layout(16, 2, 8, 8, "bf16", False)]
+
+
+def _resolve_case(layout, seed):
+    rng = np.random.default_rng(seed)
+    bs = layout.block_size
+    lens = [3 * bs + 1, 2 * bs, 1, 4 * bs - 1]
+    region_blocks = [5, 9]
+    regions, table, dense = _pool_with_dense(layout, lens, region_blocks, rng, unique=True)
+    table[3, 1] = oracle.layout.ABSENT               # a hole (not resident on this device)
+    table[2, 1] = sum(region_blocks) + 3              # beyond the sequence: never resolved
+    table[0, 2] = sum(region_blocks) + 1              # an invalid id inside the context
+    max_tokens = table.shape[1] * bs
+    return regions, region_blocks, table, lens, dense, max_tokens
+
+
+@pytest.mark.parametrize("layout", RESOLVE_LAYOUTS,
+                         ids=lambda l: f"bs{l.block_size}-{l.dtype}-{'mla' if l.latent else 'gqa'}")
+def test_resolved_offsets_point_at_each_tokens_first_key(layout):
+    """resolve_offsets_reference (with token_k_offset) over two regions, against an
+    element-wise write of distinct values: the element at the returned (region, byte offset)
+    is the token's K(h=0, t, 0), for every (b, t); -1 exactly past the context and for ABSENT
+    or invalid entries ([CrossPool] §3.1: logical KV address -> physical page)."""
+    regions, region_blocks, table, lens, dense, max_tokens = _resolve_case(layout, 620)
+    _check_resolution(layout, regions, region_blocks, table, lens, dense, max_tokens)
+
+
+@pytest.mark.parametrize("layout", RESOLVE_LAYOUTS[:3],
+                         ids=lambda l: f"{l.dtype}-{'mla' if l.latent else 'gqa'}")
+def test_resolution_pin_catches_a_wrong_token_offset(layout, monkeypatch):
+    """With token_k_offset planted as t * Dk (tokens contiguous in K), the pin fails."""
+    import oracle.decode as od
+    regions, region_blocks, table, lens, dense, max_tokens = _resolve_case(layout, 621)
+    monkeypatch.setattr(od, "token_k_offset", lambda lay, t: t * lay.head_dim_k)
+    with pytest.raises(AssertionError):
+        _check_resolution(layout, regions, region_blocks, table, lens, dense, max_tokens)
