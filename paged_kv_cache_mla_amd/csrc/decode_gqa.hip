@@ -334,7 +334,8 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
   if (G == 1) {  // the wave's partial is the group's partial
     if (n < grp) {
       const int64_t row = ((int64_t)b * a.hq + kvh * grp + n) * a.max_parts + k;
-      const float inv = 1.f / lsum;
+      // no weight (every block invalid): o = 0 beside lse = -inf, never 0 / 0
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
       float* op = a.o_part + row * D;
 #pragma unroll
       for (int t = 0; t < VT; ++t)
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
   float* sl = smem + G * grp * rs;   // [G][grp]
   if (n < grp) {
     if (p < np) {
-      const float inv = 1.f / lsum;
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
       float* op = so + (wv * grp + n) * rs;
 #pragma unroll
       for (int t = 0; t < VT; ++t)
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_decode_mfma_kern
       }
     }
     const int64_t row = ((int64_t)b * a.hq + kvh * grp + h) * a.max_parts + k;
-    a.o_part[row * D + d] = o / s;
+    a.o_part[row * D + d] = s > 0.f ? o / s : 0.f;
     if (d == 0) a.lse_part[row] = (mx + log2f(s)) * kLn2;
   }
 }
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(64 * kGW) void gqa_decode_generic_kernel(DecodeArgs
       o += (&sv[u][0][0])[h * D + d] * e;
     }
     const int64_t row = ((int64_t)b * a.hq + kvh * G + h) * a.max_parts + k;
-    a.o_part[row * D + d] = o / ls;
+    a.o_part[row * D + d] = ls > 0.f ? o / ls : 0.f;
     if (d == 0) a.lse_part[row] = mx + logf(ls);
   }
 }

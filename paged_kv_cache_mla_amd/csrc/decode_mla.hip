@@ -319,7 +319,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_kernel(DecodeArgs a, uint32
   }
   if (n < a.hq) {
     const int64_t row = ((int64_t)b * a.hq + n) * a.max_parts + k;
-    const float inv = 1.f / lsum;
+    // a group with no weight (every block invalid) writes o = 0 beside lse = -inf
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     float* op = a.o_part + row * kMlaDv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -6,6 +6,8 @@
 // and normaliser.  For each (sequence, head):
 //     M = max_p lse_p,  T = sum_p exp(lse_p - M),  lse = M + ln T,
 //     o = sum_p exp(lse_p - M) o_p / T        (= sum_p exp(lse_p - lse) o_p).
+// A partial of zero weight (lse = -inf, or a weight that underflows) is left out of the sum
+// by a select, never multiplied by 0: its o may be anything, NaN included.
 //
 // Three kernels.  The workgroup kernel: one 256-thread workgroup per (sequence, head); thread
 // (g, c) of a [groups x dv/4] arrangement owns 16-byte column c of partitions g, g + groups,
@@ -117,10 +119,9 @@ __global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
 #pragma unroll
       for (int k = 0; k < kR; ++k) {
         const int p = p0 + g + k * groups;
-        if (p < np) {  // a select: stale slots never enter the sum
-          const float w = p < kWts ? wts[p] : expf(lrow[p] - big);
-          acc += ov[k] * w;
-        }
+        const float w = p < np ? (p < kWts ? wts[p] : expf(lrow[p] - big)) : 0.f;
+        if (w != 0.f) acc += ov[k] * w;  // a select: stale slots and weightless partials
+                                         // (o may be anything there, NaN included) never enter
       }
     }
   }
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
   if (tid < cols) {
     f32x4 o = part[tid];
     for (int k = 1; k < groups; ++k) o += part[k * cols + tid];
-    if (ext) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[tid] * wx;
+    if (wx != 0.f) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[tid] * wx;
     orow_out[tid] = o * (1.f / tot);
   }
   if (a.lse_out && tid == 0) a.lse_out[row] = big + logf(tot);
@@ -181,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void merge_lse_wave_kernel(MergeArgs a) {
   for (int k = 0; k < kWaveParts; ++k) {
     const int p = s + k * S;
     const float w = __shfl(wl, p < 64 ? p : 0);
-    if (p < np) acc += ov[k] * w;  // a select: stale slots never enter the sum
+    if (p < np && w != 0.f) acc += ov[k] * w;  // a select: stale slots and weightless
+                                               // partials (o may be NaN there) never enter
   }
   for (int o = cols; o < 64; o <<= 1) {
     acc.x += __shfl_xor(acc.x, o);
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void merge_lse_wave_kernel(MergeArgs a) {
   }
   if (lane < cols) {
     f32x4 o = acc;
-    if (ext) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[lane] * wx;
+    if (wx != 0.f) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[lane] * wx;
     orow_out[lane] = o * (1.f / tot);
   }
   if (a.lse_out && lane == 0) a.lse_out[row] = big + logf(tot);
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void merge_lse_wide_kernel(MergeArgs a) {
 #pragma unroll
   for (int k = 0; k < kWideParts; ++k) {
     const float w = __shfl(wl, k);
-    if (k < np) {  // a select: stale slots never enter the sum
+    if (k < np && w != 0.f) {  // a select: stale slots and weightless partials never enter
 #pragma unroll
       for (int u = 0; u < C; ++u) acc[u] += ov[k][u] * w;
     }
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void merge_lse_wide_kernel(MergeArgs a) {
 #pragma unroll
   for (int u = 0; u < C; ++u) {
     f32x4 o = acc[u];
-    if (ext) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[lane + 64 * u] * wx;
+    if (wx != 0.f) o += reinterpret_cast<const f32x4*>(a.o_ext + row * a.dv)[lane + 64 * u] * wx;
     orow_out[lane + 64 * u] = o * inv;
   }
   if (a.lse_out && lane == 0) a.lse_out[row] = big + logf(tot);
