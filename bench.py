@@ -37,21 +37,6 @@ DESCR = {
     "mla_16k": "DeepSeek-V2-Lite-shaped MLA latent decode, B32 x 16K",
     "tiny_fp32": "tiny fp32 paged decode",
 }
-# Partitions merged on chip into each written partial, per workload (the launch configuration
-# the full-size parity tests use too): fewer partial writes next to the K/V read stream.
-GROUP_PARTS = {"gqa_32k": 16, "split_128k": 8, "prefix_shared": 2, "mla_16k": 4, "tiny_fp32": 1}
-# The split layer's device share shrinks with the host fraction r (1024-token partitions: 96,
-# 64 and 32 per sequence at r = 0.25, 0.5, 0.75), and with it the grid: measured best
-# group_parts per r (at r = 0.75, group_parts 8 would leave 128 workgroups for 256 CUs).
-SPLIT_GROUP_PARTS = {0.25: 4, 0.5: 8, 0.75: 1}
-
-
-def default_group_parts(workload, r=0.5):
-    """Partitions merged on chip per written partial in the launch configuration timed here."""
-    if workload == "split_128k" and r in SPLIT_GROUP_PARTS:
-        return SPLIT_GROUP_PARTS[r]
-    return GROUP_PARTS[workload]
-
 KERNEL_SOURCES = {
     "mla_16k": ["decode_mla.hip", "device_common.h"],
 }
@@ -389,13 +374,12 @@ def host_share_bench(args):
     # r = 0: the device pool holds every block; the same blocks in host memory (case.regions,
     # case.table) serve the host share, so any split point can be timed on one upload
     case = make_case("split_128k", "full", r=0.0)
-    G = GROUP_PARTS["split_128k"]
-    dc = DeviceCase(case, group_parts=G)
+    dc = DeviceCase(case)
     L, bs, B = int(case.ctx_lens[0]), case.block_size, case.batch
 
     def dstep(begin):
         return DecodeStep(dc.pool, dc.table, case.ctx_lens, case.part_tokens, case.num_q_heads,
-                          case.head_dim_v, tok_begin=[begin] * B, group_parts=G)
+                          case.head_dim_v, tok_begin=[begin] * B)
 
     def hshare(end):
         return HostShare(bs, case.num_kv_heads, case.head_dim_k, case.head_dim_v, case.dtype,
@@ -652,7 +636,7 @@ def sparse_bench(args):
     import torch
 
     from paged_kv_cache_mla_amd import _lib
-    from paged_kv_cache_mla_amd.api import decode_partial, merge_lse, select_blocks
+    from paged_kv_cache_mla_amd.api import choose_group_parts, decode_partial, merge_lse, select_blocks
     from paged_kv_cache_mla_amd.session import DeviceCase
     from synth import make_case
 
@@ -660,8 +644,7 @@ def sparse_bench(args):
     torch.cuda.set_device(0)
     density = args.sparse
     case = make_case("gqa_32k", "full")
-    G = GROUP_PARTS["gqa_32k"]
-    dc = DeviceCase(case, group_parts=G)
+    dc = DeviceCase(case)
     B, bs = case.batch, case.block_size
     nb = -(-int(case.ctx_lens.max()) // bs)
     k = max(1, int(round(nb * density)))
@@ -674,10 +657,10 @@ def sparse_bench(args):
     seq_sub[2] = int(case.part_tokens[0])
     bound = np.full(B, k * bs, np.int32)
     parts = -(-(k * bs) // int(case.part_tokens[0]))
-    # grouping saves partial writes but costs parallelism: with a few partitions per (sequence,
-    # KV head) the grid is too small to group (measured: 1/8 density runs 23.5 us ungrouped,
-    # 40 us with groups of 4)
-    g = args.group_parts or (1 if parts <= 16 else min(G, parts // 8))
+    # grouping saves partial writes but costs parallelism: the library's choice for the
+    # selection's bounds (with a few partitions per (sequence, KV head) it does not group)
+    g = args.group_parts or choose_group_parts(dc.pool, case.num_q_heads, bound, None,
+                                               case.part_tokens)
     max_parts = -(-parts // g)
     o_part = torch.empty((B, case.num_q_heads, max_parts, case.head_dim_v), dtype=torch.float32, device=dev)
     lse_part = torch.empty((B, case.num_q_heads, max_parts), dtype=torch.float32, device=dev)
@@ -795,7 +778,7 @@ def main():
     ap.add_argument("--workload", default="gqa_32k", choices=sorted(DESCR))
     ap.add_argument("--r", type=float, default=0.5, help="host share of split_128k")
     ap.add_argument("--group-parts", type=int, default=0,
-                    help="partitions merged on chip per written partial (default: per workload)")
+                    help="partitions merged on chip per written partial (default 0: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-share", choices=["off", "policy"], default="off",
                     help="policy: time the split workload with a native CPU share sized by the "
@@ -859,9 +842,9 @@ def main():
     log(f"[bench] generating {args.workload} (full)")
     kw = {"r": args.r} if args.workload == "split_128k" else {}
     case = make_case(args.workload, "full" if args.workload != "tiny_fp32" else "small", **kw)
-    group_parts = args.group_parts or default_group_parts(args.workload, args.r)
-    log(f"[bench] uploading (group_parts {group_parts})")
-    dc = DeviceCase(case, group_parts=group_parts)
+    dc = DeviceCase(case, group_parts=args.group_parts)
+    group_parts = dc.step.group_parts
+    log(f"[bench] uploaded (group_parts {group_parts}{', the library choice' if dc.step.auto else ''})")
     o_ext = lse_ext = None
     if case.ext_regions is not None:
         # the host share's partial enters the merge as an opaque (o, lse) input; its values do
@@ -962,6 +945,7 @@ def main():
             "block_size": case.block_size,
             "part_tokens": int(case.part_tokens[0]),
             "group_parts": group_parts,
+            "group_parts_auto": dc.step.auto,
             "kv_dtype": case.dtype,
             "device_tokens": case.device_tokens(),
             **({"r": args.r} if args.workload == "split_128k" else {}),

@@ -274,7 +274,8 @@ int32_t kvattn_partition_count(int32_t ctx_len, int32_t tok_begin, int32_t part_
  *                grid sizing; seq_dev: device int32 [3][batch] holding the same three arrays
  *                (row 1 all zeros if tok_begin is NULL), read by the kernels.
  *   max_parts    partials per sequence the o_part / lse_part arrays have room for
- *   group_parts  partitions per written partial, 1 .. KVATTN_MAX_GROUP_PARTS
+ *   group_parts  partitions per written partial, 1 .. KVATTN_MAX_GROUP_PARTS, or 0: the
+ *                library's choice for the current device, kvattn_choose_group_parts(..., 0)
  *   o_part       device fp32 [batch][num_q_heads][max_parts][Dv]
  *   lse_part     device fp32 [batch][num_q_heads][max_parts]
  *   nparts_dev   device int32 [batch]: receives the number of partials written for each
@@ -286,7 +287,7 @@ int32_t kvattn_partition_count(int32_t ctx_len, int32_t tok_begin, int32_t part_
  * Entries of o_part / lse_part for k >= nparts[b] are not written.
  * Validation (E_INVAL): null pointers, batch < 1, num_q_heads % Hkv != 0, per sequence
  * 0 <= tok_begin <= ctx_len <= max_blocks * bs, part_tokens > 0 and part_tokens % bs == 0,
- * partials per sequence <= max_parts, group_parts outside [1, KVATTN_MAX_GROUP_PARTS].
+ * partials per sequence <= max_parts, group_parts outside [0, KVATTN_MAX_GROUP_PARTS].
  * E_UNSUPPORTED: q_dtype != kv_dtype, or a head / dim combination without a kernel (GQA:
  * Dk = Dv in {64, 128, 256}, Hq / Hkv <= 16; MLA: BF16, Dk = 576, Dv = 512, Hq <= 16,
  * bs = 64); for the bf16 GQA kernel (block size >= 16) also a group needing more than 16
@@ -301,6 +302,25 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
                                     int32_t max_parts, int32_t group_parts, float* o_part,
                                     float* lse_part, int32_t* nparts_dev, int32_t* err_dev,
                                     void* hip_stream);
+
+/*
+ * The group_parts kvattn_decode_partial uses when passed 0, so that a caller can size
+ * max_parts (ceil(partitions / group_parts) per sequence) for it.  A host-only rule over the
+ * launch's work items W(g) = sum over sequences (x KV heads for GQA) of ceil(np_b / g), fitted
+ * to decode-step sweeps on MI355X ([InplaceKVCache] §5.1: any grouping of the partitions of a
+ * sequence merges to the same result, so the choice is free):
+ *   latent (MLA) kernel: the largest g in {16, 8, 4, 2} with W(g) >= num_cus, else 1;
+ *   matrix-core GQA kernel: 1 while W(1) < 8 num_cus; else the largest g in {16, 8, 4, 2}
+ *     that the kernel allows (waves per CU, LDS) with W(g) a positive multiple of num_cus, else
+ *     the largest with W(g) >= num_cus, else 1; at most 2 while the pool holds shared blocks;
+ *   VALU kernel (fp32 caches, block size < 16): 2 once W(1) >= 4 num_cus, else 1.
+ * num_cus: compute units to plan for; <= 0 = those of the current HIP device (256 if there is
+ * none).  Arguments as for kvattn_decode_partial (host arrays).  Returns g >= 1, or a negative
+ * status (E_INVAL for invalid arguments, E_UNSUPPORTED for a shape without a kernel).
+ */
+int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,
+                                  const int32_t* ctx_lens, const int32_t* tok_begin,
+                                  const int32_t* part_tokens, int32_t num_cus);
 
 /*
  * Gather probe: the loads of kvattn_decode_partial's kernel for the same arguments -- the same

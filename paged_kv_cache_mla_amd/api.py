@@ -12,7 +12,7 @@ import numpy as np
 from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
-__all__ = ["Pool", "DecodeStep", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
+__all__ = ["Pool", "DecodeStep", "choose_group_parts", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
            "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
            "ShareController", "KVStore", "VMMRange", "KvattnError", "BF16", "F32"]
 
@@ -142,6 +142,16 @@ class Pool:
     def release(self, table):
         t = np.ascontiguousarray(np.asarray(table, np.int32))
         return int(self._lib.kvattn_block_release(self.handle, _i32p(t), t.shape[0], t.shape[1]))
+
+
+def choose_group_parts(pool, num_q_heads, ctx_lens, tok_begin, part_tokens, num_cus=0):
+    """The group_parts decode_partial uses when passed 0 (num_cus 0: the current device's)."""
+    lib = _lib.load()
+    ctx, beg, part = _host_i32(ctx_lens), _host_i32(tok_begin), _host_i32(part_tokens)
+    g = lib.kvattn_choose_group_parts(pool.handle, int(ctx.shape[0]), int(num_q_heads),
+                                      _i32p(ctx), _i32p(beg), _i32p(part), int(num_cus))
+    check(g if g < 0 else 0, "choose_group_parts")
+    return int(g)
 
 
 def decode_partial(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, ctx_lens,
@@ -478,11 +488,12 @@ class DecodeStep:
     Holds the block table, the per-sequence [ctx_len, tok_begin, part_tokens] rows and the
     partial / output buffers on the device; `run` enqueues decode_partial then merge_lse on
     the current stream.  `group_parts` consecutive partitions are merged on chip into each
-    written partial (1: one partial per partition).
+    written partial (1: one partial per partition; 0, the default: the library's choice,
+    `self.group_parts` after construction, and decode_partial is called with 0).
     """
 
     def __init__(self, pool, table, ctx_lens, part_tokens, num_q_heads, head_dim_v,
-                 tok_begin=None, device="cuda", group_parts=1):
+                 tok_begin=None, device="cuda", group_parts=0):
         import torch
         self.pool = pool
         self.ctx = _host_i32(ctx_lens)
@@ -497,7 +508,9 @@ class DecodeStep:
         counts = [partition_count(int(c), int(b), int(p)) for c, b, p in zip(self.ctx, begs, self.part)]
         if min(counts) < 0:
             raise ValueError("invalid partition arguments")
-        self.group_parts = int(group_parts)
+        self.auto = int(group_parts) == 0
+        self.group_parts = (choose_group_parts(pool, num_q_heads, self.ctx, self.beg, self.part)
+                            if self.auto else int(group_parts))
         self.max_parts = max(1, max(-(-c // self.group_parts) for c in counts))
         self.table_dev = torch.from_numpy(table).to(device)
         self.seq_dev = torch.from_numpy(np.stack([self.ctx, begs, self.part]).astype(np.int32)).to(device)
@@ -517,7 +530,8 @@ class DecodeStep:
         lives."""
         self._lib = _lib.load()
         part = (_dptr(self.table_dev), self.max_blocks, _i32p(self.ctx), _i32p(self.beg),
-                _i32p(self.part), _dptr(self.seq_dev), self.max_parts, self.group_parts,
+                _i32p(self.part), _dptr(self.seq_dev), self.max_parts,
+                0 if self.auto else self.group_parts,
                 _dptr(self.o_part), _dptr(self.lse_part), _dptr(self.nparts), _dptr(self.err))
         merge = (_dptr(self.o_part), _dptr(self.lse_part), _dptr(self.nparts), self.batch,
                  self.hq, self.max_parts, self.dv)

@@ -1,5 +1,6 @@
 // C-ABI entry points of the device path: argument validation, kernel choice, launch.
 
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <string>
@@ -53,8 +54,123 @@ static kvattn_status hip_status(hipError_t e, const char* where) {
 
 enum Kind { K_MFMA, K_GENERIC, K_MLA };
 
+// Compute units of the current device (cached per device); 0 if there is no device.
+static int current_device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// The kernel for a layout and head count, before any group_parts is known; E_UNSUPPORTED
+// (with the message set) if there is none.
+static kvattn_status choose_kind(const char* what, const kvattn_layout& L, int32_t batch,
+                                 int32_t num_q_heads, const int32_t* part_tokens, Kind* out) {
+  const int hkv = L.num_kv_heads;
+  const int group = num_q_heads / hkv;
+  const int bs = L.block_size;
+  if (L.latent) {
+    if (L.kv_dtype != KVATTN_BF16 || L.head_dim_k != 576 || L.head_dim_v != 512 || bs != 64 ||
+        num_q_heads > 16)
+      return set_error(KVATTN_E_UNSUPPORTED,
+                       std::string(what) + ": latent caches need bf16, Dk 576, Dv 512, block 64, <= 16 heads");
+    *out = K_MLA;
+    return KVATTN_OK;
+  }
+  const int d = L.head_dim_k;
+  if (L.head_dim_v != d || (d != 64 && d != 128 && d != 256))
+    return set_error(KVATTN_E_UNSUPPORTED, std::string(what) + ": GQA needs Dk == Dv in {64, 128, 256}");
+  if (group > 16)
+    return set_error(KVATTN_E_UNSUPPORTED, std::string(what) + ": at most 16 query heads per KV head");
+  Kind kind = (L.kv_dtype == KVATTN_BF16 && bs >= 16 && !force_generic()) ? K_MFMA : K_GENERIC;
+  // the matrix-core kernel keeps a wave's block ids in two 64-lane registers
+  for (int b = 0; b < batch && kind == K_MFMA; ++b)
+    if (part_tokens[b] > 0 && part_tokens[b] / bs + 1 > 128) kind = K_GENERIC;
+  *out = kind;
+  return KVATTN_OK;
+}
+
+// Partitions per wave of the matrix-core kernel for a group size: two when the group splits
+// evenly, so that a long batch needs half the waves (at its register use a CU holds 8 waves of
+// head dim 128 or 256, and a second round of waves restarts the load pipeline), unless two
+// partitions would overflow the wave's 128-entry window of block ids.
+static int mfma_wave_parts(int group_parts, int32_t batch, const int32_t* part_tokens, int bs) {
+  int wave_parts = wave_parts_override();
+  if (wave_parts == 0) wave_parts = (group_parts >= 4 && group_parts % 2 == 0) ? 2 : 1;
+  if (group_parts % wave_parts != 0) wave_parts = 1;
+  for (int b = 0; b < batch; ++b)
+    if (part_tokens[b] > 0 && (int64_t)wave_parts * part_tokens[b] / bs + 1 > 128) wave_parts = 1;
+  return wave_parts;
+}
+
+// Whether a group of group_parts partitions fits the matrix-core kernel: its waves on one CU
+// and their LDS merge area within 64 KiB.
+static bool mfma_group_fits(int group_parts, int wave_parts, int group, int d) {
+  const int waves = group_parts / wave_parts;
+  if (waves <= 1) return true;
+  return waves <= gqa_mfma_max_group(d) && gqa_mfma_lds_bytes(waves, group, d) <= 65536;
+}
+
+// Work items (workgroups) of a launch at group size g: (sequences x KV heads) x partials.
+static int64_t launch_items(Kind kind, int hkv, int32_t batch, const int32_t* ctx_lens,
+                            const int32_t* tok_begin, const int32_t* part_tokens, int g) {
+  int64_t w = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int np = kvattn_partition_count(ctx_lens[b], tok_begin ? tok_begin[b] : 0, part_tokens[b]);
+    w += np > 0 ? (np + g - 1) / g : 0;
+  }
+  return w * (kind == K_MLA ? 1 : hkv);
+}
+
+// group_parts = 0: the library's choice, a rule fitted to sweeps on MI355X (decode_partial
+// plus merge, several batch x context shapes; cus = compute units).  W(g) is the launch's
+// work items at group size g.
+//  - latent (MLA) kernel, one workgroup of eight waves per CU: the largest g in {16, 8, 4, 2}
+//    with W(g) >= cus, else 1: enough groups to cover the CUs, as few partials as that allows.
+//  - matrix-core GQA kernel: 1 while W(1) < 8 cus (small launches want one-wave groups, as many
+//    as there are); otherwise the largest g in {16, 8, 4, 2} that fits the kernel with W(g) a
+//    positive multiple of cus (every round of workgroups fills the chip), else the largest
+//    with W(g) >= cus.  A pool holding shared blocks (cache-retaining loads, sequences sharing a
+//    prefix) is fastest at g <= 2.
+//  - VALU kernel (fp32 caches, small blocks): 2 once W(1) >= 4 cus, else 1.
+static int auto_group_parts(Kind kind, const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,
+                            const int32_t* ctx_lens, const int32_t* tok_begin,
+                            const int32_t* part_tokens, int cus) {
+  const kvattn_layout& L = pool->layout;
+  const int hkv = L.num_kv_heads;
+  const int group = num_q_heads / hkv;
+  if (cus <= 0) cus = 256;
+  auto W = [&](int g) { return launch_items(kind, hkv, batch, ctx_lens, tok_begin, part_tokens, g); };
+  static const int cand[4] = {16, 8, 4, 2};
+  if (kind == K_MLA) {
+    for (int g : cand)
+      if (W(g) >= cus) return g;
+    return 1;
+  }
+  if (kind == K_GENERIC) return W(1) >= 4 * (int64_t)cus ? 2 : 1;
+  if (W(1) < 8 * (int64_t)cus) return 1;
+  const int cap = pool->shared_blocks > 0 ? 2 : 16;
+  auto fits = [&](int g) {
+    return g <= cap &&
+           mfma_group_fits(g, mfma_wave_parts(g, batch, part_tokens, L.block_size), group, L.head_dim_k);
+  };
+  for (int g : cand)
+    if (fits(g) && W(g) >= cus && W(g) % cus == 0) return g;
+  for (int g : cand)
+    if (fits(g) && W(g) >= cus) return g;
+  return 1;
+}
+
 // Validation, kernel choice and kernel arguments shared by kvattn_decode_partial and
 // kvattn_gather_probe (which checks its own pointers and passes no q or partials).
+// group_parts = 0 is replaced by the library's choice for the current device.
 static kvattn_status decode_prepare(const char* what, const kvattn_pool* pool, int32_t q_dtype,
                                     int32_t batch, int32_t num_q_heads, float scale,
                                     const int32_t* table_dev, int32_t max_blocks,
@@ -67,9 +183,9 @@ static kvattn_status decode_prepare(const char* what, const kvattn_pool* pool, i
   if (batch < 1 || num_q_heads < 1 || max_blocks < 1 || max_parts < 1)
     return set_error(KVATTN_E_INVAL,
                      std::string(what) + ": batch, heads, max_blocks and max_parts must be >= 1");
-  if (group_parts < 1 || group_parts > KVATTN_MAX_GROUP_PARTS)
+  if (group_parts < 0 || group_parts > KVATTN_MAX_GROUP_PARTS)
     return set_error(KVATTN_E_INVAL,
-                     std::string(what) + ": group_parts must be in [1, KVATTN_MAX_GROUP_PARTS]");
+                     std::string(what) + ": group_parts must be in [0, KVATTN_MAX_GROUP_PARTS]");
   if (!std::isfinite(scale)) return set_error(KVATTN_E_INVAL,
                                               std::string(what) + ": scale must be finite");
   const kvattn_layout& L = pool->layout;
@@ -82,47 +198,38 @@ static kvattn_status decode_prepare(const char* what, const kvattn_pool* pool, i
                      std::string(what) + ": num_q_heads must be a multiple of num_kv_heads");
   const int group = num_q_heads / hkv;
   const int bs = L.block_size;
+  for (int b = 0; b < batch; ++b)
+    if (part_tokens[b] <= 0 || part_tokens[b] % bs != 0)
+      return set_error(KVATTN_E_INVAL,
+                       std::string(what) + ": part_tokens must be a positive multiple of block_size");
 
   // kernel choice
   Kind kind;
-  int wave_parts = 1;
-  if (L.latent) {
-    if (L.kv_dtype != KVATTN_BF16 || L.head_dim_k != 576 || L.head_dim_v != 512 || bs != 64 ||
-        num_q_heads > 16)
-      return set_error(KVATTN_E_UNSUPPORTED,
-                       std::string(what) + ": latent caches need bf16, Dk 576, Dv 512, block 64, <= 16 heads");
-    kind = K_MLA;
-  } else {
-    const int d = L.head_dim_k;
-    if (L.head_dim_v != d || (d != 64 && d != 128 && d != 256))
-      return set_error(KVATTN_E_UNSUPPORTED,
-                       std::string(what) + ": GQA needs Dk == Dv in {64, 128, 256}");
-    if (group > 16)
-      return set_error(KVATTN_E_UNSUPPORTED,
-                       std::string(what) + ": at most 16 query heads per KV head");
-    kind = (L.kv_dtype == KVATTN_BF16 && bs >= 16 && !force_generic()) ? K_MFMA : K_GENERIC;
-    // Partitions per wave of the matrix-core kernel: two when the group splits evenly, so
-    // that a long batch needs half the waves (at its register use a CU holds 8 waves of
-    // head dim 128 or 256, and a second round of waves restarts the load pipeline).
-    wave_parts = wave_parts_override();
-    if (wave_parts == 0) wave_parts = (group_parts >= 4 && group_parts % 2 == 0) ? 2 : 1;
-    if (group_parts % wave_parts != 0) wave_parts = 1;
-    // the matrix-core kernel keeps a wave's block ids in two 64-lane registers
-    for (int b = 0; b < batch && kind == K_MFMA; ++b) {
-      if (part_tokens[b] > 0 && (int64_t)wave_parts * part_tokens[b] / bs + 1 > 128) wave_parts = 1;
-      if (part_tokens[b] > 0 && part_tokens[b] / bs + 1 > 128) kind = K_GENERIC;
+  const kvattn_status ks = choose_kind(what, L, batch, num_q_heads, part_tokens, &kind);
+  if (ks != KVATTN_OK) return ks;
+  if (group_parts == 0) {
+    for (int b = 0; b < batch; ++b) {
+      const int beg = tok_begin ? tok_begin[b] : 0;
+      if (beg < 0 || beg > ctx_lens[b])
+        return set_error(KVATTN_E_INVAL, std::string(what) + ": sequence " + std::to_string(b) +
+                                             " needs 0 <= tok_begin <= ctx_len");
     }
-    if (kind == K_MFMA && group_parts / wave_parts > 1) {
+    group_parts = auto_group_parts(kind, pool, batch, num_q_heads, ctx_lens, tok_begin,
+                                   part_tokens, current_device_cus());
+  }
+  int wave_parts = 1;
+  if (kind == K_MFMA) {
+    wave_parts = mfma_wave_parts(group_parts, batch, part_tokens, bs);
+    if (!mfma_group_fits(group_parts, wave_parts, group, L.head_dim_k)) {
       // waves of a group merge their partials in LDS
-      const int waves = group_parts / wave_parts;
-      if (waves > gqa_mfma_max_group(d))
+      const int d = L.head_dim_k;
+      if (group_parts / wave_parts > gqa_mfma_max_group(d))
         return set_error(KVATTN_E_UNSUPPORTED, std::string(what) + ": group_parts above " +
                                                    std::to_string(gqa_mfma_max_group(d)) +
                                                    " for head dim " + std::to_string(d));
-      if (gqa_mfma_lds_bytes(waves, group, d) > 65536)
-        return set_error(KVATTN_E_UNSUPPORTED,
-                         std::string(what) + ": group_parts x heads per KV head x (head dim + 1) x 4 "
-                         "bytes exceeds 64 KiB");
+      return set_error(KVATTN_E_UNSUPPORTED,
+                       std::string(what) + ": group_parts x heads per KV head x (head dim + 1) x 4 "
+                       "bytes exceeds 64 KiB");
     }
   }
 
@@ -216,6 +323,29 @@ kvattn_status kvattn_decode_partial(const kvattn_pool* pool, const void* q, int3
     default: e = launch_gqa_generic(a, L.head_dim_k, L.kv_dtype == KVATTN_F32, grid, st); break;
   }
   return hip_status(e, "decode_partial launch");
+}
+
+int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,
+                                  const int32_t* ctx_lens, const int32_t* tok_begin,
+                                  const int32_t* part_tokens, int32_t num_cus) {
+  clear_error();
+  if (!pool || !ctx_lens || !part_tokens)
+    return set_error(KVATTN_E_INVAL, "choose_group_parts: null argument");
+  if (batch < 1 || num_q_heads < 1 || num_q_heads % pool->layout.num_kv_heads != 0)
+    return set_error(KVATTN_E_INVAL, "choose_group_parts: bad batch or head count");
+  for (int b = 0; b < batch; ++b) {
+    const int beg = tok_begin ? tok_begin[b] : 0;
+    if (kvattn_partition_count(ctx_lens[b], beg, part_tokens[b]) < 0 ||
+        part_tokens[b] % pool->layout.block_size != 0)
+      return set_error(KVATTN_E_INVAL, "choose_group_parts: sequence " + std::to_string(b) +
+                                           " has invalid partition arguments");
+  }
+  Kind kind;
+  const kvattn_status ks =
+      choose_kind("choose_group_parts", pool->layout, batch, num_q_heads, part_tokens, &kind);
+  if (ks != KVATTN_OK) return ks;
+  return auto_group_parts(kind, pool, batch, num_q_heads, ctx_lens, tok_begin, part_tokens,
+                          num_cus > 0 ? num_cus : current_device_cus());
 }
 
 kvattn_status kvattn_gather_probe(const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,

@@ -220,7 +220,7 @@ def test_decode_partial_validation_without_gpu(lib):
     assert _decode_call(lib, pool, max_parts=1) == _lib.E_INVAL             # 2 partitions needed
     assert _decode_call(lib, pool, scale=float("nan")) == _lib.E_INVAL
     assert _decode_call(lib, pool, batch=0) == _lib.E_INVAL
-    assert _decode_call(lib, pool, group_parts=0) == _lib.E_INVAL
+    assert _decode_call(lib, pool, group_parts=-1) == _lib.E_INVAL
     assert _decode_call(lib, pool, group_parts=17) == _lib.E_INVAL          # > KVATTN_MAX_GROUP_PARTS
     p128 = _pool(8, 0, bs=16, hkv=2, d=128)
     assert _decode_call(lib, p128, group_parts=9) == _lib.E_UNSUPPORTED     # > 8 waves at d 128
@@ -251,7 +251,7 @@ def test_gather_probe_validation_without_gpu(lib):
     assert call(ok, xsum=None) == _lib.E_INVAL
     assert call(ok, part=(32, 24)) == _lib.E_INVAL                          # not a block multiple
     assert call(ok, hq=7) == _lib.E_INVAL
-    assert call(ok, g=0) == _lib.E_INVAL
+    assert call(ok, g=-1) == _lib.E_INVAL
     assert call(_pool(8, 0, bs=16, hkv=2, d=128, dtype="f32")) == _lib.E_UNSUPPORTED
     assert call(_pool(8, 0, bs=32, hkv=2, d=128), ctx=(64, 50)) == _lib.E_UNSUPPORTED
     assert "block size 16" in lib.kvattn_last_error().decode()
@@ -322,3 +322,42 @@ def test_select_blocks_validation_without_gpu(lib):
     assert call(bs=24) == _lib.E_INVAL
     assert call(bs=512) == _lib.E_INVAL
     assert call(b=0) == _lib.E_INVAL
+
+
+# ---------------------------------------------------------------- the library's group_parts
+def _choose(pool, hq, lens, part, beg=None, cus=256):
+    from paged_kv_cache_mla_amd.api import choose_group_parts
+    return choose_group_parts(pool, hq, lens, beg, [part] * len(lens), cus)
+
+
+def test_choose_group_parts_reproduces_the_measured_sweeps():
+    """group_parts = 0 picks, for 256 CUs, the best (or within 3% of the best) entry of every
+    row of the decode-step sweeps measured on MI355X."""
+    gqa = _pool(1, 0, bs=16, hkv=4, d=128)            # Qwen3-30B-A3B layer: 32 q / 4 KV heads
+    for b, L, want in [(1, 32768, 1), (4, 32768, 1), (8, 32768, 8), (16, 8192, 1),
+                       (16, 32768, 16), (4, 131072, 16), (64, 8192, 16)]:
+        assert _choose(gqa, 32, [L] * b, 512) == want, (b, L)
+    mix = _pool(1, 0, bs=16, hkv=8, d=128)            # Mixtral split layer, 1024-token partitions
+    for r, want in [(0.25, 4), (0.5, 8), (0.75, 1)]:
+        beg = int(r * 131072)
+        assert _choose(mix, 32, [131072] * 4, 1024, [beg] * 4) == want, r
+    mla = Pool(64, 1, 576, 512, "bf16", True, [(FAKE, 1)])
+    for b, L, want in [(1, 65536, 1), (8, 16384, 1), (16, 16384, 2), (32, 16384, 4),
+                       (64, 4096, 2), (64, 16384, 8), (128, 2048, 2)]:
+        assert _choose(mla, 16, [L] * b, 512) == want, (b, L)
+    f32 = _pool(1, 0, bs=16, hkv=4, d=128, dtype="f32")
+    assert _choose(f32, 32, [8192] * 16, 512) == 2
+    assert _choose(_pool(1, 0, bs=16, hkv=1, d=64, dtype="f32"), 4, [100, 257], 64) == 1
+
+
+def test_choose_group_parts_respects_kernel_limits_and_shared_pools():
+    d256 = _pool(200, 0, bs=16, hkv=2, d=256)          # 16 q / 2 KV heads, head dim 256
+    lens = [16 * int(x) for x in np.random.default_rng(1).integers(512, 4097, 64)]
+    g = _choose(d256, 16, lens, 512)
+    assert g in (2, 4, 8)                               # 16 would need more than 64 KiB of LDS
+    st, table, _ = d256.block_table([64, 64], 4, share_src=[-1, 0], share_nblocks=[0, 3])
+    assert st == _lib.OK and d256.shared_blocks > 0
+    assert _choose(d256, 16, lens, 512) <= 2            # shared blocks: cache-retaining loads
+    with pytest.raises(Exception):
+        _choose(d256, 15, lens, 512)                    # not a multiple of the KV heads
+    assert _choose(_pool(1, 0, bs=16, hkv=2, d=128), 16, [64], 512, cus=0) >= 1  # no device

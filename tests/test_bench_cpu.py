@@ -36,13 +36,6 @@ def test_kernel_hash_covers_each_workload_sources():
     assert all(len(h) == 16 for h in hashes.values())
 
 
-def test_default_group_parts():
-    assert bench.default_group_parts("gqa_32k") == 16
-    assert bench.default_group_parts("mla_16k") == 4
-    assert [bench.default_group_parts("split_128k", r) for r in (0.25, 0.5, 0.75)] == [4, 8, 1]
-    assert bench.default_group_parts("split_128k", 0.3) == bench.GROUP_PARTS["split_128k"]
-
-
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120, cwd=ROOT)

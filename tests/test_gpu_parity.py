@@ -559,15 +559,16 @@ FULL = [("gqa_32k", {}), ("mla_16k", {}), ("split_128k", {"r": 0.25}), ("split_1
 
 @pytest.mark.parametrize("name,kw", FULL, ids=[f"{n}-{k.get('r', '')}" for n, k in FULL])
 def test_full_size_every_sequence(name, kw):
-    """Full-size workloads in the launch configuration bench.py times, every sequence and
-    head against the oracle (the split layer's host share from the oracle too)."""
-    from bench import default_group_parts
-    group_parts = default_group_parts(name, kw.get("r", 0.5))
-    _say(f"[full] generating {name} {kw} group_parts={group_parts}")
+    """Full-size workloads in the launch configuration bench.py times (group_parts chosen by
+    the library), every sequence and head against the oracle (the split layer's host share
+    from the oracle too)."""
+    _say(f"[full] generating {name} {kw}")
     case = make_case(name, "full", **kw)
     ext = oc.external_partial(case) if case.ext_regions is not None else None
     _say(f"[full] running {name} B={case.batch} device tokens={case.device_tokens()}")
-    dc, o, lse = _run(case, ext, group_parts)
+    dc, o, lse = _run(case, ext, 0)
+    group_parts = dc.step.group_parts
+    _say(f"[full] {name} ran with group_parts {group_parts} (library choice)")
     assert int(dc.step.err.item()) == 0
     nparts = dc.step.nparts.cpu().numpy()
     for b in range(case.batch):
