@@ -238,7 +238,8 @@ def summarize_counters(workload, dirs, out_path, commands):
         if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg and avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"] > 0:
             hit = f"{100 * avg['TCC_HIT_sum'] / (avg['TCC_HIT_sum'] + avg['TCC_MISS_sum']):.1f}%"
         lines.append(f"| {_short(k)} | {n} | " + " | ".join(cells) + f" | {hit} |")
-    lines.append("")
+    lines += ["", "Source these readings were taken on (void once the kernel source changes):", "",
+              "<!-- values -->", f"kernel_hash: {kernel_hash(workload)}", "<!-- values -->", ""]
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines))
     return out_path
@@ -338,6 +339,43 @@ def cpu_baseline(case, budget_s=10.0):
             "host_cpus": cores, "kind": "oracle",
             "sample": f"{n_seq} sequence passes over the {case.batch} sequences (all heads), "
                       f"{done_tokens} tokens, {nbytes} KV bytes, float64 numpy, {dt:.1f} s"}
+
+
+def oracle_host_share(case):
+    """cpu_baseline leg of the split workload: the host share [0, tok_begin) of every sequence,
+    computed by the float64 oracle on this host's cores, timed.  Its (o, lse) is the external
+    partial the timed steps merge."""
+    import numpy as np
+    import oracle
+    lay = oracle.Layout(case.block_size, case.num_kv_heads, case.head_dim_k, case.head_dim_v,
+                        case.dtype, case.latent)
+    qf = oracle.bf16_bits_to_f64(case.q) if case.dtype == "bf16" else case.q.astype(np.float64)
+    o = np.zeros((case.batch, case.num_q_heads, case.head_dim_v))
+    lse = np.full((case.batch, case.num_q_heads), -np.inf)
+    t0 = time.perf_counter()
+    tokens = 0
+    for b in range(case.batch):
+        beg = int(case.tok_begin[b])
+        k, v = oracle.gather_sequence(lay, case.ext_regions, case.ext_region_blocks,
+                                      case.ext_table[b], 0, beg)
+        o[b], lse[b] = oracle.attend(qf[b], k, v, case.scale)
+        tokens += beg
+    return o, lse, time.perf_counter() - t0, tokens
+
+
+def kv_token_slots(case):
+    """(logical, unique) K/V token slots one step reads: every sequence's tokens
+    [tok_begin, L), and the distinct (physical block, slot) pairs among them -- a block shared
+    by several sequences (prefix sharing) holds its tokens once."""
+    import numpy as np
+    bs = case.block_size
+    keys = []
+    for b in range(case.batch):
+        beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
+        t = np.arange(beg, int(case.ctx_lens[b]), dtype=np.int64)
+        keys.append(case.table[b][t // bs].astype(np.int64) * bs + t % bs)
+    allk = np.concatenate(keys) if keys else np.zeros(0, np.int64)
+    return int(allk.size), int(np.unique(allk).size)
 
 
 def _time_steps(torch, fn, steps, warmup):
@@ -846,14 +884,24 @@ def main():
     group_parts = dc.step.group_parts
     log(f"[bench] uploaded (group_parts {group_parts}{', the library choice' if dc.step.auto else ''})")
     o_ext = lse_ext = None
+    cpu_share = None
     if case.ext_regions is not None:
-        # the host share's partial enters the merge as an opaque (o, lse) input; its values do
-        # not change the work, so a seeded stand-in is used here (tests use the oracle's)
-        rng = np.random.default_rng(0)
-        o_ext = torch.from_numpy(rng.standard_normal((case.batch, case.num_q_heads, case.head_dim_v))
-                                 .astype(np.float32)).cuda()
-        lse_ext = torch.from_numpy(rng.standard_normal((case.batch, case.num_q_heads))
-                                   .astype(np.float32)).cuda()
+        if not args.no_cpu_baseline:
+            log("[bench] the host share [0, r L) of every sequence, by the oracle on the host")
+            o_np, l_np, secs, toks = oracle_host_share(case)
+            cpu_share = {"kind": "oracle", "tokens": toks, "seconds": round(secs, 3),
+                         "kv_bytes": toks * case.kv_bytes_per_token(),
+                         "GBps": round(toks * case.kv_bytes_per_token() / secs / 1e9, 3),
+                         "cores": len(os.sched_getaffinity(0)),
+                         "note": "the host share's partial merged by the timed steps"}
+        else:
+            # without the oracle leg the partial's values are a seeded stand-in: they do not
+            # change the work of the step
+            rng = np.random.default_rng(0)
+            o_np = rng.standard_normal((case.batch, case.num_q_heads, case.head_dim_v))
+            l_np = rng.standard_normal((case.batch, case.num_q_heads))
+        o_ext = torch.from_numpy(o_np.astype(np.float32)).cuda()
+        lse_ext = torch.from_numpy(l_np.astype(np.float32)).cuda()
 
     for _ in range(args.warmup):
         dc.run(o_ext, lse_ext)
@@ -867,7 +915,7 @@ def main():
     # which adds ~3 us per event to the step on MI355X).
     timer = HipTimer()
     sp = torch.cuda.current_stream().cuda_stream
-    evs = [(timer.event(), timer.event()) for _ in range(args.steps)]
+    evs = [(timer.event(), timer.event(), timer.event()) for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -876,9 +924,11 @@ def main():
         dc.partial()
         timer.record(evs[i][1], sp)
         dc.merge(o_ext, lse_ext)
+        timer.record(evs[i][2], sp)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_part = [timer.elapsed_ms(a, b) for a, b in evs]
+    t_part = [timer.elapsed_ms(a, b) for a, b, _ in evs]
+    t_steps_ev = [timer.elapsed_ms(a, c) for a, _, c in evs]
     ms_step = wall * 1e3 / args.steps
 
     # The access pattern's own ceiling, outside the timed region: the gather probe issues the
@@ -898,14 +948,22 @@ def main():
     except _lib.KvattnError as e:  # layouts the probe does not serve (fp32, other block sizes)
         log(f"[bench] no gather probe for this layout: {e}")
 
-    kv_bytes = case.device_tokens() * case.kv_bytes_per_token()
-    step = dc.step
+    bpt = case.kv_bytes_per_token()
+    slots_logical, slots_unique = kv_token_slots(case)
+    kv_bytes = slots_logical * bpt          # every sequence's K/V range, as it attends to it
+    kv_unique = slots_unique * bpt          # what must cross HBM: shared blocks once
     n_parts_total = int(dc.step.nparts.sum().item())
     q_bytes = case.q.nbytes
     table_bytes = int(sum(-(-(int(c) - (0 if case.tok_begin is None else int(case.tok_begin[b]))) //
                             case.block_size) for b, c in enumerate(case.ctx_lens))) * 4
     part_bytes = n_parts_total * case.num_q_heads * (case.head_dim_v + 1) * 4
-    kernel_bytes = kv_bytes + q_bytes + table_bytes + part_bytes
+    out_bytes = case.batch * case.num_q_heads * (case.head_dim_v + 1) * 4
+    ext_bytes = out_bytes if o_ext is not None else 0
+    # decode_partial: K/V once, q, table, partials written; the step adds the merge's reads of
+    # the partials (and of the external partial) and its output
+    kernel_bytes = kv_unique + q_bytes + table_bytes + part_bytes
+    alg_bytes = kernel_bytes + part_bytes + ext_bytes + out_bytes
+    flops = slots_logical * case.num_q_heads * 2 * (case.head_dim_k + case.head_dim_v)
     avg_part_ms = float(np.mean(t_part))
     achieved = kernel_bytes / (avg_part_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
@@ -932,7 +990,11 @@ def main():
         "t_partial_us": round(avg_part_ms * 1e3, 2),
         # the rest of the step: the merge kernel plus the launch gaps around it
         "t_merge_and_gaps_us": round((ms_step - avg_part_ms) * 1e3, 2),
+        "t_step_median_us": round(float(np.median(t_steps_ev)) * 1e3, 2),
+        "t_partial_median_us": round(float(np.median(t_part)) * 1e3, 2),
         "kv_bytes": kv_bytes,
+        "alg_bytes": alg_bytes,
+        "flops": flops,
         "copy_GBps": round(copy_gbps, 1),
         "config": {
             "workload": args.workload + ": " + DESCR[args.workload],
@@ -962,6 +1024,22 @@ def main():
             "avg_launch_us": round(avg_part_ms * 1e3, 2),
         },
     }
+    if slots_unique != slots_logical:
+        traffic = out["roofline"]["traffic"]
+        out["shared_kv"] = {
+            "kv_bytes_logical": kv_bytes,
+            "kv_bytes_unique": kv_unique,
+            "hbm_bytes_counter": traffic,
+            "token_slots_logical": slots_logical,
+            "token_slots_unique": slots_unique,
+            "unique_fraction": round(slots_unique / slots_logical, 4),
+            "unique_KV_GBps": round(kv_unique / (ms_step * 1e-3) / 1e9, 1),
+            "note": "value counts every sequence's K/V (logical); the roofline counts each "
+                    "shared block once (unique); hbm_bytes_counter is the rocprofv3 FETCH+WRITE "
+                    "of decode_partial (null when taken on other kernel source)",
+        }
+    if cpu_share is not None:
+        out["cpu_share"] = cpu_share
     if gather is not None:
         out["gather_ceiling"] = {
             "kernel": "gather probe: the decode kernel's loads, no arithmetic",

@@ -7,7 +7,11 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvattn.so")
+# KVATTN_LIB selects another build of the same sources (the sanitized host builds of
+# build.py --sanitize); relative paths are taken from the repository root
+LIB_PATH = os.environ.get("KVATTN_LIB") or os.path.join(_HERE, "libkvattn.so")
+if not os.path.isabs(LIB_PATH):
+    LIB_PATH = os.path.join(os.path.dirname(_HERE), LIB_PATH)
 
 OK = 0
 E_INVAL = -1

@@ -81,3 +81,33 @@ def test_profile_summary_picks_the_decode_kernel_not_the_probe(tmp_path):
     assert abs(float(vals["fetch_factor"]) - 2.0) < 1e-9 and abs(float(vals["write_factor"]) - 1.0) < 1e-9
     assert int(vals["hbm_bytes_per_launch"]) == round(524800.0 * 1024 * 2 + 1056.0 * 1024)
     assert vals["kernel_hash"] == bench.kernel_hash("gqa_32k")
+
+
+def test_counter_summary_records_the_kernel_hash(tmp_path):
+    """Counter summaries carry the code hash of the sources they were taken on, like the
+    trace summaries, so a reading can be tied to (or voided by) the current kernel."""
+    dec = "kvattn::mla_decode_kernel<false>(kvattn::DecodeArgs, unsigned int*)"
+    d = tmp_path / "pmc"
+    d.mkdir()
+    _write_csv(d / "run_counter_collection.csv",
+               ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"],
+               [[dec, 256, "MfmaUtil", 7.5], [dec, 256, "MfmaUtil", 6.5]])
+    out = tmp_path / "counters.md"
+    bench.summarize_counters("mla_16k", [str(d)], str(out), ["cmd"])
+    text = out.read_text()
+    assert "| 2 | 7 |" in text            # two dispatches, their average
+    assert bench.read_profile_values(str(out))["kernel_hash"] == bench.kernel_hash("mla_16k")
+
+
+def test_sanitized_build_instruments_host_code_only():
+    """The sanitizer builds put -Xarch_host before every -fsanitize= (device code is compiled
+    as usual), write to their own directory, and name the runtime to preload."""
+    from paged_kv_cache_mla_amd import build as B
+    flags = B._sanitize_flags(("address", "undefined"))
+    for i, f in enumerate(flags):
+        if f.startswith("-fsanitize="):
+            assert flags[i - 1] == "-Xarch_host"
+    assert B.sanitized_path(("thread",)) != B.OUT
+    cmd = B.sanitizer_test_command(("thread",))
+    assert "libclang_rt.tsan" in cmd and "KVATTN_LIB=" in cmd and "halt_on_error=1" in cmd
+    assert "libclang_rt.asan" in B.sanitizer_test_command(("address", "undefined"))
