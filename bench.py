@@ -915,7 +915,7 @@ def main():
     # which adds ~3 us per event to the step on MI355X).
     timer = HipTimer()
     sp = torch.cuda.current_stream().cuda_stream
-    evs = [(timer.event(), timer.event(), timer.event()) for _ in range(args.steps)]
+    evs = [(timer.event(), timer.event()) for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -924,17 +924,20 @@ def main():
         dc.partial()
         timer.record(evs[i][1], sp)
         dc.merge(o_ext, lse_ext)
-        timer.record(evs[i][2], sp)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_part = [timer.elapsed_ms(a, b) for a, b, _ in evs]
-    t_steps_ev = [timer.elapsed_ms(a, c) for a, _, c in evs]
+    t_part = [timer.elapsed_ms(a, b) for a, b in evs]
+    # a step's device time: from one decode_partial's start to the next one's (the steps are
+    # enqueued back to back, so this spans the partial, the merge and the gaps between them)
+    t_steps_ev = [timer.elapsed_ms(evs[i][0], evs[i + 1][0]) for i in range(args.steps - 1)] or [0.0]
     ms_step = wall * 1e3 / args.steps
 
     # The access pattern's own ceiling, outside the timed region: the gather probe issues the
     # decode kernel's loads (same grid, waves, table lookups and cache hints) with no arithmetic.
     gather = None
     try:
+        if dc.step.plan is not None:
+            raise NotImplementedError("the gather probe mirrors the per-sequence launch, not a plan")
         xsum = torch.zeros(case.batch * case.num_kv_heads, dtype=torch.int32, device="cuda")
         for _ in range(2):
             dc.step.probe(xsum)
@@ -945,7 +948,7 @@ def main():
             timer.record(pevs[i][1], sp)
         torch.cuda.synchronize()
         gather = float(np.mean([timer.elapsed_ms(a, b) for a, b in pevs]))
-    except _lib.KvattnError as e:  # layouts the probe does not serve (fp32, other block sizes)
+    except (_lib.KvattnError, NotImplementedError) as e:  # layouts the probe does not serve
         log(f"[bench] no gather probe for this layout: {e}")
 
     bpt = case.kv_bytes_per_token()

@@ -323,6 +323,69 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
                                   const int32_t* part_tokens, int32_t num_cus);
 
 /*
+ * ---- Decode over a work plan: sequences holding the same blocks share one pass ----
+ *
+ * Prefix caching hands the same physical blocks to several sequences ([VAMP] §II-A: cached
+ * prefixes are reused across turns and requests; [CrossPool] §3.1: the paged interface makes
+ * them ordinary table entries).  Where two sequences have the same token range in the same
+ * blocks, the range's keys and values are the same, so one pass over them serves both; each
+ * sequence still gets its own partial of the range, merged like any other ([InplaceKVCache]
+ * §5.1: partials over a partition of the tokens merge exactly).
+ *
+ * kvattn_decode_plan (host only) reads the host copy of the tables.  Block position i of
+ * sequence b (its tokens [max(tok_begin, i bs), min(ctx_len, (i + 1) bs))) is shared with
+ * every sequence whose position i holds the same block id with the same token extent; the
+ * sharers of a position form its set.  Each maximal run of positions of a sequence with the
+ * same set (an invalid id: a set of its own sequence) is taken once, from the set's lowest
+ * sequence, and cut into pieces of at most span_parts * part_tokens tokens (span_parts 0: as
+ * many whole partitions as a wave's window of 127 block ids holds); a piece becomes wave
+ * items of up to 16 / (Hq / Hkv) of its sequences each, and the items of one piece run in one
+ * workgroup of four waves where they fit.  Every sequence's range [tok_begin, ctx_len) is
+ * thus covered exactly once by the items it belongs to; its partials are written in the
+ * order of their first tokens, slots 0 .. nparts[b] - 1.  The plan is an int32 array:
+ *   header[8] = {magic, batch, n_groups, 4 n_groups, member entries M, max_parts,
+ *                Hq / Hkv, sequences per wave item}, nparts[batch],
+ *   items[4 n_groups][6] = {table row, first token, end token, sequences (0: idle wave),
+ *                           first member entry, shared flag},
+ *   members[M][2] = {sequence, partial slot}.
+ *   table        host [batch][max_blocks] int32 (the device copy's contents)
+ *   plan         host int32 [plan_cap], or NULL to query the size only
+ *   plan_len     receives the plan's length in int32 entries
+ *   n_groups     receives the workgroups of the plan (the grid of kvattn_decode_partial_plan)
+ *   max_parts    receives the most partials any sequence gets (size o_part / lse_part for it)
+ * Errors: E_INVAL (null pointers, sizes, per-sequence values as for kvattn_decode_partial,
+ * plan_cap < plan_len), E_UNSUPPORTED (not a bf16 per-head cache with block size >= 16 and
+ * head dim 64, 128 or 256; more than 16 query heads per KV head; span_parts * part_tokens
+ * spanning more than 127 blocks).
+ *
+ * kvattn_decode_partial_plan runs a plan (uploaded by the caller to plan_dev) on the
+ * device: for every item and KV head, the attention of its sequences' query heads over its
+ * token range, read once through the table row it names; sequence b's partial of item k goes
+ * to o_part[b][h][slot] / lse_part[b][h][slot] (same formulas as kvattn_decode_partial) and
+ * nparts_dev[b] receives the plan's count, so kvattn_merge_lse completes the step.  Items of a
+ * shared range are read with cache-retaining loads, the others with non-temporal loads.
+ *   q, q_dtype, batch, num_q_heads, scale, table_dev, max_blocks, o_part, lse_part, err_dev:
+ *                as for kvattn_decode_partial (max_parts >= the plan's max_parts)
+ *   plan_dev     device int32 copy of the plan (all plan_len entries); n_groups its workgroups
+ * A plan whose header disagrees with the arguments, or an item outside them, sets
+ * KVATTN_ERR_BAD_SEQ in *err_dev and is not run; invalid block ids set KVATTN_ERR_BAD_BLOCK and
+ * contribute nothing.  Errors: E_INVAL (null pointers, misalignment, sizes), E_UNSUPPORTED
+ * (as for kvattn_decode_plan, or q_dtype != kv_dtype), E_HIP.
+ */
+kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,
+                                 const int32_t* table, int32_t max_blocks,
+                                 const int32_t* ctx_lens, const int32_t* tok_begin,
+                                 const int32_t* part_tokens, int32_t span_parts, int32_t* plan,
+                                 int64_t plan_cap, int64_t* plan_len, int32_t* n_groups,
+                                 int32_t* max_parts);
+kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q, int32_t q_dtype,
+                                         int32_t batch, int32_t num_q_heads, float scale,
+                                         const int32_t* table_dev, int32_t max_blocks,
+                                         const int32_t* plan_dev, int32_t n_groups,
+                                         int32_t max_parts, float* o_part, float* lse_part,
+                                         int32_t* nparts_dev, int32_t* err_dev, void* hip_stream);
+
+/*
  * Gather probe: the loads of kvattn_decode_partial's kernel for the same arguments -- the same
  * grid, waves, block-table lookups, load widths, cache hints and order -- with no arithmetic.
  * It measures the access pattern's own bandwidth ceiling on this device, which bounds what

@@ -65,6 +65,10 @@ _PI64 = ctypes.POINTER(ctypes.c_int64)
 _SIGNATURES = {
     "kvattn_block_bytes": (_I64, [ctypes.POINTER(Layout)]),
     "kvattn_choose_group_parts": (_I32, [_P, _I32, _I32, _PI32, _PI32, _PI32, _I32]),
+    "kvattn_decode_plan": (_I32, [_P, _I32, _I32, _PI32, _I32, _PI32, _PI32, _PI32, _I32, _PI32,
+                                   _I64, _PI64, _PI32, _PI32]),
+    "kvattn_decode_partial_plan": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32, _P,
+                                           _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_pool_alloc": (_I32, [ctypes.POINTER(Layout), ctypes.POINTER(Region), _I32,
                                  ctypes.c_uint64, ctypes.POINTER(_P)]),
     "kvattn_pool_free": (None, [_P]),

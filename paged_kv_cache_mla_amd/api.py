@@ -12,7 +12,7 @@ import numpy as np
 from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
-__all__ = ["Pool", "DecodeStep", "choose_group_parts", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
+__all__ = ["Pool", "DecodeStep", "choose_group_parts", "decode_plan", "decode_partial_plan", "plan_supported", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
            "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
            "ShareController", "KVStore", "VMMRange", "KvattnError", "BF16", "F32"]
 
@@ -152,6 +152,44 @@ def choose_group_parts(pool, num_q_heads, ctx_lens, tok_begin, part_tokens, num_
                                       _i32p(ctx), _i32p(beg), _i32p(part), int(num_cus))
     check(g if g < 0 else 0, "choose_group_parts")
     return int(g)
+
+
+def plan_supported(pool, num_q_heads):
+    """Whether kvattn_decode_plan serves this pool and head count (bf16 per-head cache, block
+    size >= 16, head dim 64 / 128 / 256, at most 16 query heads per KV head)."""
+    L = pool.layout
+    return (not L.latent and L.kv_dtype == BF16 and L.block_size >= 16 and
+            L.head_dim_k == L.head_dim_v and L.head_dim_k in (64, 128, 256) and
+            num_q_heads % L.num_kv_heads == 0 and num_q_heads // L.num_kv_heads <= 16)
+
+
+def decode_plan(pool, num_q_heads, table, ctx_lens, tok_begin, part_tokens, span_parts=0):
+    """kvattn_decode_plan on host arrays: (plan int32 array, n_groups, max_parts)."""
+    lib = _lib.load()
+    t = np.ascontiguousarray(np.asarray(table, np.int32))
+    ctx, beg, part = _host_i32(ctx_lens), _host_i32(tok_begin), _host_i32(part_tokens)
+    n = ctypes.c_int64()
+    ng, mp = ctypes.c_int32(), ctypes.c_int32()
+    args = (pool.handle, int(ctx.shape[0]), int(num_q_heads), _i32p(t), int(t.shape[1]), _i32p(ctx),
+            _i32p(beg), _i32p(part), int(span_parts))
+    check(lib.kvattn_decode_plan(*args, None, 0, ctypes.byref(n), ctypes.byref(ng),
+                                 ctypes.byref(mp)), "decode_plan (size)")
+    plan = np.zeros(n.value, np.int32)
+    check(lib.kvattn_decode_plan(*args, _i32p(plan), plan.size, ctypes.byref(n), ctypes.byref(ng),
+                                 ctypes.byref(mp)), "decode_plan")
+    return plan, int(ng.value), int(mp.value)
+
+
+def decode_partial_plan(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, plan_dev,
+                        n_groups, max_parts, o_part, lse_part, nparts, err=None, stream=None):
+    lib = _lib.load()
+    bsz = int(o_part.shape[0])
+    check(lib.kvattn_decode_partial_plan(pool.handle, _dptr(q), int(q_dtype), bsz,
+                                         int(num_q_heads), ctypes.c_float(scale), _dptr(table_dev),
+                                         int(max_blocks), _dptr(plan_dev), int(n_groups),
+                                         int(max_parts), _dptr(o_part), _dptr(lse_part),
+                                         _dptr(nparts), _dptr(err), _stream(stream)),
+          "decode_partial_plan")
 
 
 def decode_partial(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, ctx_lens,
@@ -490,10 +528,15 @@ class DecodeStep:
     the current stream.  `group_parts` consecutive partitions are merged on chip into each
     written partial (1: one partial per partition; 0, the default: the library's choice,
     `self.group_parts` after construction, and decode_partial is called with 0).
+
+    `plan`: run the step from a work plan (kvattn_decode_plan / kvattn_decode_partial_plan), so
+    that sequences holding the same blocks share one pass over them.  None (the default) takes
+    the plan when group_parts is the library's choice, the pool holds shared blocks and the
+    layout has a plan kernel.  `span_parts` is the plan's partitions per wave item (0: auto).
     """
 
     def __init__(self, pool, table, ctx_lens, part_tokens, num_q_heads, head_dim_v,
-                 tok_begin=None, device="cuda", group_parts=0):
+                 tok_begin=None, device="cuda", group_parts=0, plan=None, span_parts=0):
         import torch
         self.pool = pool
         self.ctx = _host_i32(ctx_lens)
@@ -512,6 +555,13 @@ class DecodeStep:
         self.group_parts = (choose_group_parts(pool, num_q_heads, self.ctx, self.beg, self.part)
                             if self.auto else int(group_parts))
         self.max_parts = max(1, max(-(-c // self.group_parts) for c in counts))
+        if plan is None:
+            plan = self.auto and pool.shared_blocks > 0 and plan_supported(pool, num_q_heads)
+        self.plan = None
+        if plan:
+            self.plan, self.n_groups, self.max_parts = decode_plan(
+                pool, num_q_heads, table, self.ctx, self.beg, self.part, span_parts)
+            self.plan_dev = torch.from_numpy(self.plan).to(device)
         self.table_dev = torch.from_numpy(table).to(device)
         self.seq_dev = torch.from_numpy(np.stack([self.ctx, begs, self.part]).astype(np.int32)).to(device)
         f32 = torch.float32
@@ -536,17 +586,23 @@ class DecodeStep:
         merge = (_dptr(self.o_part), _dptr(self.lse_part), _dptr(self.nparts), self.batch,
                  self.hq, self.max_parts, self.dv)
         out = (_dptr(self.o_out), _dptr(self.lse_out))
+        if self.plan is not None:
+            part = (_dptr(self.table_dev), self.max_blocks, _dptr(self.plan_dev), self.n_groups,
+                    self.max_parts, _dptr(self.o_part), _dptr(self.lse_part), _dptr(self.nparts),
+                    _dptr(self.err))
         keep = (self.table_dev, self.seq_dev, self.o_part, self.lse_part, self.nparts, self.err,
-                self.o_out, self.lse_out, self.ctx, self.beg, self.part)
+                self.o_out, self.lse_out, self.ctx, self.beg, self.part,
+                getattr(self, "plan_dev", None))
         self._fixed = (part, merge, out, keep)
 
     def partial(self, q, q_dtype, scale, stream=None):
         if self._fixed is None:
             self._marshal()
-        st = self._lib.kvattn_decode_partial(self.pool.handle, _dptr(q), int(q_dtype), self.batch,
-                                             self.hq, ctypes.c_float(scale), *self._fixed[0],
-                                             _stream(stream))
-        check(st, "decode_partial")
+        fn = (self._lib.kvattn_decode_partial if self.plan is None
+              else self._lib.kvattn_decode_partial_plan)
+        st = fn(self.pool.handle, _dptr(q), int(q_dtype), self.batch, self.hq,
+                ctypes.c_float(scale), *self._fixed[0], _stream(stream))
+        check(st, "decode_partial" if self.plan is None else "decode_partial_plan")
 
     def probe(self, xsum, stream=None):
         """The gather probe over this step's ranges, in its launch configuration."""

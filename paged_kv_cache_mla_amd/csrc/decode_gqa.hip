@@ -35,6 +35,7 @@
 //    kernel.
 
 #include "device_common.h"
+#include "plan_layout.h"
 
 namespace kvattn {
 
@@ -51,9 +52,12 @@ static constexpr float kRescaleSlack = 8.f;
 template <int D>
 constexpr int mfma_max_group() { return D <= 64 ? 16 : 8; }
 
-// Partial of the token range [lo, hi) of sequence b (one or more consecutive partitions, at
-// most 127 blocks) for the query heads of KV head kvh, on the calling wave.  On return lane
-// (n, g4) holds, for head n of the group: acc[t] = unnormalised output dims 16t + 4*g4 .. +3,
+// Partial of the token range [lo, hi) of table row `trow` (one or more consecutive
+// partitions, spanning at most 64 * NWIN blocks: the wave keeps their ids in NWIN 64-lane
+// registers) for the query heads of KV head kvh, on the calling wave.  MFMA column n (lane
+// n, n + 16, ...) takes the query row `qrow` if `qvalid`, else zeros: the heads of one
+// sequence's group, or the heads of several sequences holding the same blocks.  On return
+// lane (n, g4) holds, for column n: acc[t] = unnormalised output dims 16t + 4*g4 .. +3,
 // m = reference max (log2 domain), lsum = its share of the normaliser (to be summed over the
 // four lane rows).
 //
@@ -65,10 +69,11 @@ constexpr int mfma_max_group() { return D <= 64 ? 16 : 8; }
 // output tile, so P V is accurate to ~2^-16 relative rather than bf16's 2^-9.
 // PROBE: the same loads in the same order, with no arithmetic: the in-range 16-bit elements
 // of K and V are XOR-ed into `xs` (the gather's own bandwidth ceiling, and a checksum).
-template <int D, int BSL, int PAIRS, bool NT, bool PROBE = false>
-__device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, int kvh, int lo,
-                                                   int hi, int lane, f32x4 (&acc)[D / 16],
-                                                   float& m, float& lsum, uint32_t& xs) {
+template <int D, int BSL, int PAIRS, bool NT, bool PROBE = false, int NWIN = 2>
+__device__ __forceinline__ void gqa_range_mfma(const DecodeArgs& a, const int32_t* trow,
+                                               const uint16_t* qrow, bool qvalid, int kvh, int lo,
+                                               int hi, int lane, f32x4 (&acc)[D / 16], float& m,
+                                               float& lsum, uint32_t& xs) {
   constexpr int BS = 1 << BSL;
   constexpr int KS = D / 32;       // k-steps of the QK product (32 dims each)
   constexpr int VT = D / 16;       // 16-dim output tiles of the PV product
@@ -78,24 +83,22 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
   const int t_lo = lo >> 4;
   const int ntiles = ((hi + 15) >> 4) - t_lo;
 
-  // Block ids of the range (at most 128 blocks; the launcher checks), two per lane:
-  // pid0 lane i = block wbase + i, pid1 lane i = block wbase + 64 + i.
-  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  // Block ids of the range (at most 64 * NWIN blocks; the launcher checks), NWIN per lane:
+  // pidw[w] lane i = block wbase + 64 w + i.
   const int blk_last = ((t_lo + ntiles - 1) << 4) >> BSL;
   const int wbase = (t_lo << 4) >> BSL;
-  const int pid0 = trow[min(wbase + lane, blk_last)];
-  const int pid1 = trow[min(wbase + 64 + lane, blk_last)];
+  int pidw[NWIN];
+#pragma unroll
+  for (int w = 0; w < NWIN; ++w) pidw[w] = trow[min(wbase + 64 * w + lane, blk_last)];
 
-  // B operand of the QK product: Q^T, lane (n, g4) holds head n, dims 8*(g4+4j) .. +7.
+  // B operand of the QK product: Q^T, lane (n, g4) holds column n, dims 8*(g4+4j) .. +7.
   bf16x8 qop[KS];
   if constexpr (!PROBE) {
-    const bool hv = n < a.group;
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + kvh * a.group + (hv ? n : 0)) * D);
+    const uint4* q4 = reinterpret_cast<const uint4*>(qrow);
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      uint4 v = qrow[g4 + 4 * j];
-      if (!hv) v = make_uint4(0u, 0u, 0u, 0u);
+      uint4 v = q4[g4 + 4 * j];
+      if (!qvalid) v = make_uint4(0u, 0u, 0u, 0u);
       qop[j] = as_bf16x8(v);
     }
   }
@@ -131,9 +134,12 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
     const int blk = tok0 >> BSL;
     const int sub = tok0 & (BS - 1);
     const int rb = blk - wbase;
-    const int32_t pa = __builtin_amdgcn_readlane(pid0, rb & 63);
-    const int32_t pb = __builtin_amdgcn_readlane(pid1, rb & 63);
-    const int32_t pid = rb < 64 ? pa : pb;
+    int32_t pid = __builtin_amdgcn_readlane(pidw[0], rb & 63);
+#pragma unroll
+    for (int w = 1; w < NWIN; ++w) {
+      const int32_t pw = __builtin_amdgcn_readlane(pidw[w], rb & 63);
+      pid = (rb >> 6) == w ? pw : pid;
+    }
     const bool ok = valid_block(a.rt, pid);
     vld[slot] = ok;
     gchar* base = block_addr(a.rt, ok ? pid : 0);
@@ -288,6 +294,21 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
   if (bad) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
 }
 
+// The range [lo, hi) of sequence b for the query heads of KV head kvh (column n = head n of
+// the group; columns past the group get zero queries).
+template <int D, int BSL, int PAIRS, bool NT, bool PROBE = false>
+__device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, int kvh, int lo,
+                                                   int hi, int lane, f32x4 (&acc)[D / 16],
+                                                   float& m, float& lsum, uint32_t& xs) {
+  const int n = lane & 15;
+  const bool hv = n < a.group;
+  const uint16_t* qrow =
+      PROBE ? nullptr
+            : static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.hq + kvh * a.group + (hv ? n : 0)) * D;
+  gqa_range_mfma<D, BSL, PAIRS, NT, PROBE>(a, a.table + (int64_t)b * a.max_blocks, qrow, hv, kvh,
+                                           lo, hi, lane, acc, m, lsum, xs);
+}
+
 // One workgroup of W = group_parts / wave_parts waves per (sequence, KV head, group of
 // partitions); wave w takes the group's partitions [w * wave_parts, (w + 1) * wave_parts),
 // its online softmax continuing across their boundary.  Dynamic LDS (W > 1 only):
@@ -412,6 +433,81 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_probe_kernel(Dec
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) xs ^= __shfl_xor(xs, o);
   if (lane == 0) atomicXor(xsum + (int64_t)b * a.hkv + kvh, (xs ^ (xs >> 16)) & 0xffffu);
+}
+
+// Decode over a plan (kvattn_decode_plan): workgroups of four independent waves, wave w of
+// workgroup x taking wave item 4x + w for KV head blockIdx.y.  An item is a token range of one
+// table row and up to 16 / group sequences that hold that range in the same blocks: column n
+// of the MFMA tiles is head n % group of member n / group, so one pass over the range's keys
+// and values serves every member, and each member's partial of the range goes to its own
+// slot.  The waves of a range read by several items run in one workgroup, on one CU, with
+// cache-retaining loads, so the range crosses HBM once; other ranges stream with
+// non-temporal loads.  Workgroup 0 also writes every sequence's partial count.
+template <int D, int BSL, int PAIRS>
+__global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel(DecodeArgs a,
+                                                                               const int32_t* plan,
+                                                                               int32_t n_groups) {
+  constexpr int VT = D / 16;
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+  const int kvh = blockIdx.y;
+  const int32_t* np = plan + kPlanHeader;
+  const bool hdr_ok = plan[0] == kPlanMagic && plan[1] == a.batch && plan[2] == n_groups &&
+                      plan[3] == kWavesPerGroup * n_groups && plan[6] == a.group &&
+                      plan[7] >= 1 && plan[7] * a.group <= 16;
+  if (!hdr_ok) {
+    if (blockIdx.x == 0 && kvh == 0 && threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    return;
+  }
+  if (blockIdx.x == 0 && kvh == 0)
+    for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup) a.nparts[i] = np[i];
+  if ((int)blockIdx.x >= n_groups) return;  // an empty plan launches one workgroup, no items
+  const int32_t* item = np + a.batch + kItemInts * (blockIdx.x * kWavesPerGroup + wv);
+  const int seq = item[0], lo = item[1], hi = item[2], nmem = item[3], moff = item[4];
+  const bool shared = item[5] != 0;
+  if (nmem <= 0) return;  // an idle wave (uniform)
+  const int32_t* members = np + a.batch + kItemInts * plan[3];  // [M][2]
+  bool ok = seq >= 0 && seq < a.batch && lo >= 0 && lo < hi &&
+            (int64_t)hi <= ((int64_t)a.max_blocks << BSL) && nmem <= plan[7] && moff >= 0 &&
+            (int64_t)moff + nmem <= plan[4] &&
+            ((hi - 1) >> BSL) - (lo >> BSL) < kPlanWindow;
+  const int32_t* mem = members + 2 * (int64_t)(ok ? moff : 0);  // this item's entries
+  // column n: head h of member j
+  const int j = n / a.group;
+  const int h = n - j * a.group;
+  const bool col = ok && j < nmem;
+  const int m = col ? mem[2 * j] : seq;
+  const int slot = col ? mem[2 * j + 1] : 0;
+  ok = ok && !__any(col && (m < 0 || m >= a.batch || slot < 0 || slot >= a.max_parts));
+  if (!ok) {  // uniform over the wave
+    if (lane == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    return;
+  }
+  const uint16_t* qrow =
+      static_cast<const uint16_t*>(a.q) + ((int64_t)m * a.hq + kvh * a.group + (col ? h : 0)) * D;
+  const int32_t* trow = a.table + (int64_t)seq * a.max_blocks;
+  f32x4 acc[VT];
+  float mx, lsum;
+  uint32_t unused = 0u;
+  if (shared)
+    gqa_range_mfma<D, BSL, PAIRS, false, false, kPlanWindow / 64>(a, trow, qrow, col, kvh, lo, hi,
+                                                                  lane, acc, mx, lsum, unused);
+  else
+    gqa_range_mfma<D, BSL, PAIRS, true, false, kPlanWindow / 64>(a, trow, qrow, col, kvh, lo, hi,
+                                                                 lane, acc, mx, lsum, unused);
+  lsum = rows_sum(lsum);
+  if (col) {
+    // the member and slot are read again here rather than held in registers across the loop
+    const int64_t row =
+        ((int64_t)mem[2 * j] * a.hq + kvh * a.group + h) * a.max_parts + mem[2 * j + 1];
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // no weight: o = 0 beside lse = -inf
+    float* op = a.o_part + row * D;
+#pragma unroll
+    for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(op + 16 * t + 4 * g4) = acc[t] * inv;
+    if (g4 == 0) a.lse_part[row] = (mx + log2f(lsum)) * kLn2;
+  }
 }
 
 template <typename T>
@@ -692,6 +788,41 @@ hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, bool stream, dim3 grid, h
     case 64: return launch_mfma_d<64>(a, grid, lds, stream, st);
     case 128: return launch_mfma_d<128>(a, grid, lds, stream, st);
     case 256: return launch_mfma_d<256>(a, grid, lds, stream, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int BSL>
+static hipError_t launch_plan_db(const DecodeArgs& a, const int32_t* plan, int32_t n_groups,
+                                 hipStream_t st) {
+  constexpr int PAIRS = D <= 128 ? 2 : 1;
+  const dim3 grid((unsigned)(n_groups > 0 ? n_groups : 1), (unsigned)a.hkv);
+  hipLaunchKernelGGL((gqa_decode_plan_kernel<D, BSL, PAIRS>), grid, dim3(64 * kWavesPerGroup), 0,
+                     st, a, plan, n_groups);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_plan_d(const DecodeArgs& a, const int32_t* plan, int32_t n_groups,
+                                hipStream_t st) {
+  switch (a.bs_shift) {
+    case 4: return launch_plan_db<D, 4>(a, plan, n_groups, st);
+    case 5: return launch_plan_db<D, 5>(a, plan, n_groups, st);
+    case 6: return launch_plan_db<D, 6>(a, plan, n_groups, st);
+    case 7: return launch_plan_db<D, 7>(a, plan, n_groups, st);
+    case 8: return launch_plan_db<D, 8>(a, plan, n_groups, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The plan kernel with an empty plan (n_groups = 0) runs one workgroup that only writes the
+// partial counts (all zero).
+hipError_t launch_gqa_plan(const DecodeArgs& a, int d, const int32_t* plan, int32_t n_groups,
+                           hipStream_t st) {
+  switch (d) {
+    case 64: return launch_plan_d<64>(a, plan, n_groups, st);
+    case 128: return launch_plan_d<128>(a, plan, n_groups, st);
+    case 256: return launch_plan_d<256>(a, plan, n_groups, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -15,6 +15,8 @@ hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, bool stream, dim3 grid, h
 int gqa_mfma_max_group(int d);
 size_t gqa_mfma_lds_bytes(int group_parts, int group, int d);
 hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, hipStream_t st);
+hipError_t launch_gqa_plan(const DecodeArgs& a, int d, const int32_t* plan, int32_t n_groups,
+                           hipStream_t st);
 hipError_t launch_mla(const DecodeArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_gqa_probe(const DecodeArgs& a, int d, bool stream, dim3 grid, uint32_t* xsum,
                             hipStream_t st);
@@ -374,6 +376,60 @@ kvattn_status kvattn_gather_probe(const kvattn_pool* pool, int32_t batch, int32_
                                      : launch_gqa_probe(a, L.head_dim_k, pool->shared_blocks == 0,
                                                         grid, xsum_dev, st);
   return hip_status(e, "gather_probe launch");
+}
+
+kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q, int32_t q_dtype,
+                                         int32_t batch, int32_t num_q_heads, float scale,
+                                         const int32_t* table_dev, int32_t max_blocks,
+                                         const int32_t* plan_dev, int32_t n_groups,
+                                         int32_t max_parts, float* o_part, float* lse_part,
+                                         int32_t* nparts_dev, int32_t* err_dev, void* hip_stream) {
+  clear_error();
+  if (!pool || !q || !table_dev || !plan_dev || !o_part || !lse_part || !nparts_dev)
+    return set_error(KVATTN_E_INVAL, "decode_partial_plan: null argument");
+  if (!aligned16(q) || !aligned16(o_part))
+    return set_error(KVATTN_E_INVAL, "decode_partial_plan: q and o_part must be 16-byte aligned");
+  if (batch < 1 || num_q_heads < 1 || max_blocks < 1 || max_parts < 1 || n_groups < 0)
+    return set_error(KVATTN_E_INVAL, "decode_partial_plan: bad sizes");
+  if (!std::isfinite(scale)) return set_error(KVATTN_E_INVAL, "decode_partial_plan: scale must be finite");
+  const kvattn_layout& L = pool->layout;
+  if (q_dtype != L.kv_dtype)
+    return set_error(KVATTN_E_UNSUPPORTED, "decode_partial_plan: q_dtype must equal the cache dtype");
+  if (num_q_heads % L.num_kv_heads != 0)
+    return set_error(KVATTN_E_INVAL, "decode_partial_plan: num_q_heads must be a multiple of num_kv_heads");
+  const int group = num_q_heads / L.num_kv_heads;
+  const int d = L.head_dim_k;
+  if (L.latent || L.kv_dtype != KVATTN_BF16 || L.block_size < 16 || L.head_dim_v != d ||
+      (d != 64 && d != 128 && d != 256) || group > 16)
+    return set_error(KVATTN_E_UNSUPPORTED,
+                     "decode_partial_plan: needs a bf16 per-head cache with block size >= 16, head "
+                     "dim 64, 128 or 256 and at most 16 query heads per KV head");
+  if (n_groups > 0 && pool->total_blocks == 0)
+    return set_error(KVATTN_E_INVAL, "decode_partial_plan: the pool holds no blocks");
+  DecodeArgs a{};
+  a.rt = region_table(pool);
+  a.q = q;
+  a.table = table_dev;
+  a.seq = nullptr;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.nparts = nparts_dev;
+  a.err = err_dev;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = L.num_kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks;
+  a.max_parts = max_parts;
+  a.grid_ng = 1;
+  a.group_parts = 1;
+  a.wave_parts = 1;
+  a.bs = L.block_size;
+  a.bs_shift = log2_exact(L.block_size);
+  a.scale = scale;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+  return hip_status(launch_gqa_plan(a, d, plan_dev, n_groups, static_cast<hipStream_t>(hip_stream)),
+                    "decode_partial_plan launch");
 }
 
 kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,

@@ -1,0 +1,23 @@
+// Layout of the decode plan written by kvattn_decode_plan and read by the plan kernel: one
+// int32 array of
+//   header [kPlanHeader]: magic, batch, workgroups G, wave items (4 G), member entries M,
+//                         partials per sequence at most, query heads per KV head, members per
+//                         wave
+//   nparts [batch]:       partials each sequence gets
+//   items  [4 G][kItemInts]: table row, first token, end token, members (0 = idle wave),
+//                         offset of its first member entry, shared flag (the range is read by
+//                         more than one wave item)
+//   members [M][2]:       sequence, partial slot
+#pragma once
+
+#include <stdint.h>
+
+namespace kvattn {
+
+constexpr int32_t kPlanMagic = 0x4E4C5031;
+constexpr int kPlanHeader = 8;
+constexpr int kItemInts = 6;
+constexpr int kWavesPerGroup = 4;
+constexpr int kPlanWindow = 128;  // blocks one wave item may span (two 64-lane id registers)
+
+}  // namespace kvattn

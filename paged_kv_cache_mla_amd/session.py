@@ -22,7 +22,7 @@ def _to_device(arr, device):
 
 
 class DeviceCase:
-    def __init__(self, case, device="cuda", seed=0, group_parts=0):
+    def __init__(self, case, device="cuda", seed=0, group_parts=0, plan=None, span_parts=0):
         self.case = case
         self.regions = [_to_device(r, device) for r in case.regions]
         self.pool = Pool(case.block_size, case.num_kv_heads, case.head_dim_k, case.head_dim_v,
@@ -35,7 +35,8 @@ class DeviceCase:
         self.table = table
         self.step = DecodeStep(self.pool, table, case.ctx_lens, case.part_tokens,
                                case.num_q_heads, case.head_dim_v, tok_begin=case.tok_begin,
-                               device=device, group_parts=group_parts)
+                               device=device, group_parts=group_parts, plan=plan,
+                               span_parts=span_parts)
         self.q = _to_device(case.q, device)
         self.q_dtype = F32 if case.dtype == "f32" else BF16
 

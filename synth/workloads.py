@@ -13,7 +13,9 @@ Five workloads, shaped like the models the pages run (sizes of the full variants
                  pool holds only [r*L, L).
   prefix_shared  64 sequences in 8 groups of 8 sharing their first 75% of blocks, lengths
                  16 * U{512..4096}, 16 q / 2 KV heads, d 256, bf16, bs 16, two disjoint
-                 regions (base + reclaimed) with seeded interleaving of physical ids.
+                 regions (base + reclaimed) with seeded interleaving of physical ids.  The
+                 prefixes nest: every member other than its group's longest takes its first
+                 floor(0.75 * nblocks) blocks from the longest member's table.
   mla_16k        DeepSeek-V2-Lite-shaped MLA: batch 32 x 16384, 16 heads on one 576-d
                  latent (value = first 512), bf16, bs 64, seeded tables, scale 1/sqrt(192).
 Each has a "small" variant that the float64 oracle finishes in seconds while still
@@ -229,32 +231,37 @@ def _prefix_shared(variant):
     lens = (16 * rlen.integers(lo, hi + 1, size=groups * per_group)).astype(np.int32)
     nbs = [_nblocks(int(L), bs) for L in lens]
     max_blocks = max(nbs)
-    # logical plan: group prefix of floor(0.75 * min nblocks) blocks, rest private
-    plan = []
-    shared = []
+    # nested prefixes: in each group the longest member (the lowest index among equals) owns
+    # its whole table; every other member's first floor(0.75 * nblocks) blocks are the
+    # leader's first blocks (shared, ref-counted), the rest of its table is private
+    leaders, shared = [], []
     for g in range(groups):
-        members = range(g * per_group, (g + 1) * per_group)
-        nsh = (3 * min(nbs[m] for m in members)) // 4
-        shared.append(nsh)
-    total = sum(shared) + sum(nbs[m] - shared[m // per_group] for m in range(len(lens)))
+        members = list(range(g * per_group, (g + 1) * per_group))
+        lead = max(members, key=lambda m: (nbs[m], -m))
+        leaders.append(lead)
+        for m in members:
+            shared.append(0 if m == lead else (3 * nbs[m]) // 4)
+    total = sum(nbs[m] - shared[m] for m in range(len(lens)))
     ids = rtab.permutation(total).astype(np.int32)    # seeded interleave over both regions
     table = np.full((len(lens), max_blocks), ABSENT, np.int32)
     pos = 0
     for g in range(groups):
-        first = g * per_group
-        nsh = shared[g]
-        prefix = ids[pos:pos + nsh]
-        pos += nsh
-        for m in range(first, first + per_group):
-            table[m, :nsh] = prefix
-            priv = nbs[m] - nsh
-            table[m, nsh:nbs[m]] = ids[pos:pos + priv]
+        lead = leaders[g]
+        table[lead, :nbs[lead]] = ids[pos:pos + nbs[lead]]
+        pos += nbs[lead]
+        for m in range(g * per_group, (g + 1) * per_group):
+            if m == lead:
+                continue
+            table[m, :shared[m]] = table[lead, :shared[m]]
+            priv = nbs[m] - shared[m]
+            table[m, shared[m]:nbs[m]] = ids[pos:pos + priv]
             pos += priv
     base = int(np.ceil(0.37 * total))
     case = _finish("prefix_shared", variant, seed, bs, 2, 256, 256, "bf16", False, 16,
                    1 / 16.0, [base, total - base], table, lens, None,
                    [512] * len(lens), rq, rkv)
-    case.info["shared_blocks"] = shared
+    case.info["shared_blocks"] = shared     # per sequence: leading blocks taken from its leader
+    case.info["leaders"] = leaders
     case.info["group_size"] = per_group
     return case
 

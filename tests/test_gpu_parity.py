@@ -524,20 +524,23 @@ def test_partition_of_invalid_blocks_contributes_nothing(name, b, ntok, group_pa
     partial (o = 0 beside lse = -inf), and the output is the attention over the remaining
     tokens."""
     from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.session import DeviceCase
     case = make_case(name, "small")
-    bad = case.table.copy()
-    bad[b, :ntok // case.block_size] = sum(case.region_blocks) + 7
     good = case.table
-    case.table = bad
+    bad = good.copy()
+    bad[b, :ntok // case.block_size] = sum(case.region_blocks) + 7
     _say(f"[invalid] {name} seq {b}: first {ntok} tokens in invalid blocks, group_parts {group_parts}")
-    dc, o, lse = _run(case, None, group_parts)
+    dc = DeviceCase(case, group_parts=group_parts)     # the pool admits only valid tables:
+    dc.step.table_dev.copy_(torch.from_numpy(bad))     # the invalid ids go to the device copy
+    o, lse = dc.run()
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
     assert int(dc.step.err.item()) & _lib.ERR_BAD_BLOCK
     o_part = dc.step.o_part.cpu().numpy()
     l_part = dc.step.lse_part.cpu().numpy()
     n = int(dc.step.nparts.cpu().numpy()[b])
     assert np.isfinite(o_part[b, :, :n]).all()
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    case.table = good
     lay = oc.layout_of(case)
     k, v = oracle.gather_sequence(lay, case.regions, case.region_blocks, good[b], ntok,
                                   int(case.ctx_lens[b]))
@@ -568,10 +571,14 @@ def test_full_size_every_sequence(name, kw):
     _say(f"[full] running {name} B={case.batch} device tokens={case.device_tokens()}")
     dc, o, lse = _run(case, ext, 0)
     group_parts = dc.step.group_parts
-    _say(f"[full] {name} ran with group_parts {group_parts} (library choice)")
+    _say(f"[full] {name} ran with group_parts {group_parts} (library choice)"
+         + (f", from a plan of {dc.step.n_groups} workgroups" if dc.step.plan is not None else ""))
     assert int(dc.step.err.item()) == 0
     nparts = dc.step.nparts.cpu().numpy()
-    for b in range(case.batch):
+    if dc.step.plan is not None:          # a pool with shared blocks runs its plan
+        from tests.test_plan_cpu import parse
+        assert np.array_equal(nparts, parse(dc.step.plan, case.batch)[1])
+    for b in range(case.batch if dc.step.plan is None else 0):
         beg = 0 if case.tok_begin is None else int(case.tok_begin[b])
         count = oracle.partition_count(int(case.ctx_lens[b]), beg, int(case.part_tokens[b]))
         assert nparts[b] == -(-count // group_parts)

@@ -1,0 +1,207 @@
+"""GPU parity of the planned decode (kvattn_decode_plan + kvattn_decode_partial_plan + merge),
+through the C ABI, against the float64 oracle.
+
+Sequences that hold the same token range in the same blocks share one wave item, whose
+columns carry several sequences' query heads ([VAMP] §II-A prefix reuse; [CrossPool] §3.1
+paged tables); every sequence still gets its own partials, which merge to its attention
+([InplaceKVCache] §5.1).  Tolerances as in test_gpu_parity: bf16 caches max |o - o_ref| /
+max |o_ref| <= 2e-3, lse within 2e-3; each item's partial is checked against the oracle's
+attention over its token range, element by element.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_case
+from synth.workloads import _normals, _streams
+from tests import oracle_cases as oc
+from tests.test_plan_cpu import parse
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on CPU-only hosts)")
+    from paged_kv_cache_mla_amd import _lib
+    _lib.load()
+    torch.cuda.set_device(0)
+
+
+def _run_plan(case, span_parts=0, plan=True):
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    dc = DeviceCase(case, plan=plan, span_parts=span_parts)
+    o, lse = dc.run()
+    torch.cuda.synchronize()
+    return dc, o.cpu().numpy(), lse.cpu().numpy()
+
+
+def _check_items(case, dc):
+    """Every item's partial for every member equals the oracle's attention over the item's
+    token range of that member; nparts equals the plan's counts."""
+    plan = dc.step.plan
+    hdr, nparts, items, members = parse(plan, case.batch)
+    assert np.array_equal(dc.step.nparts.cpu().numpy(), nparts)
+    o_part = dc.step.o_part.cpu().numpy()
+    l_part = dc.step.lse_part.cpu().numpy()
+    lay = oc.layout_of(case)
+    qf = oc.q_f64(case)
+    worst = 0.0
+    for seq, lo, hi, nmem, moff, _ in items:
+        for m, slot in members[moff:moff + nmem]:
+            k, v = oracle.gather_sequence(lay, case.regions, case.region_blocks, case.table[m], lo, hi)
+            o_ref, l_ref = oracle.attend(qf[m], k, v, case.scale)
+            err = float(np.max(np.abs(o_part[m, :, slot] - o_ref))) / float(np.max(np.abs(o_ref)))
+            worst = max(worst, err)
+            assert err <= oc.out_tol(case), (m, slot, err)
+            assert float(np.max(np.abs(l_part[m, :, slot] - l_ref))) <= oc.lse_tol(case)
+    return worst
+
+
+@pytest.mark.parametrize("span_parts", [0, 1, 2])
+def test_prefix_pool_plan_matches_oracle(span_parts):
+    case = make_case("prefix_shared", "small")
+    _say(f"[plan] prefix_shared small, span_parts {span_parts}")
+    dc, o, lse = _run_plan(case, span_parts)
+    assert dc.step.plan is not None and int(dc.step.err.item()) == 0
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    worst = _check_items(case, dc)
+    _say(f"[plan] out error {err:.3e}, worst item partial {worst:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+
+
+def test_shared_pool_takes_the_plan_by_default_and_both_paths_agree():
+    """A pool holding shared blocks runs the plan when group_parts is the library's choice;
+    the per-sequence kernel on the same pool (group_parts given) agrees within rounding, and
+    the plan path is bitwise deterministic."""
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    case = make_case("prefix_shared", "small")
+    auto = DeviceCase(case)
+    assert auto.step.plan is not None
+    o1, l1 = (t.clone() for t in auto.run())
+    o2, l2 = auto.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    per_seq = DeviceCase(case, group_parts=2)
+    assert per_seq.step.plan is None
+    o3, l3 = per_seq.run()
+    torch.cuda.synchronize()
+    o_ref, _ = oc.full_reference(case)
+    assert oc.out_error(case, o1.cpu().numpy(), o_ref) <= oc.out_tol(case)
+    assert oc.out_error(case, o3.cpu().numpy(), o_ref) <= oc.out_tol(case)
+
+
+def _custom_case(bs, hkv, d, hq, table, lens, begins, part, pool_blocks, seed=1011):
+    """A bf16 per-head case over `pool_blocks` blocks of random data with the given table."""
+    from synth.workloads import _finish
+    rq, rkv, _, _ = _streams(seed)
+    return _finish("plan_custom", "small", seed, bs, hkv, d, d, "bf16", False, hq,
+                   1 / np.sqrt(float(d)), [pool_blocks], np.asarray(table, np.int32), lens,
+                   begins, [part] * len(lens), rq, rkv)
+
+
+def _sharing_table(rng, nseq, nblk, pool_blocks, bs):
+    """Sequences over a common stock of blocks: each takes a prefix of a random length from
+    one of two stems, then private blocks; one sequence also differs from its stem in one
+    block inside the prefix."""
+    ids = rng.permutation(pool_blocks).astype(np.int32)
+    stems = [ids[:nblk], ids[nblk:2 * nblk]]
+    pos = 2 * nblk
+    t = np.full((nseq, nblk), -1, np.int32)
+    for s in range(nseq):
+        stem = stems[s % 2]
+        k = int(rng.integers(0, nblk + 1))
+        t[s, :k] = stem[:k]
+        t[s, k:] = ids[pos:pos + nblk - k]
+        pos += nblk - k
+    t[2, 1] = ids[pos]
+    return t
+
+
+GEOMS = [(16, 2, 256, 16), (16, 4, 128, 32), (32, 2, 64, 2), (64, 1, 128, 16), (16, 2, 128, 6),
+         (16, 1, 64, 16), (128, 2, 128, 4)]
+
+
+@pytest.mark.parametrize("bs,hkv,d,hq", GEOMS, ids=[f"bs{g[0]}-hkv{g[1]}-d{g[2]}-hq{g[3]}" for g in GEOMS])
+def test_plan_kernel_geometries_with_ragged_sharing(bs, hkv, d, hq):
+    """Sharing of random prefix lengths from two stems, ragged ends and starts (one sequence
+    starts inside a block), block sizes 16 .. 128, head dims 64 / 128 / 256, 1 .. 16 query
+    heads per KV head (16 .. 1 sequences per wave item)."""
+    rng = np.random.default_rng(bs * 7 + d + hq)
+    nseq, nblk = 9, 24
+    pool_blocks = 2 * nblk + nseq * nblk + 8
+    table = _sharing_table(rng, nseq, nblk, pool_blocks, bs)
+    lens = [int(nblk * bs - rng.integers(0, bs)) for _ in range(nseq)]
+    lens[4] = bs * 3 + 1
+    begins = [0] * nseq
+    begins[5] = bs // 2 + 1
+    case = _custom_case(bs, hkv, d, hq, table, lens, begins, bs * 4, pool_blocks)
+    for s in range(nseq):
+        case.table[s, -(-lens[s] // bs):] = -1
+    _say(f"[plan-geom] bs={bs} hkv={hkv} d={d} hq={hq}")
+    dc, o, lse = _run_plan(case, span_parts=2)
+    assert int(dc.step.err.item()) == 0
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    worst = _check_items(case, dc)
+    _say(f"[plan-geom] out error {err:.3e}, worst item {worst:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+
+
+def test_plan_with_invalid_ids_and_a_stale_header():
+    """An invalid id inside a range is flagged and contributes nothing; a plan whose header
+    does not match the call is refused by the kernel (flagged, nothing written)."""
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    case = make_case("prefix_shared", "small")
+    dc = DeviceCase(case)
+    bad = dc.table.copy()
+    b = 0                     # the lowest sequence of its shared prefix: its row is the one read
+    bad[b, 2] = sum(case.region_blocks) + 5
+    dc.step.table_dev.copy_(torch.from_numpy(bad))
+    o, lse = dc.run()
+    torch.cuda.synchronize()
+    assert int(dc.step.err.item()) & _lib.ERR_BAD_BLOCK
+    assert np.isfinite(o.cpu().numpy()).all()
+    # a plan for another batch size
+    dc2 = DeviceCase(case)
+    dc2.step.plan_dev[1] = case.batch + 1
+    dc2.step.nparts.fill_(-5)
+    dc2.step.partial(dc2.q, dc2.q_dtype, case.scale)
+    torch.cuda.synchronize()
+    assert int(dc2.step.err.item()) & _lib.ERR_BAD_SEQ
+    assert (dc2.step.nparts.cpu().numpy() == -5).all()
+
+
+def test_plan_relabelled_blocks_give_identical_bits():
+    """Moving every physical block (and rewriting the tables) changes no output bit: the plan's
+    items and their arithmetic depend on which blocks are equal, not on where they are."""
+    case = make_case("prefix_shared", "small")
+    _, o1, l1 = _run_plan(case)
+    rng = np.random.default_rng(9)
+    total = sum(case.region_blocks)
+    perm = rng.permutation(total).astype(np.int32)
+    flat = np.concatenate(case.regions)
+    nel = case.elems_per_block()
+    moved = np.empty_like(flat)
+    for old in range(total):
+        moved[perm[old] * nel:(perm[old] + 1) * nel] = flat[old * nel:(old + 1) * nel]
+    c2 = make_case("prefix_shared", "small")
+    c2.regions = [moved[:case.region_blocks[0] * nel], moved[case.region_blocks[0] * nel:]]
+    c2.table = np.where(case.table >= 0, perm[np.maximum(case.table, 0)], -1).astype(np.int32)
+    _, o2, l2 = _run_plan(c2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

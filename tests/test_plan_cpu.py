@@ -1,0 +1,192 @@
+"""CPU tests of the decode plan (kvattn_decode_plan): sequences that hold the same token range
+in the same blocks share one wave item ([VAMP] §II-A prefix reuse; [CrossPool] §3.1 paged
+tables); every sequence's tokens are covered exactly once by the items it is a member of, its
+partial slots run 0 .. nparts - 1 in token order ([InplaceKVCache] §5.1: any partition of the
+tokens merges exactly), and the plan reads each shared range once.  No GPU: the planner is host
+bookkeeping, and fake device addresses are never touched.
+"""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_mla_amd import _lib
+from paged_kv_cache_mla_amd.api import Pool, decode_plan
+from synth import make_case
+
+FAKE = 0x7F0000000000
+HEADER, ITEM = 8, 6
+
+
+def _pool_for(case):
+    return Pool(case.block_size, case.num_kv_heads, case.head_dim_k, case.head_dim_v, case.dtype,
+                case.latent, [(FAKE + (i << 32), n) for i, n in enumerate(case.region_blocks)])
+
+
+def parse(plan, batch):
+    hdr = plan[:HEADER]
+    nparts = plan[HEADER:HEADER + batch]
+    n_items = int(hdr[3])
+    items = plan[HEADER + batch:HEADER + batch + ITEM * n_items].reshape(n_items, ITEM)
+    members = plan[HEADER + batch + ITEM * n_items:].reshape(-1, 2)
+    return hdr, nparts, items, members
+
+
+def check_plan(plan, n_groups, max_parts, table, lens, begins, parts, bs, group, span=3):
+    """The plan's invariants (raises AssertionError)."""
+    batch = len(lens)
+    hdr, nparts, items, members = parse(plan, batch)
+    assert hdr[0] == 0x4E4C5031 and hdr[1] == batch and hdr[2] == n_groups
+    assert hdr[3] == 4 * n_groups and hdr[4] == members.shape[0] and hdr[6] == group
+    mpw = 16 // group
+    assert hdr[7] == mpw and max_parts == max(1, int(nparts.max()))
+    covered = [[] for _ in range(batch)]       # (lo, hi, slot) per sequence
+    for x, (seq, lo, hi, nmem, moff, shared) in enumerate(items):
+        if nmem == 0:
+            continue
+        assert 1 <= nmem <= mpw and 0 <= lo < hi
+        assert (hi - 1) // bs - lo // bs < 128                 # the wave's window of block ids
+        mem = members[moff:moff + nmem]
+        assert seq in mem[:, 0] or shared                      # the row read is a member's
+        blocks = table[seq][lo // bs:(hi - 1) // bs + 1]
+        assert (blocks >= 0).all()
+        for m, slot in mem:
+            assert np.array_equal(table[m][lo // bs:(hi - 1) // bs + 1], blocks), (x, m)
+            assert lo >= begins[m] and hi <= lens[m]
+            assert hi - lo <= span * parts[m]               # at most span partitions of tokens
+            covered[m].append((lo, hi, slot))
+    for b in range(batch):
+        cov = sorted(covered[b])
+        assert [s for _, _, s in cov] == list(range(len(cov))) == list(range(nparts[b]))
+        pos = begins[b]
+        for lo, hi, _ in cov:
+            assert lo == pos
+            pos = hi
+        assert pos == lens[b]
+    return items, members
+
+
+def _case_arrays(case):
+    begins = np.zeros(case.batch, np.int32) if case.tok_begin is None else case.tok_begin
+    return case.table, case.ctx_lens, begins, case.part_tokens
+
+
+@pytest.mark.parametrize("variant", ["small", "full"])
+def test_prefix_pool_plan_covers_each_sequence_and_reads_shared_blocks_once(variant):
+    case = make_case("prefix_shared", variant)
+    pool = _pool_for(case)
+    table, lens, begins, parts = _case_arrays(case)
+    plan, ng, mp = decode_plan(pool, case.num_q_heads, table, lens, begins, parts)
+    group = case.num_q_heads // case.num_kv_heads
+    items, members = check_plan(plan, ng, mp, table, lens, begins, parts, case.block_size, group)
+    # tokens the plan reads per KV head: each item's range once per distinct (row, range)
+    ranges = {(int(s), int(lo), int(hi)) for s, lo, hi, n, _, _ in items if n > 0}
+    read = sum(hi - lo for _, lo, hi in ranges)
+    bs = case.block_size
+    keys = np.concatenate([table[b][np.arange(lens[b]) // bs].astype(np.int64) * bs + np.arange(lens[b]) % bs
+                           for b in range(case.batch)])
+    unique = np.unique(keys).size
+    logical = int(lens.sum())
+    # sharing is found block by block: the plan reads exactly the unique token slots
+    assert read == unique, (read, unique, logical)
+    assert read < 0.5 * logical
+    # the waves of a shared range (up to four) sit in one workgroup
+    by_range = {}
+    for x, (s, lo, hi, n, _, shared) in enumerate(items):
+        if n > 0 and shared:
+            by_range.setdefault((s, lo), []).append(x // 4)
+    for wgs in by_range.values():
+        if len(wgs) <= 4:
+            assert len(set(wgs)) == 1
+
+
+def test_private_layer_plan_is_one_item_per_span():
+    """Without shared blocks every item is private, one sequence, up to the window's
+    partitions (3 partitions of 32 blocks in 127 block ids), partial counts as the span implies."""
+    case = make_case("gqa_32k", "small")
+    pool = _pool_for(case)
+    table, lens, begins, parts = _case_arrays(case)
+    plan, ng, mp = decode_plan(pool, case.num_q_heads, table, lens, begins, parts)
+    items, _ = check_plan(plan, ng, mp, table, lens, begins, parts, 16, 8)
+    assert (items[:, 5] == 0).all() and (items[items[:, 3] > 0, 3] == 1).all()
+    hdr, nparts, _, _ = parse(plan, case.batch)
+    for b in range(case.batch):
+        npart = -(-int(lens[b]) // 512)
+        assert nparts[b] == -(-npart // 3)
+    plan2, ng2, mp2 = decode_plan(pool, case.num_q_heads, table, lens, begins, parts, span_parts=2)
+    check_plan(plan2, ng2, mp2, table, lens, begins, parts, 16, 8, span=2)
+    assert mp2 == -(-(-(-int(lens.max()) // 512)) // 2)
+
+
+def test_sharing_needs_identical_blocks_and_ranges():
+    """Sharing is decided block position by position: the same block id with the same token
+    extent.  A differing block splits the run, a different start leaves only the first block
+    apart, an invalid id stays private, and pieces are at most span_parts partitions long;
+    groups of 1 .. 16 query heads per KV head (16 .. 1 sequences per wave item)."""
+    bs = 16
+    pool = Pool(bs, 2, 64, 64, "bf16", False, [(FAKE, 400)])
+    rng = np.random.default_rng(3)
+    ids = rng.permutation(400).astype(np.int32)
+    mb = 40
+    t = np.full((6, mb), -1, np.int32)
+    t[0, :40] = ids[:40]
+    t[1, :40] = ids[:40]                  # same as 0
+    t[2, :40] = ids[:40]
+    t[2, 5] = ids[100]                    # differs in partition 1 (blocks 4..7 at P = 64)
+    t[3, :40] = ids[:40]                  # same blocks, different begin
+    t[4, :30] = ids[:30]
+    t[4, 30:40] = ids[200:210]            # shares blocks 0..29
+    t[5, :40] = ids[300:340]
+    t[5, 2] = 999                         # invalid id: private, flagged by the kernel
+    lens = np.array([640, 640, 640, 600, 640, 640], np.int32)
+    begins = np.array([0, 0, 0, 8, 0, 0], np.int32)
+    parts = np.array([64] * 6, np.int32)
+    for hq in (2, 6, 16, 32):
+        group = hq // 2
+        plan, ng, mp = decode_plan(pool, hq, t, lens, begins, parts, span_parts=3)
+        items, members = check_plan(plan, ng, mp, t, lens, begins, parts, bs, group, span=3)
+        mem_sets = {}
+        for s, lo, hi, n, off, sh in items:
+            if n:
+                for m, _ in members[off:off + n]:
+                    mem_sets.setdefault((int(s), int(lo), int(hi)), set()).add(int(m))
+        together = {k: sorted(v) for k, v in mem_sets.items()}
+        # block 5 of sequence 2 differs: [80, 96) is 0, 1, 4 only, and 2 shares 0's other
+        # blocks; 3 shares the blocks but starts at token 8, so only its first block differs;
+        # 4 shares blocks 0..29; 5 (an invalid id) shares nothing
+        assert together[(0, 0, 16)] == [0, 1, 2, 4] and together[(3, 8, 16)] == [3]
+        assert together[(0, 16, 80)] == [0, 1, 2, 3, 4]
+        assert together[(0, 80, 96)] == [0, 1, 3, 4] and together[(2, 80, 96)] == [2]
+        assert all(5 not in v or v == [5] for v in together.values())
+        assert max(hi for (_, lo, hi), v in together.items() if 4 in v and len(v) > 1) == 30 * bs
+
+
+def test_plan_errors():
+    case = make_case("prefix_shared", "small")
+    pool = _pool_for(case)
+    table, lens, begins, parts = _case_arrays(case)
+    with pytest.raises(_lib.KvattnError):
+        decode_plan(pool, 15, table, lens, begins, parts)                  # heads not a multiple
+    with pytest.raises(_lib.KvattnError):
+        decode_plan(pool, 16, table, lens, begins, parts + 1)              # not a block multiple
+    bad_beg = begins.copy()
+    bad_beg[0] = lens[0] + 1
+    with pytest.raises(_lib.KvattnError):
+        decode_plan(pool, 16, table, lens, bad_beg, parts)
+    with pytest.raises(_lib.KvattnError):          # pieces of 2 x 2064 tokens: > 127 blocks
+        decode_plan(pool, 16, table, lens, begins, np.full_like(parts, 2064), span_parts=2)
+    decode_plan(pool, 16, table, lens, begins, np.full_like(parts, 4096))   # 0: pieces fit
+    mla = Pool(64, 1, 576, 512, "bf16", True, [(FAKE, 4)])
+    with pytest.raises(_lib.KvattnError):
+        decode_plan(mla, 16, np.zeros((1, 4), np.int32), [64], None, [64])
+    # a buffer one entry short is refused
+    lib = _lib.load()
+    import ctypes
+    plan, ng, mp = decode_plan(pool, 16, table, lens, begins, parts)
+    n, g, m = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+    t = np.ascontiguousarray(table)
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))  # noqa: E731
+    buf = np.zeros(plan.size - 1, np.int32)
+    st = lib.kvattn_decode_plan(pool.handle, case.batch, 16, p32(t), t.shape[1], p32(lens),
+                                p32(np.ascontiguousarray(begins)), p32(parts), 0, p32(buf),
+                                buf.size, ctypes.byref(n), ctypes.byref(g), ctypes.byref(m))
+    assert st == _lib.E_INVAL and n.value == plan.size
