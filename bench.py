@@ -817,6 +817,12 @@ def main():
     ap.add_argument("--r", type=float, default=0.5, help="host share of split_128k")
     ap.add_argument("--group-parts", type=int, default=0,
                     help="partitions merged on chip per written partial (default 0: the library's choice)")
+    ap.add_argument("--span-parts", type=int, default=0,
+                    help="pools with shared blocks: partitions per wave item of the decode plan "
+                         "(default 0: the library's choice)")
+    ap.add_argument("--no-claim", action="store_true",
+                    help="pools with shared blocks: run the plan one unit per workgroup instead "
+                         "of with work counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-share", choices=["off", "policy"], default="off",
                     help="policy: time the split workload with a native CPU share sized by the "
@@ -880,7 +886,8 @@ def main():
     log(f"[bench] generating {args.workload} (full)")
     kw = {"r": args.r} if args.workload == "split_128k" else {}
     case = make_case(args.workload, "full" if args.workload != "tiny_fp32" else "small", **kw)
-    dc = DeviceCase(case, group_parts=args.group_parts)
+    dc = DeviceCase(case, group_parts=args.group_parts, span_parts=args.span_parts,
+                    claim=not args.no_claim)
     group_parts = dc.step.group_parts
     log(f"[bench] uploaded (group_parts {group_parts}{', the library choice' if dc.step.auto else ''})")
     o_ext = lse_ext = None
@@ -1011,6 +1018,9 @@ def main():
             "part_tokens": int(case.part_tokens[0]),
             "group_parts": group_parts,
             "group_parts_auto": dc.step.auto,
+            **({"plan_workgroups": dc.step.n_groups, "plan_max_parts": dc.step.max_parts,
+                "span_parts": args.span_parts, "claim": not args.no_claim}
+               if dc.step.plan is not None else {}),
             "kv_dtype": case.dtype,
             "device_tokens": case.device_tokens(),
             **({"r": args.r} if args.workload == "split_128k" else {}),

@@ -367,9 +367,17 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  *   q, q_dtype, batch, num_q_heads, scale, table_dev, max_blocks, o_part, lse_part, err_dev:
  *                as for kvattn_decode_partial (max_parts >= the plan's max_parts)
  *   plan_dev     device int32 copy of the plan (all plan_len entries); n_groups its workgroups
+ *   work_dev     device uint32 [2] work counters, or NULL.  NULL: one workgroup per (plan
+ *                workgroup, KV head) unit.  Given: as many workgroups as the device holds at
+ *                once, each taking the next unit from the counters when it is done, so that the
+ *                CUs and XCDs that finish first take more (the partials do not depend on which
+ *                workgroup ran a unit: the result is the same bit for bit).  The counters must
+ *                be zero before the first call (e.g. zero-filled once); every call that
+ *                completes leaves them zero again.  Calls that overlap on one work_dev race.
  * A plan whose header disagrees with the arguments, or an item outside them, sets
- * KVATTN_ERR_BAD_SEQ in *err_dev and is not run; invalid block ids set KVATTN_ERR_BAD_BLOCK and
- * contribute nothing.  Errors: E_INVAL (null pointers, misalignment, sizes), E_UNSUPPORTED
+ * KVATTN_ERR_BAD_SEQ in *err_dev and is not run (the counters are then left as they are);
+ * invalid block ids set KVATTN_ERR_BAD_BLOCK and contribute nothing.  Errors: E_INVAL (null
+ * pointers, misalignment (work_dev: 8 bytes), sizes), E_UNSUPPORTED
  * (as for kvattn_decode_plan, or q_dtype != kv_dtype), E_HIP.
  */
 kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t batch, int32_t num_q_heads,
@@ -382,8 +390,9 @@ kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q,
                                          int32_t batch, int32_t num_q_heads, float scale,
                                          const int32_t* table_dev, int32_t max_blocks,
                                          const int32_t* plan_dev, int32_t n_groups,
-                                         int32_t max_parts, float* o_part, float* lse_part,
-                                         int32_t* nparts_dev, int32_t* err_dev, void* hip_stream);
+                                         uint32_t* work_dev, int32_t max_parts, float* o_part,
+                                         float* lse_part, int32_t* nparts_dev, int32_t* err_dev,
+                                         void* hip_stream);
 
 /*
  * Gather probe: the loads of kvattn_decode_partial's kernel for the same arguments -- the same

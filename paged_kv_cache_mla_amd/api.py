@@ -181,14 +181,17 @@ def decode_plan(pool, num_q_heads, table, ctx_lens, tok_begin, part_tokens, span
 
 
 def decode_partial_plan(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, plan_dev,
-                        n_groups, max_parts, o_part, lse_part, nparts, err=None, stream=None):
+                        n_groups, max_parts, o_part, lse_part, nparts, err=None, stream=None,
+                        work=None):
+    """work: a zeroed device uint32 [2] (torch int32 tensor) for the claiming launch, or None."""
     lib = _lib.load()
     bsz = int(o_part.shape[0])
     check(lib.kvattn_decode_partial_plan(pool.handle, _dptr(q), int(q_dtype), bsz,
                                          int(num_q_heads), ctypes.c_float(scale), _dptr(table_dev),
                                          int(max_blocks), _dptr(plan_dev), int(n_groups),
-                                         int(max_parts), _dptr(o_part), _dptr(lse_part),
-                                         _dptr(nparts), _dptr(err), _stream(stream)),
+                                         _dptr(work), int(max_parts), _dptr(o_part),
+                                         _dptr(lse_part), _dptr(nparts), _dptr(err),
+                                         _stream(stream)),
           "decode_partial_plan")
 
 
@@ -532,11 +535,13 @@ class DecodeStep:
     `plan`: run the step from a work plan (kvattn_decode_plan / kvattn_decode_partial_plan), so
     that sequences holding the same blocks share one pass over them.  None (the default) takes
     the plan when group_parts is the library's choice, the pool holds shared blocks and the
-    layout has a plan kernel.  `span_parts` is the plan's partitions per wave item (0: auto).
+    layout has a plan kernel.  `span_parts` is the plan's partitions per wave item (0: auto);
+    `claim` runs the plan with work counters (workgroups take the next unit when done).
     """
 
     def __init__(self, pool, table, ctx_lens, part_tokens, num_q_heads, head_dim_v,
-                 tok_begin=None, device="cuda", group_parts=0, plan=None, span_parts=0):
+                 tok_begin=None, device="cuda", group_parts=0, plan=None, span_parts=0,
+                 claim=True):
         import torch
         self.pool = pool
         self.ctx = _host_i32(ctx_lens)
@@ -562,6 +567,8 @@ class DecodeStep:
             self.plan, self.n_groups, self.max_parts = decode_plan(
                 pool, num_q_heads, table, self.ctx, self.beg, self.part, span_parts)
             self.plan_dev = torch.from_numpy(self.plan).to(device)
+            # the work counters: zero once; every completed launch leaves them zero
+            self.work = torch.zeros(2, dtype=torch.int32, device=device) if claim else None
         self.table_dev = torch.from_numpy(table).to(device)
         self.seq_dev = torch.from_numpy(np.stack([self.ctx, begs, self.part]).astype(np.int32)).to(device)
         f32 = torch.float32
@@ -588,11 +595,11 @@ class DecodeStep:
         out = (_dptr(self.o_out), _dptr(self.lse_out))
         if self.plan is not None:
             part = (_dptr(self.table_dev), self.max_blocks, _dptr(self.plan_dev), self.n_groups,
-                    self.max_parts, _dptr(self.o_part), _dptr(self.lse_part), _dptr(self.nparts),
-                    _dptr(self.err))
+                    _dptr(self.work), self.max_parts, _dptr(self.o_part), _dptr(self.lse_part),
+                    _dptr(self.nparts), _dptr(self.err))
         keep = (self.table_dev, self.seq_dev, self.o_part, self.lse_part, self.nparts, self.err,
                 self.o_out, self.lse_out, self.ctx, self.beg, self.part,
-                getattr(self, "plan_dev", None))
+                getattr(self, "plan_dev", None), getattr(self, "work", None))
         self._fixed = (part, merge, out, keep)
 
     def partial(self, q, q_dtype, scale, stream=None):

@@ -34,6 +34,9 @@
 //    fp32 caches and block sizes below 16, and as an independent cross-check of the MFMA
 //    kernel.
 
+#include <algorithm>
+#include <atomic>
+
 #include "device_common.h"
 #include "plan_layout.h"
 
@@ -435,36 +438,22 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_probe_kernel(Dec
   if (lane == 0) atomicXor(xsum + (int64_t)b * a.hkv + kvh, (xs ^ (xs >> 16)) & 0xffffu);
 }
 
-// Decode over a plan (kvattn_decode_plan): workgroups of four independent waves, wave w of
-// workgroup x taking wave item 4x + w for KV head blockIdx.y.  An item is a token range of one
-// table row and up to 16 / group sequences that hold that range in the same blocks: column n
-// of the MFMA tiles is head n % group of member n / group, so one pass over the range's keys
-// and values serves every member, and each member's partial of the range goes to its own
-// slot.  The waves of a range read by several items run in one workgroup, on one CU, with
-// cache-retaining loads, so the range crosses HBM once; other ranges stream with
-// non-temporal loads.  Workgroup 0 also writes every sequence's partial count.
+// One wave item of a plan (kvattn_decode_plan): wave `wv` of workgroup `grp` for KV head kvh.
+// An item is a token range of one table row and up to 16 / group sequences that hold that
+// range in the same blocks: column n of the MFMA tiles is head n % group of member n / group,
+// so one pass over the range's keys and values serves every member, and each member's
+// partial of the range goes to its own slot.  Items of a range read by several waves carry
+// the shared flag and read with cache-retaining loads (the waves run in one workgroup, on one
+// CU, so the range crosses HBM once); the others stream with non-temporal loads.  An idle
+// wave returns at once; an item outside the call's arguments sets KVATTN_ERR_BAD_SEQ.
 template <int D, int BSL, int PAIRS>
-__global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel(DecodeArgs a,
-                                                                               const int32_t* plan,
-                                                                               int32_t n_groups) {
+__device__ __forceinline__ void gqa_plan_item(const DecodeArgs& a, const int32_t* plan, int grp,
+                                              int kvh, int wv, int lane) {
   constexpr int VT = D / 16;
-  const int wv = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g4 = lane >> 4;
-  const int kvh = blockIdx.y;
   const int32_t* np = plan + kPlanHeader;
-  const bool hdr_ok = plan[0] == kPlanMagic && plan[1] == a.batch && plan[2] == n_groups &&
-                      plan[3] == kWavesPerGroup * n_groups && plan[6] == a.group &&
-                      plan[7] >= 1 && plan[7] * a.group <= 16;
-  if (!hdr_ok) {
-    if (blockIdx.x == 0 && kvh == 0 && threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
-    return;
-  }
-  if (blockIdx.x == 0 && kvh == 0)
-    for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup) a.nparts[i] = np[i];
-  if ((int)blockIdx.x >= n_groups) return;  // an empty plan launches one workgroup, no items
-  const int32_t* item = np + a.batch + kItemInts * (blockIdx.x * kWavesPerGroup + wv);
+  const int32_t* item = np + a.batch + kItemInts * ((int64_t)grp * kWavesPerGroup + wv);
   const int seq = item[0], lo = item[1], hi = item[2], nmem = item[3], moff = item[4];
   const bool shared = item[5] != 0;
   if (nmem <= 0) return;  // an idle wave (uniform)
@@ -507,6 +496,54 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel
 #pragma unroll
     for (int t = 0; t < VT; ++t) *reinterpret_cast<f32x4*>(op + 16 * t + 4 * g4) = acc[t] * inv;
     if (g4 == 0) a.lse_part[row] = (mx + log2f(lsum)) * kLn2;
+  }
+}
+
+// Decode over a plan: workgroups of four independent waves.  The plan's units are its
+// (workgroup, KV head) pairs, unit u = group u / Hkv, KV head u % Hkv, in the plan's order
+// (most bytes first).  Without a work counter (work == NULL) workgroup x runs unit x.  With
+// one, the grid is the workgroups the device holds at once: workgroup x runs unit x, then
+// claims unit gridDim.x + work[0]++ until none are left, so the CUs (and XCDs) that finish
+// first take the rest; a unit's partials do not depend on which workgroup ran it.  The last
+// workgroup to leave sets work[0] = work[1] = 0 again for the next launch.  Workgroup 0 also
+// writes every sequence's partial count.
+template <int D, int BSL, int PAIRS>
+__global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel(DecodeArgs a,
+                                                                               const int32_t* plan,
+                                                                               int32_t n_groups,
+                                                                               uint32_t* work) {
+  __shared__ int s_unit;
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int32_t* np = plan + kPlanHeader;
+  const bool hdr_ok = plan[0] == kPlanMagic && plan[1] == a.batch && plan[2] == n_groups &&
+                      plan[3] == kWavesPerGroup * n_groups && plan[6] == a.group &&
+                      plan[7] >= 1 && plan[7] * a.group <= 16;
+  if (!hdr_ok) {  // every workgroup returns here (the counters are left as they are)
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    return;
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup) a.nparts[i] = np[i];
+  const int units = n_groups * a.hkv;
+  if (!work) {  // grid (n_groups, Hkv): one unit per workgroup (an empty plan: no unit)
+    if ((int)blockIdx.x < n_groups) gqa_plan_item<D, BSL, PAIRS>(a, plan, blockIdx.x, blockIdx.y, wv, lane);
+    return;
+  }
+  int u = blockIdx.x;
+  while (u < units) {  // uniform over the workgroup
+    gqa_plan_item<D, BSL, PAIRS>(a, plan, u / a.hkv, u % a.hkv, wv, lane);
+    __syncthreads();  // every wave is done with s_unit's last value
+    if (threadIdx.x == 0) s_unit = (int)gridDim.x + (int)atomicAdd(&work[0], 1u);
+    __syncthreads();
+    u = s_unit;
+  }
+  if (threadIdx.x == 0) {
+    __threadfence();  // this workgroup's claims are done before it counts itself out
+    if (atomicAdd(&work[1], 1u) == gridDim.x - 1) {
+      atomicExch(&work[0], 0u);
+      atomicExch(&work[1], 0u);
+    }
   }
 }
 
@@ -792,37 +829,59 @@ hipError_t launch_gqa_mfma(const DecodeArgs& a, int d, bool stream, dim3 grid, h
   }
 }
 
+// Workgroups of the plan kernel one CU holds at once (its register use and four-wave
+// workgroups), per instantiation; 2 if the runtime does not say.
+template <int D, int BSL, int PAIRS>
+static int plan_groups_per_cu() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_decode_plan_kernel<D, BSL, PAIRS>,
+                                                   64 * kWavesPerGroup, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 2;
+  }
+  cached.store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int D, int BSL>
 static hipError_t launch_plan_db(const DecodeArgs& a, const int32_t* plan, int32_t n_groups,
-                                 hipStream_t st) {
+                                 uint32_t* work, int cus, hipStream_t st) {
   constexpr int PAIRS = D <= 128 ? 2 : 1;
-  const dim3 grid((unsigned)(n_groups > 0 ? n_groups : 1), (unsigned)a.hkv);
+  dim3 grid((unsigned)(n_groups > 0 ? n_groups : 1), (unsigned)a.hkv);
+  if (work) {
+    const int64_t units = (int64_t)n_groups * a.hkv;
+    const int64_t resident = (int64_t)(cus > 0 ? cus : 256) * plan_groups_per_cu<D, BSL, PAIRS>();
+    grid = dim3((unsigned)std::max<int64_t>(1, std::min(units, resident)), 1);
+  }
   hipLaunchKernelGGL((gqa_decode_plan_kernel<D, BSL, PAIRS>), grid, dim3(64 * kWavesPerGroup), 0,
-                     st, a, plan, n_groups);
+                     st, a, plan, n_groups, work);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_plan_d(const DecodeArgs& a, const int32_t* plan, int32_t n_groups,
-                                hipStream_t st) {
+                                uint32_t* work, int cus, hipStream_t st) {
   switch (a.bs_shift) {
-    case 4: return launch_plan_db<D, 4>(a, plan, n_groups, st);
-    case 5: return launch_plan_db<D, 5>(a, plan, n_groups, st);
-    case 6: return launch_plan_db<D, 6>(a, plan, n_groups, st);
-    case 7: return launch_plan_db<D, 7>(a, plan, n_groups, st);
-    case 8: return launch_plan_db<D, 8>(a, plan, n_groups, st);
+    case 4: return launch_plan_db<D, 4>(a, plan, n_groups, work, cus, st);
+    case 5: return launch_plan_db<D, 5>(a, plan, n_groups, work, cus, st);
+    case 6: return launch_plan_db<D, 6>(a, plan, n_groups, work, cus, st);
+    case 7: return launch_plan_db<D, 7>(a, plan, n_groups, work, cus, st);
+    case 8: return launch_plan_db<D, 8>(a, plan, n_groups, work, cus, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// The plan kernel with an empty plan (n_groups = 0) runs one workgroup that only writes the
-// partial counts (all zero).
+// The plan kernel; with an empty plan (n_groups = 0) one workgroup only writes the partial
+// counts (all zero).  work: the two-counter workspace (NULL: one unit per workgroup).
 hipError_t launch_gqa_plan(const DecodeArgs& a, int d, const int32_t* plan, int32_t n_groups,
-                           hipStream_t st) {
+                           uint32_t* work, int cus, hipStream_t st) {
   switch (d) {
-    case 64: return launch_plan_d<64>(a, plan, n_groups, st);
-    case 128: return launch_plan_d<128>(a, plan, n_groups, st);
-    case 256: return launch_plan_d<256>(a, plan, n_groups, st);
+    case 64: return launch_plan_d<64>(a, plan, n_groups, work, cus, st);
+    case 128: return launch_plan_d<128>(a, plan, n_groups, work, cus, st);
+    case 256: return launch_plan_d<256>(a, plan, n_groups, work, cus, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,7 +16,7 @@ int gqa_mfma_max_group(int d);
 size_t gqa_mfma_lds_bytes(int group_parts, int group, int d);
 hipError_t launch_gqa_generic(const DecodeArgs& a, int d, bool f32, dim3 grid, hipStream_t st);
 hipError_t launch_gqa_plan(const DecodeArgs& a, int d, const int32_t* plan, int32_t n_groups,
-                           hipStream_t st);
+                           uint32_t* work, int cus, hipStream_t st);
 hipError_t launch_mla(const DecodeArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_gqa_probe(const DecodeArgs& a, int d, bool stream, dim3 grid, uint32_t* xsum,
                             hipStream_t st);
@@ -382,8 +382,9 @@ kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q,
                                          int32_t batch, int32_t num_q_heads, float scale,
                                          const int32_t* table_dev, int32_t max_blocks,
                                          const int32_t* plan_dev, int32_t n_groups,
-                                         int32_t max_parts, float* o_part, float* lse_part,
-                                         int32_t* nparts_dev, int32_t* err_dev, void* hip_stream) {
+                                         uint32_t* work_dev, int32_t max_parts, float* o_part,
+                                         float* lse_part, int32_t* nparts_dev, int32_t* err_dev,
+                                         void* hip_stream) {
   clear_error();
   if (!pool || !q || !table_dev || !plan_dev || !o_part || !lse_part || !nparts_dev)
     return set_error(KVATTN_E_INVAL, "decode_partial_plan: null argument");
@@ -428,7 +429,10 @@ kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q,
   a.bs_shift = log2_exact(L.block_size);
   a.scale = scale;
   a.scale_log2 = scale * 1.44269504088896340736f;
-  return hip_status(launch_gqa_plan(a, d, plan_dev, n_groups, static_cast<hipStream_t>(hip_stream)),
+  if (work_dev && (reinterpret_cast<uintptr_t>(work_dev) & 7u) != 0)
+    return set_error(KVATTN_E_INVAL, "decode_partial_plan: work_dev must be 8-byte aligned");
+  return hip_status(launch_gqa_plan(a, d, plan_dev, n_groups, work_dev, current_device_cus(),
+                                    static_cast<hipStream_t>(hip_stream)),
                     "decode_partial_plan launch");
 }
 

@@ -232,10 +232,19 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
     groups[open[oi]].push_back(k);
     placed[k] = 1;
   }
-  // longest workgroup first
+  // most HBM bytes first: a workgroup reads each distinct range of its waves once (the waves
+  // of one shared range read it together), so its cost is the sum over its distinct ranges
   std::vector<int64_t> gwork(groups.size(), 0);
   for (size_t g = 0; g < groups.size(); ++g)
-    for (int32_t k : groups[g]) gwork[g] = std::max(gwork[g], item_work[k]);
+    for (size_t u = 0; u < groups[g].size(); ++u) {
+      const Item& it = items[groups[g][u]];
+      bool seen = false;
+      for (size_t v = 0; v < u; ++v) {
+        const Item& o = items[groups[g][v]];
+        seen |= o.seq == it.seq && o.lo == it.lo && o.hi == it.hi;
+      }
+      if (!seen) gwork[g] += item_work[groups[g][u]];
+    }
   std::vector<int32_t> gorder(groups.size());
   for (size_t g = 0; g < groups.size(); ++g) gorder[g] = (int32_t)g;
   std::stable_sort(gorder.begin(), gorder.end(),

@@ -22,7 +22,8 @@ def _to_device(arr, device):
 
 
 class DeviceCase:
-    def __init__(self, case, device="cuda", seed=0, group_parts=0, plan=None, span_parts=0):
+    def __init__(self, case, device="cuda", seed=0, group_parts=0, plan=None, span_parts=0,
+                 claim=True):
         self.case = case
         self.regions = [_to_device(r, device) for r in case.regions]
         self.pool = Pool(case.block_size, case.num_kv_heads, case.head_dim_k, case.head_dim_v,
@@ -36,7 +37,7 @@ class DeviceCase:
         self.step = DecodeStep(self.pool, table, case.ctx_lens, case.part_tokens,
                                case.num_q_heads, case.head_dim_v, tok_begin=case.tok_begin,
                                device=device, group_parts=group_parts, plan=plan,
-                               span_parts=span_parts)
+                               span_parts=span_parts, claim=claim)
         self.q = _to_device(case.q, device)
         self.q_dtype = F32 if case.dtype == "f32" else BF16
 

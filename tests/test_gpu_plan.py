@@ -205,3 +205,24 @@ def test_plan_relabelled_blocks_give_identical_bits():
     c2.table = np.where(case.table >= 0, perm[np.maximum(case.table, 0)], -1).astype(np.int32)
     _, o2, l2 = _run_plan(c2)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["prefix_shared", "gqa_32k"])
+def test_claiming_launch_equals_one_unit_per_workgroup(name):
+    """With work counters the workgroups take units as they finish (as many workgroups as the
+    device holds); the result equals the one-unit-per-workgroup launch bit for bit, every
+    step, and every launch leaves the counters at zero."""
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    case = make_case(name, "small")
+    fixed = DeviceCase(case, plan=True, claim=False)
+    claim = DeviceCase(case, plan=True, claim=True)
+    assert fixed.step.work is None and claim.step.work is not None
+    o_f, l_f = (t.clone() for t in fixed.run())
+    for step in range(4):
+        o_c, l_c = claim.run()
+        torch.cuda.synchronize()
+        assert torch.equal(o_c, o_f) and torch.equal(l_c, l_f), step
+        assert (claim.step.work.cpu().numpy() == 0).all(), step
+    assert int(claim.step.err.item()) == 0
+    o_ref, _ = oc.full_reference(case)
+    assert oc.out_error(case, o_f.cpu().numpy(), o_ref) <= oc.out_tol(case)

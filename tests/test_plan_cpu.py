@@ -190,3 +190,30 @@ def test_plan_errors():
                                 p32(np.ascontiguousarray(begins)), p32(parts), 0, p32(buf),
                                 buf.size, ctypes.byref(n), ctypes.byref(g), ctypes.byref(m))
     assert st == _lib.E_INVAL and n.value == plan.size
+
+
+def test_decode_partial_plan_validation_without_gpu():
+    """Argument checks of kvattn_decode_partial_plan, all before any launch."""
+    import ctypes
+    lib = _lib.load()
+    case = make_case("prefix_shared", "small")
+    pool = _pool_for(case)
+    vp = ctypes.c_void_p
+
+    def call(p=pool, q=FAKE, qd=_lib.BF16, batch=16, hq=16, plan=FAKE, ng=3, work=None, mp=4,
+             o=FAKE, lse=FAKE, npart=FAKE):
+        return lib.kvattn_decode_partial_plan(p.handle, vp(q) if q else None, qd, batch, hq,
+                                              ctypes.c_float(0.1), vp(FAKE), 97,
+                                              vp(plan) if plan else None, ng,
+                                              vp(work) if work else None, mp,
+                                              vp(o) if o else None, vp(lse), vp(npart), None, None)
+    assert call(q=None) == _lib.E_INVAL
+    assert call(plan=None) == _lib.E_INVAL
+    assert call(q=FAKE + 4) == _lib.E_INVAL                  # q not 16-byte aligned
+    assert call(work=FAKE + 4) == _lib.E_INVAL               # work counters not 8-byte aligned
+    assert call(ng=-1) == _lib.E_INVAL
+    assert call(mp=0) == _lib.E_INVAL
+    assert call(hq=15) == _lib.E_INVAL
+    assert call(qd=_lib.F32) == _lib.E_UNSUPPORTED
+    mla = Pool(64, 1, 576, 512, "bf16", True, [(FAKE, 4)])
+    assert call(p=mla) == _lib.E_UNSUPPORTED
