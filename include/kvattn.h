@@ -395,6 +395,28 @@ kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q,
                                          void* hip_stream);
 
 /*
+ * kvattn_decode_partial_plan for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same call with the
+ * work counters in a library-owned device array instead of work_dev.  The array is a
+ * file-scope device variable of 64 uint32 (256 bytes) on every GPU the library runs on, held
+ * until the process ends, and looked up once per device on the first call with that device
+ * current; the call itself allocates nothing.  The plan kernel needs two of its words for any
+ * sizes, so no call is refused for its size.  Every call on a GPU shares that GPU's array:
+ * each completed call leaves the counters zero for the next, and calls that overlap on one
+ * GPU (several streams at once) race.  Arguments, results and errors as for
+ * kvattn_decode_partial_plan (results equal bit for bit); also E_HIP if the array's address
+ * cannot be looked up, E_UNSUPPORTED for a device index of 64 or more.
+ */
+kvattn_status kvattn_decode_partial_plan_noalloc(const kvattn_pool* pool, const void* q,
+                                                 int32_t q_dtype, int32_t batch,
+                                                 int32_t num_q_heads, float scale,
+                                                 const int32_t* table_dev, int32_t max_blocks,
+                                                 const int32_t* plan_dev, int32_t n_groups,
+                                                 int32_t max_parts, float* o_part,
+                                                 float* lse_part, int32_t* nparts_dev,
+                                                 int32_t* err_dev, void* hip_stream);
+
+/*
  * Gather probe: the loads of kvattn_decode_partial's kernel for the same arguments -- the same
  * grid, waves, block-table lookups, load widths, cache hints and order -- with no arithmetic.
  * It measures the access pattern's own bandwidth ceiling on this device, which bounds what

@@ -69,6 +69,8 @@ _SIGNATURES = {
                                    _I64, _PI64, _PI32, _PI32]),
     "kvattn_decode_partial_plan": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32, _P,
                                            _I32, _P, _I32, _P, _P, _P, _P, _P]),
+    "kvattn_decode_partial_plan_noalloc": (_I32, [_P, _P, _I32, _I32, _I32, ctypes.c_float, _P, _I32,
+                                                   _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "kvattn_pool_alloc": (_I32, [ctypes.POINTER(Layout), ctypes.POINTER(Region), _I32,
                                  ctypes.c_uint64, ctypes.POINTER(_P)]),
     "kvattn_pool_free": (None, [_P]),

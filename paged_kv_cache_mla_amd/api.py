@@ -12,7 +12,7 @@ import numpy as np
 from . import _lib
 from ._lib import BF16, F32, KvattnError, check
 
-__all__ = ["Pool", "DecodeStep", "choose_group_parts", "decode_plan", "decode_partial_plan", "plan_supported", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
+__all__ = ["Pool", "DecodeStep", "choose_group_parts", "decode_plan", "decode_partial_plan", "decode_partial_plan_noalloc", "plan_supported", "decode_partial", "merge_lse", "resolve_offsets", "append_kv", "select_blocks",
            "partition_count", "block_bytes", "host_partial", "HostShare", "share_optimum", "share_fit",
            "ShareController", "KVStore", "VMMRange", "KvattnError", "BF16", "F32"]
 
@@ -193,6 +193,21 @@ def decode_partial_plan(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blo
                                          _dptr(lse_part), _dptr(nparts), _dptr(err),
                                          _stream(stream)),
           "decode_partial_plan")
+
+
+def decode_partial_plan_noalloc(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks,
+                                plan_dev, n_groups, max_parts, o_part, lse_part, nparts, err=None,
+                                stream=None):
+    """kvattn_decode_partial_plan with the library's own per-GPU work counters (no work_dev)."""
+    lib = _lib.load()
+    bsz = int(o_part.shape[0])
+    check(lib.kvattn_decode_partial_plan_noalloc(pool.handle, _dptr(q), int(q_dtype), bsz,
+                                                 int(num_q_heads), ctypes.c_float(scale),
+                                                 _dptr(table_dev), int(max_blocks), _dptr(plan_dev),
+                                                 int(n_groups), int(max_parts), _dptr(o_part),
+                                                 _dptr(lse_part), _dptr(nparts), _dptr(err),
+                                                 _stream(stream)),
+          "decode_partial_plan_noalloc")
 
 
 def decode_partial(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, ctx_lens,

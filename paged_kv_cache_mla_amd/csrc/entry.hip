@@ -3,6 +3,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "device_common.h"
@@ -283,6 +284,38 @@ static kvattn_status decode_prepare(const char* what, const kvattn_pool* pool, i
   return KVATTN_OK;
 }
 
+// Work counters of kvattn_decode_partial_plan_noalloc: a file-scope device array, one copy on
+// every GPU the library runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up once per device
+// (scratch_on_current_device) and only that address is passed to kernels.  The plan kernel
+// uses two words; every launch that completes leaves them zero, as the module load does.
+constexpr int kScratchWords = 64;  // 256 bytes per GPU
+constexpr int kPlanWorkWords = 2;  // what any call needs, whatever its sizes
+static_assert(kPlanWorkWords <= kScratchWords, "the plan kernel's counters fit the scratch array");
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static uint32_t* g_scratch_ptr[kMaxDevices];  // device address per device, once looked up
+
+static kvattn_status scratch_on_current_device(uint32_t** out) {
+  int dev = -1;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return set_error(KVATTN_E_HIP, std::string("scratch: hipGetDevice: ") + hipGetErrorString(ge));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(KVATTN_E_UNSUPPORTED, "scratch: device index beyond " + std::to_string(kMaxDevices));
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(KVATTN_E_HIP, std::string("scratch: hipGetSymbolAddress: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return KVATTN_OK;
+}
+
 }  // namespace kvattn
 
 using namespace kvattn;
@@ -434,6 +467,23 @@ kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q,
   return hip_status(launch_gqa_plan(a, d, plan_dev, n_groups, work_dev, current_device_cus(),
                                     static_cast<hipStream_t>(hip_stream)),
                     "decode_partial_plan launch");
+}
+
+kvattn_status kvattn_decode_partial_plan_noalloc(const kvattn_pool* pool, const void* q,
+                                                 int32_t q_dtype, int32_t batch,
+                                                 int32_t num_q_heads, float scale,
+                                                 const int32_t* table_dev, int32_t max_blocks,
+                                                 const int32_t* plan_dev, int32_t n_groups,
+                                                 int32_t max_parts, float* o_part,
+                                                 float* lse_part, int32_t* nparts_dev,
+                                                 int32_t* err_dev, void* hip_stream) {
+  clear_error();
+  uint32_t* work = nullptr;
+  const kvattn_status s = scratch_on_current_device(&work);
+  if (s != KVATTN_OK) return s;
+  return kvattn_decode_partial_plan(pool, q, q_dtype, batch, num_q_heads, scale, table_dev,
+                                    max_blocks, plan_dev, n_groups, work, max_parts, o_part,
+                                    lse_part, nparts_dev, err_dev, hip_stream);
 }
 
 kvattn_status kvattn_merge_lse(const float* o_part, const float* lse_part,
