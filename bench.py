@@ -820,9 +820,11 @@ def main():
     ap.add_argument("--span-parts", type=int, default=0,
                     help="pools with shared blocks: partitions per wave item of the decode plan "
                          "(default 0: the library's choice)")
-    ap.add_argument("--no-claim", action="store_true",
-                    help="pools with shared blocks: run the plan one unit per workgroup instead "
-                         "of with work counters")
+    ap.add_argument("--plan", action="store_true",
+                    help="run the step from a decode plan even when the pool holds no shared blocks")
+    ap.add_argument("--claim", action="store_true",
+                    help="pools with shared blocks: run the plan with work counters (workgroups "
+                         "take the next unit when done) instead of one unit per workgroup")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-share", choices=["off", "policy"], default="off",
                     help="policy: time the split workload with a native CPU share sized by the "
@@ -887,7 +889,7 @@ def main():
     kw = {"r": args.r} if args.workload == "split_128k" else {}
     case = make_case(args.workload, "full" if args.workload != "tiny_fp32" else "small", **kw)
     dc = DeviceCase(case, group_parts=args.group_parts, span_parts=args.span_parts,
-                    claim=not args.no_claim)
+                    claim=args.claim, plan=True if args.plan else None)
     group_parts = dc.step.group_parts
     log(f"[bench] uploaded (group_parts {group_parts}{', the library choice' if dc.step.auto else ''})")
     o_ext = lse_ext = None
@@ -1019,7 +1021,7 @@ def main():
             "group_parts": group_parts,
             "group_parts_auto": dc.step.auto,
             **({"plan_workgroups": dc.step.n_groups, "plan_max_parts": dc.step.max_parts,
-                "span_parts": args.span_parts, "claim": not args.no_claim}
+                "span_parts": args.span_parts, "claim": args.claim}
                if dc.step.plan is not None else {}),
             "kv_dtype": case.dtype,
             "device_tokens": case.device_tokens(),

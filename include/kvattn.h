@@ -339,14 +339,17 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  * same set (an invalid id: a set of its own sequence) is taken once, from the set's lowest
  * sequence, and cut into pieces of at most span_parts * part_tokens tokens (span_parts 0: as
  * many whole partitions as a wave's window of 127 block ids holds); a piece becomes wave
- * items of up to 16 / (Hq / Hkv) of its sequences each, and the items of one piece run in one
- * workgroup of four waves where they fit.  Every sequence's range [tok_begin, ctx_len) is
+ * items of up to 16 / (Hq / Hkv) of its sequences each.  A piece of k >= 2 items runs in
+ * ceil(k / 4) workgroups of its own whose four waves stage the range through LDS together
+ * (mode 2: it crosses HBM once per such workgroup; a workgroup of fewer items is padded with
+ * items of no sequence); single items fill workgroups of four independent waves (mode 1, a
+ * shared range one wave reads for all its sharers; mode 0, private).  Every sequence's range [tok_begin, ctx_len) is
  * thus covered exactly once by the items it belongs to; its partials are written in the
  * order of their first tokens, slots 0 .. nparts[b] - 1.  The plan is an int32 array:
  *   header[8] = {magic, batch, n_groups, 4 n_groups, member entries M, max_parts,
  *                Hq / Hkv, sequences per wave item}, nparts[batch],
  *   items[4 n_groups][6] = {table row, first token, end token, sequences (0: idle wave),
- *                           first member entry, shared flag},
+ *                           first member entry, mode 0 / 1 / 2},
  *   members[M][2] = {sequence, partial slot}.
  *   table        host [batch][max_blocks] int32 (the device copy's contents)
  *   plan         host int32 [plan_cap], or NULL to query the size only
@@ -362,8 +365,9 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  * device: for every item and KV head, the attention of its sequences' query heads over its
  * token range, read once through the table row it names; sequence b's partial of item k goes
  * to o_part[b][h][slot] / lse_part[b][h][slot] (same formulas as kvattn_decode_partial) and
- * nparts_dev[b] receives the plan's count, so kvattn_merge_lse completes the step.  Items of a
- * shared range are read with cache-retaining loads, the others with non-temporal loads.
+ * nparts_dev[b] receives the plan's count, so kvattn_merge_lse completes the step.  Modes 0
+ * and 1 stream their range with non-temporal loads; a mode-2 workgroup (all four items mode 2
+ * with one range, else KVATTN_ERR_BAD_SEQ) loads it into LDS once for its four waves.
  *   q, q_dtype, batch, num_q_heads, scale, table_dev, max_blocks, o_part, lse_part, err_dev:
  *                as for kvattn_decode_partial (max_parts >= the plan's max_parts)
  *   plan_dev     device int32 copy of the plan (all plan_len entries); n_groups its workgroups

@@ -556,7 +556,7 @@ class DecodeStep:
 
     def __init__(self, pool, table, ctx_lens, part_tokens, num_q_heads, head_dim_v,
                  tok_begin=None, device="cuda", group_parts=0, plan=None, span_parts=0,
-                 claim=True):
+                 claim=False):
         import torch
         self.pool = pool
         self.ctx = _host_i32(ctx_lens)

@@ -312,6 +312,251 @@ __device__ __forceinline__ void gqa_partition_mfma(const DecodeArgs& a, int b, i
                                            lo, hi, lane, acc, m, lsum, xs);
 }
 
+// The range [lo, hi) of table row `trow` read by the four waves of a workgroup together
+// (staged wave items of a plan: one range, up to 4 x 16 / group sequences), so that it crosses
+// HBM once.  A stage is a pair of 16-token tiles (32 tokens), 2 * D / 32 K lines and D / 16 V
+// lines of 1 KiB.  Within a pair, row r = 4 a + b of score tile u stands for token
+// 8 a + 4 u + b, so that the eight tokens 8 g4 .. 8 g4 + 7 whose weights lane group g4 holds
+// in the PV product are contiguous: the V operand of lane (n, g4) is row n of its 16-row
+// group, tokens 8 g4 .. + 7, one 16-byte piece of the cache.  K line (u, j) holds at lane
+// (n, g4) the 16-byte chunk 4 j + g4 of the token of row n of tile u; V line h holds at lane
+// (n, g4) row 16 h + n, tokens 8 g4 .. + 7.  Every wave loads a quarter of each stage's lines
+// (lane i: the line's bytes 16 i .. 16 i + 15, read back by the same lane position, so LDS
+// reads and writes are 16-byte, bank-conflict free) into a register ring AHEAD stages deep,
+// and writes a stage into one half of `lds` (two stages) when its turn comes, so that the
+// four waves keep AHEAD stages of distinct bytes in flight between them.  Per stage p: write
+// the wave's lines of stage p into half p % 2 (every wave finished reading stage p - 2 there
+// before the previous barrier), refill that ring slot with stage p + AHEAD, barrier, then
+// score both tiles with K read from LDS, the online softmax, and the PV product with V read
+// from LDS: the arithmetic of the per-wave ring loop of gqa_range_mfma, tokens taken in
+// another order.  A wave with no sequence (`active` false: padding) loads and writes its
+// lines but computes nothing.  A tile past the range loads the range's last tile again and a
+// stage past the last loads one line for all lanes (every load unconditional, so that the
+// wait before a stage's LDS write leaves the later stages' loads in flight); such slots are
+// fully masked.  The trip count depends on the range only, so all four waves meet every
+// barrier.
+template <int D, int BSL, int AHEAD>
+__device__ __forceinline__ void gqa_range_staged(const DecodeArgs& a, const int32_t* trow,
+                                                 const uint16_t* qrow, bool qvalid, bool active,
+                                                 int kvh, int lo, int hi, int wv, int lane,
+                                                 uint32_t lds, f32x4 (&acc)[D / 16], float& m,
+                                                 float& lsum) {
+  wv = __builtin_amdgcn_readfirstlane(wv);  // uniform: the line offsets stay scalar
+  typedef __attribute__((address_space(3))) u32x4 lw32x4;
+  typedef __attribute__((address_space(3))) const u32x4 lu32x4;
+  constexpr int BS = 1 << BSL;
+  constexpr int KS = D / 32;
+  constexpr int VT = D / 16;
+  constexpr int KLINES = 2 * KS;
+  constexpr int LINES = KLINES + VT;
+  constexpr int LPW = LINES / kWavesPerGroup;  // lines per wave and stage
+  constexpr int KPW = KLINES / kWavesPerGroup;
+  static_assert(KLINES % kWavesPerGroup == 0 && LINES % kWavesPerGroup == 0, "line split");
+  constexpr uint32_t STAGE = LINES * 1024;
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+  const int t_lo = lo >> 4;
+  const int ntiles = ((hi + 15) >> 4) - t_lo;
+  const int npairs = (ntiles + 1) >> 1;
+
+  const int blk_last = ((t_lo + ntiles - 1) << 4) >> BSL;
+  const int wbase = (t_lo << 4) >> BSL;
+  const int pid0 = trow[min(wbase + lane, blk_last)];
+  const int pid1 = trow[min(wbase + 64 + lane, blk_last)];
+  auto tile_pid = [&](int rel) -> int32_t {  // uniform
+    const int rb = ((((t_lo + rel) << 4) >> BSL) - wbase);
+    const int32_t pa = __builtin_amdgcn_readlane(pid0, rb & 63);
+    const int32_t pb = __builtin_amdgcn_readlane(pid1, rb & 63);
+    return rb < 64 ? pa : pb;
+  };
+
+  bf16x8 qop[KS];
+  {
+    const uint4* q4 = reinterpret_cast<const uint4*>(qrow);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      uint4 v = q4[g4 + 4 * j];
+      if (!qvalid) v = make_uint4(0u, 0u, 0u, 0u);
+      qop[j] = as_bf16x8(v);
+    }
+  }
+
+  // lane parts of the addresses: K, the token of row n of tile 0 (8 (n / 4) + n % 4, in pair
+  // tile n / 8) and chunk g4; V, row n and tokens 8 g4 .. (pair tile g4 / 2)
+  const int ktile = n >> 3;
+  const uint32_t kpart = (uint32_t)((((kvh * (D / 8) + g4) << BSL) + (8 * ((n >> 2) & 1) + (n & 3))) * 16);
+  const int vtile = g4 >> 1;
+  const uint64_t vpart = (uint64_t)a.hkv * BS * D * 2 +
+                         (uint64_t)((((kvh * D + n) << BSL) + 8 * (g4 & 1)) * 2);
+  // Line i of this wave in a stage: its place in the stage (LDS line) and its byte offset
+  // from the lane's base address.  Where a kind of line numbers at least four, each wave
+  // takes a fixed share of both tiles' (K) or row groups' (V) lines.
+  auto line_of = [&](int i, uint32_t& off) -> int {
+    if (i < KPW) {  // K line (u, j): score tile u, k-step j
+      int u, j;
+      if (KS >= kWavesPerGroup) {
+        u = i / (KS / kWavesPerGroup);
+        j = wv + kWavesPerGroup * (i % (KS / kWavesPerGroup));
+      } else {
+        u = wv / KS;
+        j = wv % KS;
+      }
+      off = (uint32_t)(u * 4 * 16 + j * (4 * BS * 16));
+      return u * KS + j;
+    }
+    const int h = wv + kWavesPerGroup * (i - KPW);  // V line h: rows 16 h .. 16 h + 15
+    off = (uint32_t)((16 * h) << BSL) * 2u;
+    return KLINES + h;
+  };
+  const uint64_t dummy =
+      (uint64_t)(uintptr_t)block_addr(a.rt, valid_block(a.rt, tile_pid(0)) ? tile_pid(0) : 0);
+  auto load_stage = [&](int p, u32x4 (&r)[LPW]) {
+    uint64_t tb[2];
+    int sub[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int rel = min(2 * p + w, ntiles - 1);  // past the range: the last tile again
+      const int32_t pid = tile_pid(rel);
+      tb[w] = (uint64_t)(uintptr_t)block_addr(a.rt, valid_block(a.rt, pid) ? pid : 0);
+      sub[w] = ((t_lo + rel) << 4) & (BS - 1);
+    }
+    const bool past = p >= npairs;  // uniform
+    const uint64_t kb = past ? dummy : (ktile ? tb[1] : tb[0]) + kpart + (uint32_t)((ktile ? sub[1] : sub[0]) * 16);
+    const uint64_t vb = past ? dummy : (vtile ? tb[1] : tb[0]) + vpart + (uint32_t)((vtile ? sub[1] : sub[0]) * 2);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      uint32_t off;
+      line_of(i, off);
+      const uint64_t src = (i < KPW ? kb : vb) + (past ? 0u : off);
+      r[i] = __builtin_nontemporal_load(reinterpret_cast<gu32x4*>((uintptr_t)src));
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < VT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  m = kNegInf;
+  lsum = 0.f;
+  bool bad = false;
+  const float scale_log2 = a.scale_log2;
+
+  u32x4 ring[AHEAD][LPW];
+  // stage by stage, in order (no scheduling across): the wait before stage p's LDS write
+  // then counts only the loads of the stages after it
+#pragma unroll
+  for (int u = 0; u < AHEAD; ++u) {
+    load_stage(u, ring[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int p0 = 0; p0 < npairs; p0 += AHEAD) {
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u) {
+      // a stage past the last (npairs not a multiple of AHEAD) runs fully masked: no weight,
+      // no rescale; the loop body has no exit, so the loads stay in one order
+      const int p = p0 + u;
+      const uint32_t sb = lds + (uint32_t)(p & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        uint32_t off;
+        const int line = line_of(i, off);
+        *(lw32x4*)(uintptr_t)(sb + line * 1024u + lane * 16u) = ring[u][i];
+      }
+      load_stage(p + AHEAD, ring[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // stage p is in LDS for every wave
+      if (!active) continue;
+      const int ra = 2 * p;
+      const bool vldA = valid_block(a.rt, tile_pid(min(ra, ntiles - 1)));
+      const bool vldB = ra + 1 < ntiles && valid_block(a.rt, tile_pid(ra + 1));
+      bad |= (!vldA & (ra < ntiles)) | (!vldB & (ra + 1 < ntiles));
+      const bool vld = vtile ? vldB : vldA;  // tokens 8 g4 .. lie in pair tile g4 / 2
+      const int pbase = (t_lo + ra) << 4;
+      // scores S^T = K Q^T of both tiles, K operands read from LDS, masked to the range
+      float sv[2][4];
+      uint32_t okbits[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          const u32x4 kv = *(lu32x4*)(uintptr_t)(sb + (w * KS + j) * 1024u + lane * 16u);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qop[j], sacc, 0, 0, 0);
+        }
+        const int tb = pbase + 8 * g4 + 4 * w;
+        okbits[w] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tb + i;
+          const bool ok = vld & (t >= lo) & (t < hi);  // bitwise: no short-circuit branches
+          sv[w][i] = ok ? sacc[i] * scale_log2 : kNegInf;
+          okbits[w] |= (uint32_t)ok << i;
+        }
+      }
+      // online softmax in the log2 domain with the lazy rescale of the per-wave ring loop
+      const float mx = rows_max(fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                                      fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3]))));
+      if (__any(mx > m + kRescaleSlack)) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m = -inf
+#pragma unroll
+        for (int t = 0; t < VT; ++t) acc[t] *= alpha;
+        lsum *= alpha;
+        m = mnew;
+      }
+      const float mref = m == kNegInf ? 0.f : m;
+      float pw[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = __builtin_amdgcn_exp2f(sv[0][i] - mref);
+        pw[4 + i] = __builtin_amdgcn_exp2f(sv[1][i] - mref);
+      }
+      u32x4 phi, plo;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t h = cvt_pk_bf16(pw[2 * k], pw[2 * k + 1]);
+        phi[k] = h;
+        plo[k] = cvt_pk_bf16(pw[2 * k] - __uint_as_float(h << 16),
+                             pw[2 * k + 1] - __uint_as_float(h & 0xffff0000u));
+      }
+      lsum += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+      const bf16x8 bhi = as_bf16x8(phi), blo = as_bf16x8(plo);
+      // V^T P^T with the V operands read from LDS.  In a pair not wholly inside the range and
+      // valid (its first or last, past the end: stale LDS, an invalid block) the other token
+      // slots may hold anything, NaN bit patterns included, and a zero weight does not cancel
+      // a NaN, so those slots are zeroed as they are read (the token validity of lane group
+      // g4 is the same in the score and V layouts).
+      const bool edge = !vldA | (!vldB & (ra + 1 < ntiles)) | (pbase < lo) | (pbase + 32 > hi);
+      if (edge) {  // uniform
+        uint32_t vm[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t ob = okbits[w >> 1] >> (2 * (w & 1));
+          vm[w] = ((ob & 1u) ? 0xffffu : 0u) | ((ob & 2u) ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int t = 0; t < VT; ++t) {
+          const u32x4 v = *(lu32x4*)(uintptr_t)(sb + (KLINES + t) * 1024u + lane * 16u);
+          const bf16x8 vop = as_bf16x8(u32x4{v[0] & vm[0], v[1] & vm[1], v[2] & vm[2], v[3] & vm[3]});
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, bhi, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, blo, acc[t], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < VT; ++t) {
+          const bf16x8 vop =
+              as_bf16x8(*(lu32x4*)(uintptr_t)(sb + (KLINES + t) * 1024u + lane * 16u));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, bhi, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, blo, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (bad) flag_error(a.err, KVATTN_ERR_BAD_BLOCK);
+}
+
+// Stages a staged workgroup's waves keep in flight (register ring depth) per head dim.
+template <int D>
+__host__ __device__ constexpr int staged_ahead() { return D == 256 ? 2 : 4; }
+
 // One workgroup of W = group_parts / wave_parts waves per (sequence, KV head, group of
 // partitions); wave w takes the group's partitions [w * wave_parts, (w + 1) * wave_parts),
 // its online softmax continuing across their boundary.  Dynamic LDS (W > 1 only):
@@ -438,52 +683,79 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_probe_kernel(Dec
   if (lane == 0) atomicXor(xsum + (int64_t)b * a.hkv + kvh, (xs ^ (xs >> 16)) & 0xffffu);
 }
 
+// LDS the plan kernel reserves per workgroup: two stages of gqa_range_staged.
+__host__ __device__ constexpr uint32_t plan_lds_bytes(int d) { return 2u * (2 * (d / 32) + d / 16) * 1024u; }
+
 // One wave item of a plan (kvattn_decode_plan): wave `wv` of workgroup `grp` for KV head kvh.
 // An item is a token range of one table row and up to 16 / group sequences that hold that
 // range in the same blocks: column n of the MFMA tiles is head n % group of member n / group,
 // so one pass over the range's keys and values serves every member, and each member's
-// partial of the range goes to its own slot.  Items of a range read by several waves carry
-// the shared flag and read with cache-retaining loads (the waves run in one workgroup, on one
-// CU, so the range crosses HBM once); the others stream with non-temporal loads.  An idle
-// wave returns at once; an item outside the call's arguments sets KVATTN_ERR_BAD_SEQ.
+// partial of the range goes to its own slot.  Item modes: 0, a private range, and 1, a range
+// one wave reads for all its sharers, are streamed with non-temporal loads (each is read once
+// either way); 2, staged: the workgroup's four waves share one range (their sharers split
+// between them) and read it once through LDS (gqa_range_staged; padding waves with no
+// sequence still load their share).
+// Every wave of a workgroup reads all four of its items, so the staged decision, and the
+// range a staged workgroup loops over, are the same for all of them.  An idle wave returns at
+// once; an item outside the call's arguments sets KVATTN_ERR_BAD_SEQ.
 template <int D, int BSL, int PAIRS>
 __device__ __forceinline__ void gqa_plan_item(const DecodeArgs& a, const int32_t* plan, int grp,
-                                              int kvh, int wv, int lane) {
+                                              int kvh, int wv, int lane, uint32_t lds) {
   constexpr int VT = D / 16;
   const int n = lane & 15;
   const int g4 = lane >> 4;
   const int32_t* np = plan + kPlanHeader;
-  const int32_t* item = np + a.batch + kItemInts * ((int64_t)grp * kWavesPerGroup + wv);
+  const int32_t* items0 = np + a.batch + kItemInts * ((int64_t)grp * kWavesPerGroup);
+  const int32_t* item = items0 + kItemInts * wv;
   const int seq = item[0], lo = item[1], hi = item[2], nmem = item[3], moff = item[4];
-  const bool shared = item[5] != 0;
-  if (nmem <= 0) return;  // an idle wave (uniform)
+  bool staged = true, any_staged = false;
+#pragma unroll
+  for (int w = 0; w < kWavesPerGroup; ++w) {
+    const int32_t* it = items0 + kItemInts * w;
+    staged &= it[5] == 2 && it[0] == items0[0] && it[1] == items0[1] && it[2] == items0[2];
+    any_staged |= it[5] == 2;
+  }
+  if (any_staged && !staged) {  // uniform over the workgroup: nobody reaches a barrier
+    if (wv == 0 && lane == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    return;
+  }
+  if (!staged && nmem <= 0) return;  // an idle wave (uniform)
+  const bool range_ok = seq >= 0 && seq < a.batch && lo >= 0 && lo < hi &&
+                        (int64_t)hi <= ((int64_t)a.max_blocks << BSL) &&
+                        ((hi - 1) >> BSL) - (lo >> BSL) < kPlanWindow;
+  if (!range_ok) {  // uniform over the workgroup when staged (one range)
+    if (lane == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    return;
+  }
   const int32_t* members = np + a.batch + kItemInts * plan[3];  // [M][2]
-  bool ok = seq >= 0 && seq < a.batch && lo >= 0 && lo < hi &&
-            (int64_t)hi <= ((int64_t)a.max_blocks << BSL) && nmem <= plan[7] && moff >= 0 &&
-            (int64_t)moff + nmem <= plan[4] &&
-            ((hi - 1) >> BSL) - (lo >> BSL) < kPlanWindow;
+  bool ok = nmem >= 0 && nmem <= plan[7] && moff >= 0 && (int64_t)moff + nmem <= plan[4];
   const int32_t* mem = members + 2 * (int64_t)(ok ? moff : 0);  // this item's entries
   // column n: head h of member j
   const int j = n / a.group;
   const int h = n - j * a.group;
-  const bool col = ok && j < nmem;
+  bool col = ok && j < nmem;
   const int m = col ? mem[2 * j] : seq;
   const int slot = col ? mem[2 * j + 1] : 0;
   ok = ok && !__any(col && (m < 0 || m >= a.batch || slot < 0 || slot >= a.max_parts));
   if (!ok) {  // uniform over the wave
     if (lane == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
-    return;
+    if (!staged) return;
+    col = false;  // a staged wave keeps loading its share of the range for the others
   }
   const uint16_t* qrow =
-      static_cast<const uint16_t*>(a.q) + ((int64_t)m * a.hq + kvh * a.group + (col ? h : 0)) * D;
+      static_cast<const uint16_t*>(a.q) +
+      ((int64_t)(col ? m : seq) * a.hq + kvh * a.group + (col ? h : 0)) * D;
   const int32_t* trow = a.table + (int64_t)seq * a.max_blocks;
   f32x4 acc[VT];
   float mx, lsum;
   uint32_t unused = 0u;
-  if (shared)
+  if (staged)
+    gqa_range_staged<D, BSL, staged_ahead<D>()>(a, trow, qrow, col, __any(col), kvh, lo, hi, wv,
+                                                lane, lds, acc, mx, lsum);
+  else if (item[5] == 1)  // other waves of the workgroup read the same range: keep it in L2
     gqa_range_mfma<D, BSL, PAIRS, false, false, kPlanWindow / 64>(a, trow, qrow, col, kvh, lo, hi,
                                                                   lane, acc, mx, lsum, unused);
-  else
+  else  // one wave reads the range, once, whatever its sharers: stream it
     gqa_range_mfma<D, BSL, PAIRS, true, false, kPlanWindow / 64>(a, trow, qrow, col, kvh, lo, hi,
                                                                  lane, acc, mx, lsum, unused);
   lsum = rows_sum(lsum);
@@ -513,6 +785,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel
                                                                                int32_t n_groups,
                                                                                uint32_t* work) {
   __shared__ int s_unit;
+  extern __shared__ __attribute__((aligned(16))) char plan_lds[];  // plan_lds_bytes(D)
+  const uint32_t lds = (uint32_t)(uintptr_t)plan_lds;
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int32_t* np = plan + kPlanHeader;
@@ -527,12 +801,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel
     for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup) a.nparts[i] = np[i];
   const int units = n_groups * a.hkv;
   if (!work) {  // grid (n_groups, Hkv): one unit per workgroup (an empty plan: no unit)
-    if ((int)blockIdx.x < n_groups) gqa_plan_item<D, BSL, PAIRS>(a, plan, blockIdx.x, blockIdx.y, wv, lane);
+    if ((int)blockIdx.x < n_groups)
+      gqa_plan_item<D, BSL, PAIRS>(a, plan, blockIdx.x, blockIdx.y, wv, lane, lds);
     return;
   }
   int u = blockIdx.x;
   while (u < units) {  // uniform over the workgroup
-    gqa_plan_item<D, BSL, PAIRS>(a, plan, u / a.hkv, u % a.hkv, wv, lane);
+    gqa_plan_item<D, BSL, PAIRS>(a, plan, u / a.hkv, u % a.hkv, wv, lane, lds);
     __syncthreads();  // every wave is done with s_unit's last value
     if (threadIdx.x == 0) s_unit = (int)gridDim.x + (int)atomicAdd(&work[0], 1u);
     __syncthreads();
@@ -838,7 +1113,8 @@ static int plan_groups_per_cu() {
   if (v > 0) return v;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_decode_plan_kernel<D, BSL, PAIRS>,
-                                                   64 * kWavesPerGroup, 0) != hipSuccess || n < 1) {
+                                                   64 * kWavesPerGroup, plan_lds_bytes(D)) != hipSuccess ||
+      n < 1) {
     (void)hipGetLastError();
     n = 2;
   }
@@ -856,8 +1132,8 @@ static hipError_t launch_plan_db(const DecodeArgs& a, const int32_t* plan, int32
     const int64_t resident = (int64_t)(cus > 0 ? cus : 256) * plan_groups_per_cu<D, BSL, PAIRS>();
     grid = dim3((unsigned)std::max<int64_t>(1, std::min(units, resident)), 1);
   }
-  hipLaunchKernelGGL((gqa_decode_plan_kernel<D, BSL, PAIRS>), grid, dim3(64 * kWavesPerGroup), 0,
-                     st, a, plan, n_groups, work);
+  hipLaunchKernelGGL((gqa_decode_plan_kernel<D, BSL, PAIRS>), grid, dim3(64 * kWavesPerGroup),
+                     plan_lds_bytes(D), st, a, plan, n_groups, work);
   return hipGetLastError();
 }
 

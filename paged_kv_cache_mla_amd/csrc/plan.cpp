@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdlib>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -154,6 +155,18 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
     }
   }
 
+  // wave items of each item's range: a range that several waves read is mode 1 (or staged),
+  // one a single wave reads, for however many sharers, is streamed like a private one
+  std::vector<int32_t> run_items(items.size(), 1);
+  for (size_t k = 0; k < items.size();) {
+    size_t e = k + 1;
+    while (items[k].shared && e < items.size() && items[e].shared && items[e].seq == items[k].seq &&
+           items[e].lo == items[k].lo)
+      ++e;
+    for (size_t u = k; u < e; ++u) run_items[u] = (int32_t)(e - k);
+    k = e;
+  }
+
   // slots: every member's items in order of their first token
   std::vector<std::vector<std::pair<int32_t, int32_t>>> per_seq(batch);  // (lo, item)
   for (size_t k = 0; k < items.size(); ++k)
@@ -171,9 +184,21 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
     most = std::max<int32_t>(most, (int32_t)per_seq[b].size());
   }
 
-  // workgroups of four waves: the waves of one shared range together (one CU reads it once
-  // for all of them), longest work first; private items fill the free waves
+  // workgroups of four waves.  A shared range cut into k >= 3 wave items (more sharers than
+  // one wave's columns hold) is read by whole workgroups together: its items are split as
+  // evenly as possible over ceil(k / 4) workgroups of their own, staged (item mode 2: the four
+  // waves load the range once into LDS and each computes its sharers' partials from it; a
+  // workgroup of fewer than four items is padded with items of no sequence).  A range of two
+  // items goes to one workgroup as two independent waves that read it through L2 (mode 1).
+  // Single items, shared (one wave reads the range for all its sharers) or private, fill the
+  // free waves, longest work first.  Tuning only: KVATTN_PLAN_STAGE_MIN sets the k from which
+  // ranges are staged, KVATTN_PLAN_LAYOUT=same stages none.
+  const char* lay_env = std::getenv("KVATTN_PLAN_LAYOUT");
+  const std::string layout = lay_env ? lay_env : "stage";
+  const char* smin_env = std::getenv("KVATTN_PLAN_STAGE_MIN");
+  const size_t stage_min = layout == "stage" ? (smin_env ? (size_t)std::atoi(smin_env) : 3) : SIZE_MAX;
   std::vector<std::vector<int32_t>> groups;       // item indices
+  std::vector<char> staged;                       // per group
   std::vector<int32_t> open;                      // groups with free waves
   std::vector<int32_t> order(items.size());
   for (size_t k = 0; k < items.size(); ++k) order[k] = (int32_t)k;
@@ -184,37 +209,52 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
   std::vector<char> placed(items.size(), 0);
   for (int32_t k : order) {
     if (placed[k] || !items[k].shared) continue;
-    size_t e = k;
-    while (e + 1 < items.size() && items[e + 1].shared && items[e + 1].seq == items[k].seq &&
-           items[e + 1].lo == items[k].lo)
-      ++e;
-    // items[k] may not be the first of its run when an equal-work sort moved it; find the start
-    size_t s = k;
-    while (s > 0 && items[s - 1].shared && items[s - 1].seq == items[k].seq && items[s - 1].lo == items[k].lo)
-      --s;
-    size_t n = e - s + 1;
-    size_t at = s;
-    while (n >= (size_t)kWavesPerGroup) {
+    auto same = [&](size_t x) {
+      return items[x].shared && items[x].seq == items[k].seq && items[x].lo == items[k].lo;
+    };
+    size_t s = k, e = k;  // the run [s, e]; equal-work sorting may have put k inside it
+    while (s > 0 && same(s - 1)) --s;
+    while (e + 1 < items.size() && same(e + 1)) ++e;
+    const size_t n = e - s + 1;
+    if (n == 1) continue;  // a single item: placed with the private ones
+    if (n >= stage_min) {
+      const size_t ngr = (n + kWavesPerGroup - 1) / kWavesPerGroup;
+      size_t at = s;
+      for (size_t q = 0; q < ngr; ++q) {
+        const size_t take = n / ngr + (q < n % ngr ? 1 : 0);
+        groups.push_back({});
+        staged.push_back(1);
+        for (size_t w = 0; w < take; ++w) {
+          groups.back().push_back((int32_t)at);
+          placed[at++] = 1;
+        }
+      }
+      continue;
+    }
+    size_t left = n, at = s;
+    while (left >= (size_t)kWavesPerGroup) {
       groups.push_back({});
+      staged.push_back(0);
       for (int w = 0; w < kWavesPerGroup; ++w) {
         groups.back().push_back((int32_t)at);
         placed[at++] = 1;
       }
-      n -= kWavesPerGroup;
+      left -= kWavesPerGroup;
     }
-    if (n > 0) {
+    if (left > 0) {
       int32_t g = -1;
       for (int32_t o : open)
-        if (kWavesPerGroup - (int)groups[o].size() >= (int)n) {
+        if (kWavesPerGroup - (int)groups[o].size() >= (int)left) {
           g = o;
           break;
         }
       if (g < 0) {
         g = (int32_t)groups.size();
         groups.push_back({});
+        staged.push_back(0);
         open.push_back(g);
       }
-      for (size_t w = 0; w < n; ++w) {
+      for (size_t w = 0; w < left; ++w) {
         groups[g].push_back((int32_t)at);
         placed[at++] = 1;
       }
@@ -228,16 +268,20 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
     if (oi == open.size()) {
       open.push_back((int32_t)groups.size());
       groups.push_back({});
+      staged.push_back(0);
     }
     groups[open[oi]].push_back(k);
     placed[k] = 1;
   }
-  // most HBM bytes first: a workgroup reads each distinct range of its waves once (the waves
-  // of one shared range read it together), so its cost is the sum over its distinct ranges
-  std::vector<int64_t> gwork(groups.size(), 0);
+  // Order of the workgroups in the launch: longest wave item first.  Measured on MI355X on
+  // the 64-sequence shared pool, no other order was faster: most HBM bytes first, alternating
+  // staged and other workgroups, staged first, staged last.  KVATTN_PLAN_ORDER=bytes (tuning
+  // only) orders by HBM bytes: the sum over the distinct ranges of a workgroup's waves.
+  std::vector<int64_t> gwork(groups.size(), 0), glong(groups.size(), 0);
   for (size_t g = 0; g < groups.size(); ++g)
     for (size_t u = 0; u < groups[g].size(); ++u) {
       const Item& it = items[groups[g][u]];
+      glong[g] = std::max(glong[g], item_work[groups[g][u]]);
       bool seen = false;
       for (size_t v = 0; v < u; ++v) {
         const Item& o = items[groups[g][v]];
@@ -247,12 +291,22 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
     }
   std::vector<int32_t> gorder(groups.size());
   for (size_t g = 0; g < groups.size(); ++g) gorder[g] = (int32_t)g;
+  const char* ord = std::getenv("KVATTN_PLAN_ORDER");
+  const std::vector<int64_t>& key = (ord && std::string(ord) == "bytes") ? gwork : glong;
   std::stable_sort(gorder.begin(), gorder.end(),
-                   [&](int32_t x, int32_t y) { return gwork[x] > gwork[y]; });
+                   [&](int32_t x, int32_t y) { return key[x] > key[y]; });
+
+  // the workgroups in launch order
+  std::vector<std::vector<int32_t>> fin;
+  std::vector<char> fin_staged;
+  for (int32_t g : gorder) {
+    fin.push_back(groups[g]);
+    fin_staged.push_back(staged[g]);
+  }
 
   int64_t n_members = 0;
   for (const Item& it : items) n_members += (int64_t)it.members.size();
-  const int64_t ng = (int64_t)groups.size();
+  const int64_t ng = (int64_t)fin.size();
   const int64_t n_item_slots = ng * kWavesPerGroup;
   const int64_t need = kPlanHeader + batch + kItemInts * n_item_slots + 2 * n_members;
   if (need > INT32_MAX || ng > INT32_MAX / 64)
@@ -278,11 +332,16 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
   for (int b = 0; b < batch; ++b) np_out[b] = (int32_t)per_seq[b].size();
   int32_t moff = 0;
   for (int64_t g = 0; g < ng; ++g) {
-    const std::vector<int32_t>& gi = groups[gorder[g]];
+    const std::vector<int32_t>& gi = fin[g];
     for (int w = 0; w < kWavesPerGroup; ++w) {
       int32_t* o = it_out + kItemInts * (g * kWavesPerGroup + w);
-      if (w >= (int)gi.size()) {  // an idle wave
-        o[0] = 0; o[1] = 0; o[2] = 0; o[3] = 0; o[4] = 0; o[5] = 0;
+      const bool st = fin_staged[g];
+      if (w >= (int)gi.size()) {  // an idle wave, or a staged wave of no sequence
+        for (int i = 0; i < kItemInts; ++i) o[i] = 0;
+        if (st) {  // a staged workgroup's first item is a real one
+          const Item& f = items[gi[0]];
+          o[0] = f.seq; o[1] = f.lo; o[2] = f.hi; o[5] = 2;
+        }
         continue;
       }
       const Item& it = items[gi[w]];
@@ -291,7 +350,7 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
       o[2] = it.hi;
       o[3] = (int32_t)it.members.size();
       o[4] = moff;
-      o[5] = it.shared;
+      o[5] = st ? 2 : (run_items[gi[w]] > 1 ? 1 : 0);
       for (size_t u = 0; u < it.members.size(); ++u) {
         mem_out[2 * moff] = it.members[u];
         mem_out[2 * moff + 1] = slot_of[gi[w]][u];

@@ -5,8 +5,9 @@
 //                         wave
 //   nparts [batch]:       partials each sequence gets
 //   items  [4 G][kItemInts]: table row, first token, end token, members (0 = idle wave),
-//                         offset of its first member entry, shared flag (the range is read by
-//                         more than one wave item)
+//                         offset of its first member entry, mode (0 private, 1 a shared range
+//                         one wave reads for all its sharers, 2 staged: the workgroup's four
+//                         items have one range, loaded once into LDS for all four waves)
 //   members [M][2]:       sequence, partial slot
 #pragma once
 

@@ -23,7 +23,7 @@ def _to_device(arr, device):
 
 class DeviceCase:
     def __init__(self, case, device="cuda", seed=0, group_parts=0, plan=None, span_parts=0,
-                 claim=True):
+                 claim=False):
         self.case = case
         self.regions = [_to_device(r, device) for r in case.regions]
         self.pool = Pool(case.block_size, case.num_kv_heads, case.head_dim_k, case.head_dim_v,

@@ -6,6 +6,8 @@ tokens merges exactly), and the plan reads each shared range once.  No GPU: the 
 bookkeeping, and fake device addresses are never touched.
 """
 
+import functools
+
 import numpy as np
 import pytest
 
@@ -15,6 +17,12 @@ from synth import make_case
 
 FAKE = 0x7F0000000000
 HEADER, ITEM = 8, 6
+
+
+@functools.lru_cache(maxsize=None)
+def _case(name, variant):
+    """Cases are only read here: one build per (name, variant) for the whole module."""
+    return make_case(name, variant)
 
 
 def _pool_for(case):
@@ -39,6 +47,15 @@ def check_plan(plan, n_groups, max_parts, table, lens, begins, parts, bs, group,
     assert hdr[3] == 4 * n_groups and hdr[4] == members.shape[0] and hdr[6] == group
     mpw = 16 // group
     assert hdr[7] == mpw and max_parts == max(1, int(nparts.max()))
+    # a staged workgroup (mode 2): all four items mode 2 over one range, at least two of them
+    # with sequences (the rest padding); modes 0 / 1 only in workgroups of independent waves
+    for g in range(n_groups):
+        gi = items[4 * g:4 * g + 4]
+        if (gi[:, 5] == 2).any():
+            assert (gi[:, 5] == 2).all() and (gi[:, :3] == gi[0, :3]).all(), g
+            assert (gi[:, 3] > 0).sum() >= 2
+        else:
+            assert set(gi[:, 5].tolist()) <= {0, 1}
     covered = [[] for _ in range(batch)]       # (lo, hi, slot) per sequence
     for x, (seq, lo, hi, nmem, moff, shared) in enumerate(items):
         if nmem == 0:
@@ -72,7 +89,7 @@ def _case_arrays(case):
 
 @pytest.mark.parametrize("variant", ["small", "full"])
 def test_prefix_pool_plan_covers_each_sequence_and_reads_shared_blocks_once(variant):
-    case = make_case("prefix_shared", variant)
+    case = _case("prefix_shared", variant)
     pool = _pool_for(case)
     table, lens, begins, parts = _case_arrays(case)
     plan, ng, mp = decode_plan(pool, case.num_q_heads, table, lens, begins, parts)
@@ -89,14 +106,59 @@ def test_prefix_pool_plan_covers_each_sequence_and_reads_shared_blocks_once(vari
     # sharing is found block by block: the plan reads exactly the unique token slots
     assert read == unique, (read, unique, logical)
     assert read < 0.5 * logical
-    # the waves of a shared range (up to four) sit in one workgroup
+    if variant == "full":   # ranges of every kind: staged, two waves, one wave
+        assert check_range_modes(items, members) == {1, 2, 3}
+    check_range_modes(items, members)
+
+
+def check_range_modes(items, members, stage_min=3):
+    """Placement of a range's wave items by their number k: k >= stage_min, ceil(k / 4)
+    staged workgroups of their own (mode 2), sizes within one; 2 <= k < stage_min, one
+    workgroup, mode 1; k = 1, mode 0 (read once, streamed), shared or private."""
     by_range = {}
-    for x, (s, lo, hi, n, _, shared) in enumerate(items):
-        if n > 0 and shared:
-            by_range.setdefault((s, lo), []).append(x // 4)
-    for wgs in by_range.values():
-        if len(wgs) <= 4:
-            assert len(set(wgs)) == 1
+    for x, (s, lo, hi, n, off, mode) in enumerate(items):
+        if n > 0:
+            by_range.setdefault((s, lo, hi), []).append((x // 4, mode, n))
+    kinds = set()
+    for v in by_range.values():
+        k = len(v)
+        wgs = sorted({g for g, _, _ in v})
+        modes = {m for _, m, _ in v}
+        if k >= stage_min:
+            assert modes == {2} and len(wgs) == -(-k // 4)
+            sizes = [sum(1 for g, _, _ in v if g == w) for w in wgs]
+            assert max(sizes) - min(sizes) <= 1
+        elif k >= 2:
+            assert modes == {1} and len(wgs) == 1
+        else:
+            assert modes == {0}
+        kinds.add(min(k, stage_min))
+    return kinds
+
+
+@pytest.mark.parametrize("layout,stage_min", [("same", 99), ("stage", 2), ("stage", 4)])
+def test_placement_switches_keep_items_and_slots(monkeypatch, layout, stage_min):
+    """The tuning switches (KVATTN_PLAN_LAYOUT=same: no staged workgroup; KVATTN_PLAN_STAGE_MIN:
+    the k from which a range is staged) change where the wave items run, not the items, their
+    members or their slots."""
+    case = _case("prefix_shared", "full")
+    pool = _pool_for(case)
+    table, lens, begins, parts = _case_arrays(case)
+    group = case.num_q_heads // case.num_kv_heads
+    plan_d, ng_d, mp_d = decode_plan(pool, case.num_q_heads, table, lens, begins, parts)
+    items_d, members_d = check_plan(plan_d, ng_d, mp_d, table, lens, begins, parts,
+                                    case.block_size, group)
+    monkeypatch.setenv("KVATTN_PLAN_LAYOUT", layout)
+    monkeypatch.setenv("KVATTN_PLAN_STAGE_MIN", str(stage_min))
+    plan, ng, mp = decode_plan(pool, case.num_q_heads, table, lens, begins, parts)
+    items, members = check_plan(plan, ng, mp, table, lens, begins, parts, case.block_size, group)
+    check_range_modes(items, members, stage_min)
+    assert mp == mp_d and ((items[:, 5] == 2).any() == (layout == "stage"))
+
+    def entries(it, mem):
+        return sorted((int(s), int(lo), int(hi), int(m), int(sl)) for s, lo, hi, n, off, _ in it
+                      for m, sl in mem[off:off + n])
+    assert entries(items, members) == entries(items_d, members_d)
 
 
 def test_private_layer_plan_is_one_item_per_span():
