@@ -339,11 +339,12 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  * same set (an invalid id: a set of its own sequence) is taken once, from the set's lowest
  * sequence, and cut into pieces of at most span_parts * part_tokens tokens (span_parts 0: as
  * many whole partitions as a wave's window of 127 block ids holds); a piece becomes wave
- * items of up to 16 / (Hq / Hkv) of its sequences each.  A piece of k >= 2 items runs in
+ * items of up to 16 / (Hq / Hkv) of its sequences each.  A piece of k >= 3 items runs in
  * ceil(k / 4) workgroups of its own whose four waves stage the range through LDS together
  * (mode 2: it crosses HBM once per such workgroup; a workgroup of fewer items is padded with
- * items of no sequence); single items fill workgroups of four independent waves (mode 1, a
- * shared range one wave reads for all its sharers; mode 0, private).  Every sequence's range [tok_begin, ctx_len) is
+ * items of no sequence); the two items of a piece of k = 2 run as two waves of one workgroup
+ * (mode 1); single items, shared or private, are streamed by one wave (mode 0).  Workgroups
+ * other than staged ones hold four independent waves.  Every sequence's range [tok_begin, ctx_len) is
  * thus covered exactly once by the items it belongs to; its partials are written in the
  * order of their first tokens, slots 0 .. nparts[b] - 1.  The plan is an int32 array:
  *   header[8] = {magic, batch, n_groups, 4 n_groups, member entries M, max_parts,
@@ -365,9 +366,10 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  * device: for every item and KV head, the attention of its sequences' query heads over its
  * token range, read once through the table row it names; sequence b's partial of item k goes
  * to o_part[b][h][slot] / lse_part[b][h][slot] (same formulas as kvattn_decode_partial) and
- * nparts_dev[b] receives the plan's count, so kvattn_merge_lse completes the step.  Modes 0
- * and 1 stream their range with non-temporal loads; a mode-2 workgroup (all four items mode 2
- * with one range, else KVATTN_ERR_BAD_SEQ) loads it into LDS once for its four waves.
+ * nparts_dev[b] receives the plan's count, so kvattn_merge_lse completes the step.  Mode 0
+ * streams its range with non-temporal loads, mode 1 reads it with cache-retaining loads (the
+ * other waves of its range hit in L2), and a mode-2 workgroup (all four items mode 2 with one
+ * range, else KVATTN_ERR_BAD_SEQ) loads it into LDS once for its four waves.
  *   q, q_dtype, batch, num_q_heads, scale, table_dev, max_blocks, o_part, lse_part, err_dev:
  *                as for kvattn_decode_partial (max_parts >= the plan's max_parts)
  *   plan_dev     device int32 copy of the plan (all plan_len entries); n_groups its workgroups

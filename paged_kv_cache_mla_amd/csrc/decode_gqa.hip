@@ -690,11 +690,12 @@ __host__ __device__ constexpr uint32_t plan_lds_bytes(int d) { return 2u * (2 * 
 // An item is a token range of one table row and up to 16 / group sequences that hold that
 // range in the same blocks: column n of the MFMA tiles is head n % group of member n / group,
 // so one pass over the range's keys and values serves every member, and each member's
-// partial of the range goes to its own slot.  Item modes: 0, a private range, and 1, a range
-// one wave reads for all its sharers, are streamed with non-temporal loads (each is read once
-// either way); 2, staged: the workgroup's four waves share one range (their sharers split
-// between them) and read it once through LDS (gqa_range_staged; padding waves with no
-// sequence still load their share).
+// partial of the range goes to its own slot.  Item modes: 0, a range this wave alone reads
+// (private, or one wave for all its sharers), streamed with non-temporal loads; 1, a range
+// another wave of the workgroup reads too (its other sharers), read with cache-retaining
+// loads so that the second read hits in L2; 2, staged: the workgroup's four waves share one
+// range (their sharers split between them) and read it once through LDS (gqa_range_staged;
+// padding waves with no sequence still load their share).
 // Every wave of a workgroup reads all four of its items, so the staged decision, and the
 // range a staged workgroup loops over, are the same for all of them.  An idle wave returns at
 // once; an item outside the call's arguments sets KVATTN_ERR_BAD_SEQ.

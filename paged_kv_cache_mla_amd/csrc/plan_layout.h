@@ -5,9 +5,10 @@
 //                         wave
 //   nparts [batch]:       partials each sequence gets
 //   items  [4 G][kItemInts]: table row, first token, end token, members (0 = idle wave),
-//                         offset of its first member entry, mode (0 private, 1 a shared range
-//                         one wave reads for all its sharers, 2 staged: the workgroup's four
-//                         items have one range, loaded once into LDS for all four waves)
+//                         offset of its first member entry, mode (0: the range is read by this
+//                         wave alone, 1: also by another wave of the workgroup, through L2,
+//                         2: staged, the workgroup's four items have one range, loaded once
+//                         into LDS for all four waves)
 //   members [M][2]:       sequence, partial slot
 #pragma once
 
