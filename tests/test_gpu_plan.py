@@ -226,3 +226,83 @@ def test_claiming_launch_equals_one_unit_per_workgroup(name):
     assert int(claim.step.err.item()) == 0
     o_ref, _ = oc.full_reference(case)
     assert oc.out_error(case, o_f.cpu().numpy(), o_ref) <= oc.out_tol(case)
+
+
+def _one_row_case(nseq, length, begin, bs, hkv, d, hq, seed):
+    """`nseq` sequences holding one table row over the same tokens [begin, length): every range
+    has nseq sharers."""
+    rng = np.random.default_rng(seed)
+    nblk = -(-length // bs)
+    pool_blocks = nblk + 6
+    ids = rng.permutation(pool_blocks).astype(np.int32)
+    table = np.tile(ids[:nblk], (nseq, 1))
+    return _custom_case(bs, hkv, d, hq, table, [length] * nseq, [begin] * nseq, bs * 4,
+                        pool_blocks, seed)
+
+
+STAGED = [(256, 16, 2, 1237, 0), (128, 32, 4, 901, 21), (64, 16, 1, 2047, 5)]
+
+
+@pytest.mark.parametrize("d,hq,hkv,length,begin", STAGED,
+                         ids=[f"d{s[0]}-hq{s[1]}-hkv{s[2]}-L{s[3]}-b{s[4]}" for s in STAGED])
+def test_staged_ranges_ignore_nan_in_unused_slots(d, hq, hkv, length, begin):
+    """Eight sequences on one table row: every range has eight sharers, which at 8 or 16 query
+    heads per KV head fill 4 or 8 wave items, so every range is staged (mode 2).  Every token
+    slot outside [begin, length) holds a NaN bit pattern; the staged workgroups read whole
+    32-token stages, and the lines of a tile or stage past the range load other tiles again,
+    so those slots reach the waves and must get zero weight and zeroed V.  Ragged ends, a start
+    inside a block, pairs not a multiple of the ring depth."""
+    from tests.test_gpu_parity import _poison_unused_slots
+    case = _poison_unused_slots(_one_row_case(8, length, begin, 16, hkv, d, hq, 1013 + d))
+    _say(f"[staged] d={d} hq={hq} hkv={hkv} L={length} begin={begin}")
+    dc, o, lse = _run_plan(case, span_parts=2)
+    _, _, items, _ = parse(dc.step.plan, case.batch)
+    assert (items[items[:, 3] > 0, 5] == 2).all()
+    assert int(dc.step.err.item()) == 0
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    worst = _check_items(case, dc)
+    _say(f"[staged] out error {err:.3e}, worst item {worst:.3e}")
+    assert err <= oc.out_tol(case)
+    assert float(np.max(np.abs(lse - lse_ref))) <= oc.lse_tol(case)
+
+
+def test_staged_range_with_an_invalid_id_is_flagged():
+    """A block id that turns invalid inside a staged range after the plan was made (the plan
+    is built from the host table, the device table changes): KVATTN_ERR_BAD_BLOCK, finite
+    output, the block's tokens contribute nothing to its range's partials, and every other
+    partial still equals the oracle's."""
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    case = _one_row_case(8, 1500, 0, 16, 2, 256, 16, 1021)
+    dc = DeviceCase(case, plan=True, span_parts=1)
+    bad = dc.table.copy()
+    bad[:, 40] = sum(case.region_blocks) + 3          # tokens [640, 656)
+    dc.step.table_dev.copy_(torch.from_numpy(bad))
+    o, lse = dc.run()
+    torch.cuda.synchronize()
+    assert int(dc.step.err.item()) & _lib.ERR_BAD_BLOCK
+    assert np.isfinite(o.cpu().numpy()).all()
+    hdr, nparts, items, members = parse(dc.step.plan, case.batch)
+    o_part = dc.step.o_part.cpu().numpy()
+    qf = oc.q_f64(case)
+    lay = oc.layout_of(case)
+    holding = 0
+    for seq, lo, hi, nmem, moff, mode in items:
+        if nmem == 0:
+            continue
+        assert mode == 2
+        spans = [(lo, hi)]
+        if lo < 656 and hi > 640:      # the range holds the invalid block: the rest of it
+            spans = [(a, b) for a, b in ((lo, 640), (656, hi)) if b > a]
+            holding += 1
+        for m, slot in members[moff:moff + nmem]:
+            parts = [oracle.gather_sequence(lay, case.regions, case.region_blocks, case.table[m], a, b)
+                     for a, b in spans]
+            k = np.concatenate([p[0] for p in parts])
+            v = np.concatenate([p[1] for p in parts])
+            o_ref, _ = oracle.attend(qf[m], k, v, case.scale)
+            err = float(np.max(np.abs(o_part[m, :, slot] - o_ref))) / float(np.max(np.abs(o_ref)))
+            assert err <= oc.out_tol(case), (m, slot, lo, hi, err)
+    assert holding > 0
