@@ -380,8 +380,9 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  *                workgroup ran a unit: the result is the same bit for bit).  The counters must
  *                be zero before the first call (e.g. zero-filled once); every call that
  *                completes leaves them zero again.  Calls that overlap on one work_dev race.
- * A plan whose header disagrees with the arguments, or an item outside them, sets
- * KVATTN_ERR_BAD_SEQ in *err_dev and is not run (the counters are then left as they are);
+ * A plan whose header disagrees with the arguments (its max_parts above the call's included),
+ * or an item outside them, sets KVATTN_ERR_BAD_SEQ in *err_dev and is not run (the counters
+ * are then left as they are);
  * invalid block ids set KVATTN_ERR_BAD_BLOCK and contribute nothing.  Errors: E_INVAL (null
  * pointers, misalignment (work_dev: 8 bytes), sizes), E_UNSUPPORTED
  * (as for kvattn_decode_plan, or q_dtype != kv_dtype), E_HIP.

@@ -792,14 +792,16 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel
   const int lane = threadIdx.x & 63;
   const int32_t* np = plan + kPlanHeader;
   const bool hdr_ok = plan[0] == kPlanMagic && plan[1] == a.batch && plan[2] == n_groups &&
-                      plan[3] == kWavesPerGroup * n_groups && plan[6] == a.group &&
-                      plan[7] >= 1 && plan[7] * a.group <= 16;
+                      plan[3] == kWavesPerGroup * n_groups && plan[5] >= 1 &&
+                      plan[5] <= a.max_parts && plan[6] == a.group && plan[7] >= 1 &&
+                      plan[7] * a.group <= 16;
   if (!hdr_ok) {  // every workgroup returns here (the counters are left as they are)
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
     return;
   }
   if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup) a.nparts[i] = np[i];
+    for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup)
+      a.nparts[i] = min(max(np[i], 0), a.max_parts);
   const int units = n_groups * a.hkv;
   if (!work) {  // grid (n_groups, Hkv): one unit per workgroup (an empty plan: no unit)
     if ((int)blockIdx.x < n_groups)

@@ -185,6 +185,17 @@ def test_plan_with_invalid_ids_and_a_stale_header():
     torch.cuda.synchronize()
     assert int(dc2.step.err.item()) & _lib.ERR_BAD_SEQ
     assert (dc2.step.nparts.cpu().numpy() == -5).all()
+    # buffers sized for fewer partials than the plan writes: refused the same way
+    from paged_kv_cache_mla_amd.api import decode_partial_plan
+    dc3 = DeviceCase(case)
+    dc3.step.nparts.fill_(-5)
+    st = dc3.step
+    decode_partial_plan(st.pool, dc3.q, dc3.q_dtype, case.num_q_heads, case.scale, st.table_dev,
+                        st.max_blocks, st.plan_dev, st.n_groups, st.max_parts - 1, st.o_part,
+                        st.lse_part, st.nparts, st.err)
+    torch.cuda.synchronize()
+    assert int(st.err.item()) & _lib.ERR_BAD_SEQ
+    assert (st.nparts.cpu().numpy() == -5).all()
 
 
 def test_plan_relabelled_blocks_give_identical_bits():
