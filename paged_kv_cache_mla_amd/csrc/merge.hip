@@ -13,9 +13,10 @@
 // (g, c) of a [groups x dv/4] arrangement owns 16-byte column c of partitions g, g + groups,
 // ...  The merge is bound by the latency of a few dependent steps, not by bandwidth, so the
 // order is: issue the loads of
-// the thread's first kR partial columns and of the first lse values at once, before the
-// partition count is known (bounded by max_parts), then take the block max, write the weights
-// to LDS while summing them, and only then consume the partial columns already in registers.
+// the thread's first kSpec partial columns and of the first lse values at once, before the
+// partition count is known (bounded by max_parts), then its next kR - kSpec columns bounded
+// by the count, then take the block max, write the weights to LDS while summing them, and
+// only then consume the partial columns already in registers.
 // Partitions beyond kR * groups (long sequences, wide heads) follow in further chunks of
 // kR * groups.  Every sum runs in a fixed order, so the result is bitwise reproducible.
 // The two wave kernels below take one wave per (sequence, head) with every partial in
@@ -32,6 +33,7 @@ static constexpr float kNegInfG = -__builtin_huge_valf();
 static constexpr int kThreads = 256;
 static constexpr int kWts = 2048;  // partitions whose weights are kept in LDS
 static constexpr int kR = 16;      // partial columns per thread held in registers
+static constexpr int kSpec = 4;    // of which loaded before the partition count is known
 
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
@@ -71,16 +73,24 @@ __global__ __launch_bounds__(kThreads) void merge_lse_kernel(MergeArgs a) {
   const f32x4* orow = reinterpret_cast<const f32x4*>(a.o_part + row * a.max_parts * a.dv);
 
   // 1. loads issued before the partition count arrives: the partial columns of the first
-  //    kR * groups partition slots and the first 256 lse slots, bounded by max_parts (slots
-  //    past the sequence's count hold stale data and are discarded by selection below)
+  //    kSpec * groups partition slots and the first 256 lse slots, bounded by max_parts
+  //    (slots past the sequence's count hold stale data and are discarded by selection
+  //    below); the rest of the first chunk follows as soon as the count is known, bounded by
+  //    it, so a short sequence in a call sized for long ones reads only its own partials
   f32x4 ov[kR];
 #pragma unroll
   for (int k = 0; k < kR; ++k) {
     const int p = g + k * groups;
-    ov[k] = (active && p < a.max_parts) ? orow[(int64_t)p * cols + c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    ov[k] = (active && k < kSpec && p < a.max_parts) ? orow[(int64_t)p * cols + c]
+                                                      : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float l0 = tid < a.max_parts ? lrow[tid] : kNegInfG;
   const int np = np_raw < 0 ? 0 : (np_raw > a.max_parts ? a.max_parts : np_raw);
+#pragma unroll
+  for (int k = kSpec; k < kR; ++k) {
+    const int p = g + k * groups;
+    if (active && p < np) ov[k] = orow[(int64_t)p * cols + c];
+  }
 
   // 2. M = max over partitions (and the external partial)
   float mx = lx;
