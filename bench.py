@@ -1018,7 +1018,8 @@ def main():
             "head_dim_v": case.head_dim_v,
             "block_size": case.block_size,
             "part_tokens": int(case.part_tokens[0]),
-            "group_parts": group_parts,
+            # the plan decomposes by its own wave items: no group_parts
+            "group_parts": group_parts if dc.step.plan is None else None,
             "group_parts_auto": dc.step.auto,
             **({"plan_workgroups": dc.step.n_groups, "plan_max_parts": dc.step.max_parts,
                 "span_parts": args.span_parts, "claim": args.claim}
