@@ -317,3 +317,36 @@ def test_staged_range_with_an_invalid_id_is_flagged():
             err = float(np.max(np.abs(o_part[m, :, slot] - o_ref))) / float(np.max(np.abs(o_ref)))
             assert err <= oc.out_tol(case), (m, slot, lo, hi, err)
     assert holding > 0
+
+
+def test_plan_with_empty_sequences_and_an_empty_batch():
+    """A sequence with no tokens (tok_begin = ctx_len) gets no wave item and no partial: its
+    output is zero and its lse -inf, like the oracle's; the others are unaffected.  A batch
+    with no tokens at all plans zero workgroups, and the launch only writes zero counts."""
+    bs, hkv, d, hq = 16, 2, 128, 16
+    rng = np.random.default_rng(77)
+    nseq, nblk = 6, 20
+    pool_blocks = 2 * nblk + nseq * nblk + 8
+    table = _sharing_table(rng, nseq, nblk, pool_blocks, bs)
+    lens = [nblk * bs - 3] * nseq
+    begins = [0] * nseq
+    begins[1] = lens[1]                 # empty at its end
+    begins[4] = lens[4] = 5 * bs + 2     # empty inside a block
+    for s in range(nseq):
+        table[s, -(-lens[s] // bs):] = -1
+    case = _custom_case(bs, hkv, d, hq, table, lens, begins, bs * 4, pool_blocks)
+    dc, o, lse = _run_plan(case, span_parts=2)
+    assert int(dc.step.err.item()) == 0
+    nparts = dc.step.nparts.cpu().numpy()
+    assert nparts[1] == 0 and nparts[4] == 0 and (np.delete(nparts, [1, 4]) > 0).all()
+    o_ref, lse_ref = oc.full_reference(case)
+    assert (o[[1, 4]] == 0).all() and np.isneginf(lse[[1, 4]]).all()
+    assert oc.out_error(case, o, o_ref) <= oc.out_tol(case)
+    keep = np.delete(np.arange(nseq), [1, 4])
+    assert float(np.max(np.abs(lse[keep] - lse_ref[keep]))) <= oc.lse_tol(case)
+    # no tokens anywhere: an empty plan
+    empty = _custom_case(bs, hkv, d, hq, table, lens, lens, bs * 4, pool_blocks)
+    dc0, o0, lse0 = _run_plan(empty)
+    assert dc0.step.n_groups == 0 and int(dc0.step.err.item()) == 0
+    assert (dc0.step.nparts.cpu().numpy() == 0).all()
+    assert (o0 == 0).all() and np.isneginf(lse0).all()
