@@ -779,8 +779,10 @@ __device__ __forceinline__ void gqa_plan_item(const DecodeArgs& a, const int32_t
 // claims unit gridDim.x + work[0]++ until none are left, so the CUs (and XCDs) that finish
 // first take the rest; a unit's partials do not depend on which workgroup ran it.  The last
 // workgroup to leave sets work[0] = work[1] = 0 again for the next launch.  Workgroup 0 also
-// writes every sequence's partial count.
-template <int D, int BSL, int PAIRS>
+// writes every sequence's partial count.  CLAIM selects the claiming form at compile time:
+// the one-unit form then holds no claim loop, whose state would add to the register pressure
+// (and spill stores) of the item path.
+template <int D, int BSL, int PAIRS, bool CLAIM>
 __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel(DecodeArgs a,
                                                                                const int32_t* plan,
                                                                                int32_t n_groups,
@@ -802,12 +804,12 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup)
       a.nparts[i] = min(max(np[i], 0), a.max_parts);
-  const int units = n_groups * a.hkv;
-  if (!work) {  // grid (n_groups, Hkv): one unit per workgroup (an empty plan: no unit)
+  if constexpr (!CLAIM) {  // grid (n_groups, Hkv): one unit per workgroup (an empty plan: none)
     if ((int)blockIdx.x < n_groups)
       gqa_plan_item<D, BSL, PAIRS>(a, plan, blockIdx.x, blockIdx.y, wv, lane, lds);
     return;
   }
+  const int units = n_groups * a.hkv;
   int u = blockIdx.x;
   while (u < units) {  // uniform over the workgroup
     gqa_plan_item<D, BSL, PAIRS>(a, plan, u / a.hkv, u % a.hkv, wv, lane, lds);
@@ -1115,7 +1117,7 @@ static int plan_groups_per_cu() {
   int v = cached.load(std::memory_order_relaxed);
   if (v > 0) return v;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_decode_plan_kernel<D, BSL, PAIRS>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_decode_plan_kernel<D, BSL, PAIRS, true>,
                                                    64 * kWavesPerGroup, plan_lds_bytes(D)) != hipSuccess ||
       n < 1) {
     (void)hipGetLastError();
@@ -1135,8 +1137,12 @@ static hipError_t launch_plan_db(const DecodeArgs& a, const int32_t* plan, int32
     const int64_t resident = (int64_t)(cus > 0 ? cus : 256) * plan_groups_per_cu<D, BSL, PAIRS>();
     grid = dim3((unsigned)std::max<int64_t>(1, std::min(units, resident)), 1);
   }
-  hipLaunchKernelGGL((gqa_decode_plan_kernel<D, BSL, PAIRS>), grid, dim3(64 * kWavesPerGroup),
-                     plan_lds_bytes(D), st, a, plan, n_groups, work);
+  if (work)
+    hipLaunchKernelGGL((gqa_decode_plan_kernel<D, BSL, PAIRS, true>), grid,
+                       dim3(64 * kWavesPerGroup), plan_lds_bytes(D), st, a, plan, n_groups, work);
+  else
+    hipLaunchKernelGGL((gqa_decode_plan_kernel<D, BSL, PAIRS, false>), grid,
+                       dim3(64 * kWavesPerGroup), plan_lds_bytes(D), st, a, plan, n_groups, work);
   return hipGetLastError();
 }
 
