@@ -774,7 +774,7 @@ __device__ __forceinline__ void gqa_plan_item(const DecodeArgs& a, const int32_t
 
 // Decode over a plan: workgroups of four independent waves.  The plan's units are its
 // (workgroup, KV head) pairs, unit u = group u / Hkv, KV head u % Hkv, in the plan's order
-// (most bytes first).  Without a work counter (work == NULL) workgroup x runs unit x.  With
+// (longest wave item first).  Without a work counter (work == NULL) workgroup x runs unit x.  With
 // one, the grid is the workgroups the device holds at once: workgroup x runs unit x, then
 // claims unit gridDim.x + work[0]++ until none are left, so the CUs (and XCDs) that finish
 // first take the rest; a unit's partials do not depend on which workgroup ran it.  The last

@@ -120,7 +120,6 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
   // wave items of up to mpw sequences
   std::vector<Item> items;
   std::vector<int64_t> item_work;  // tokens
-  const std::vector<int32_t> none;
   for (int b = 0; b < batch; ++b) {
     const int beg = tok_begin ? tok_begin[b] : 0;
     const int len = ctx_lens[b];
