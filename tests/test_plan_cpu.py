@@ -279,3 +279,69 @@ def test_decode_partial_plan_validation_without_gpu():
     assert call(qd=_lib.F32) == _lib.E_UNSUPPORTED
     mla = Pool(64, 1, 576, 512, "bf16", True, [(FAKE, 4)])
     assert call(p=mla) == _lib.E_UNSUPPORTED
+
+
+def _random_pool_case(rng):
+    """A random shared pool: sequences that take prefixes of random length from a few stems
+    (some of them nested), then private blocks; random starts (some inside a block), ends,
+    block size, group size and span; now and then an invalid id or an empty sequence."""
+    bs = int(rng.choice([16, 32, 64]))
+    hkv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 4, 6, 8, 16]))
+    nseq = int(rng.integers(1, 24))
+    nblk = int(rng.integers(1, 90))
+    nstem = int(rng.integers(1, 4))
+    pool_blocks = nstem * nblk + nseq * nblk + 4
+    ids = rng.permutation(pool_blocks).astype(np.int32)
+    stems = [ids[s * nblk:(s + 1) * nblk] for s in range(nstem)]
+    pos = nstem * nblk
+    table = np.full((nseq, nblk), -1, np.int32)
+    lens = np.zeros(nseq, np.int32)
+    begins = np.zeros(nseq, np.int32)
+    for s in range(nseq):
+        nb = int(rng.integers(1, nblk + 1))
+        k = int(rng.integers(0, nb + 1))
+        table[s, :k] = stems[int(rng.integers(0, nstem))][:k]
+        table[s, k:nb] = ids[pos:pos + nb - k]
+        pos += nb - k
+        lens[s] = nb * bs - int(rng.integers(0, bs))
+        r = rng.random()
+        begins[s] = 0 if r < 0.6 else (int(rng.integers(0, lens[s] + 1)) if r < 0.95 else lens[s])
+        if rng.random() < 0.1 and nb > 1:
+            table[s, int(rng.integers(0, nb))] = pool_blocks + 7       # invalid: private
+    parts = np.full(nseq, bs * int(rng.choice([1, 2, 4, 8])), np.int32)
+    span = int(rng.integers(0, 4))
+    while span > 0 and span * parts[0] // bs >= 128:
+        span -= 1
+    return bs, hkv, group, table, lens, begins, parts, span, pool_blocks
+
+
+@pytest.mark.parametrize("seed", range(100))
+def test_random_pools_plan_invariants(seed):
+    """The plan invariants on random pools: coverage of every sequence's tokens exactly once,
+    slots in token order, sharing only over identical blocks and extents, the window, the
+    placement rules; and, where no id is invalid, exactly the unique token slots read."""
+    rng = np.random.default_rng(5000 + seed)
+    bs, hkv, group, table, lens, begins, parts, span, pool_blocks = _random_pool_case(rng)
+    pool = Pool(bs, hkv, 64, 64, "bf16", False, [(FAKE, pool_blocks)])
+    plan, ng, mp = decode_plan(pool, hkv * group, table, lens, begins, parts, span_parts=span)
+    items, members = check_plan(plan, ng, mp, table, lens, begins, parts, bs, group,
+                                span=span if span else 128)
+    check_range_modes(items, members)
+    if not (table >= pool_blocks).any():
+        # every distinct (position, block id, token extent) key is read once: blocks held with
+        # the same extent are read once for all their holders, and a block two sequences hold
+        # with different extents (a start or an end inside it) once per extent
+        ranges = {(int(s), int(lo), int(hi)) for s, lo, hi, n, _, _ in items if n > 0}
+        read = sum(hi - lo for _, lo, hi in ranges)
+        keys = set()
+        for b in range(len(lens)):
+            for i in range(begins[b] // bs, (lens[b] - 1) // bs + 1 if lens[b] > begins[b] else 0):
+                keys.add((i, int(table[b, i]), max(int(begins[b]), i * bs), min(int(lens[b]), (i + 1) * bs)))
+        assert read == sum(hi - lo for _, _, lo, hi in keys), (read, len(keys))
+        if (begins == 0).all():          # equal starts: shared blocks differ only in their last
+            slots = set()                # block's extent, so at most one extra read per holder
+            for b in range(len(lens)):
+                t = np.arange(begins[b], lens[b])
+                slots.update(zip(table[b][t // bs].tolist(), (t % bs).tolist()))
+            assert len(slots) <= read <= len(slots) + bs * len(lens)
