@@ -350,3 +350,46 @@ def test_plan_with_empty_sequences_and_an_empty_batch():
     assert dc0.step.n_groups == 0 and int(dc0.step.err.item()) == 0
     assert (dc0.step.nparts.cpu().numpy() == 0).all()
     assert (o0 == 0).all() and np.isneginf(lse0).all()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_pools_plan_matches_oracle(seed):
+    """Random small shared pools (stems of random prefix length, some sequences starting
+    inside a block or empty, block sizes 16 / 32 / 64, head dims 64 / 128 / 256, 1 to 16 query
+    heads per KV head, spans 0 to 3): every item's partial of every member and the merged
+    output against the oracle."""
+    rng = np.random.default_rng(9000 + seed)
+    bs = int(rng.choice([16, 32, 64]))
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2]))
+    group = int(rng.choice([1, 2, 4, 8, 16]))
+    nseq, nblk, nstem = int(rng.integers(2, 12)), int(rng.integers(2, 30)), int(rng.integers(1, 3))
+    pool_blocks = nstem * nblk + nseq * nblk + 4
+    ids = rng.permutation(pool_blocks).astype(np.int32)
+    table = np.full((nseq, nblk), -1, np.int32)
+    lens, begins, pos = [], [], nstem * nblk
+    for s in range(nseq):
+        nb = int(rng.integers(1, nblk + 1))
+        k = int(rng.integers(0, nb + 1))
+        stem = int(rng.integers(0, nstem))
+        table[s, :k] = ids[stem * nblk:stem * nblk + k]
+        table[s, k:nb] = ids[pos:pos + nb - k]
+        pos += nb - k
+        length = nb * bs - int(rng.integers(0, bs))
+        r = rng.random()
+        lens.append(length)
+        begins.append(0 if r < 0.7 else (int(rng.integers(0, length + 1)) if r < 0.95 else length))
+    parts = bs * int(rng.choice([1, 2, 4]))
+    span = int(rng.integers(0, 4))
+    case = _custom_case(bs, hkv, d, hkv * group, table, lens, begins, parts, pool_blocks, 1200 + seed)
+    _say(f"[plan-rand] seed={seed} bs={bs} d={d} hkv={hkv} group={group} nseq={nseq} span={span}")
+    dc, o, lse = _run_plan(case, span_parts=span)
+    assert int(dc.step.err.item()) == 0
+    o_ref, lse_ref = oc.full_reference(case)
+    err = oc.out_error(case, o, o_ref)
+    worst = _check_items(case, dc)
+    _say(f"[plan-rand] out error {err:.3e}, worst item {worst:.3e}")
+    assert err <= oc.out_tol(case)
+    live = np.asarray(lens) > np.asarray(begins)
+    assert float(np.max(np.abs(lse[live] - lse_ref[live]))) <= oc.lse_tol(case)
+    assert np.isneginf(lse[~live]).all() and (o[~live] == 0).all()
