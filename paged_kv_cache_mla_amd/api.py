@@ -172,12 +172,22 @@ def decode_plan(pool, num_q_heads, table, ctx_lens, tok_begin, part_tokens, span
     ng, mp = ctypes.c_int32(), ctypes.c_int32()
     args = (pool.handle, int(ctx.shape[0]), int(num_q_heads), _i32p(t), int(t.shape[1]), _i32p(ctx),
             _i32p(beg), _i32p(part), int(span_parts))
-    check(lib.kvattn_decode_plan(*args, None, 0, ctypes.byref(n), ctypes.byref(ng),
-                                 ctypes.byref(mp)), "decode_plan (size)")
-    plan = np.zeros(n.value, np.int32)
-    check(lib.kvattn_decode_plan(*args, _i32p(plan), plan.size, ctypes.byref(n), ctypes.byref(ng),
-                                 ctypes.byref(mp)), "decode_plan")
-    return plan, int(ng.value), int(mp.value)
+    # one call into a buffer of the largest length a plan can have: with P block positions,
+    # at most P member entries (each covers a position of its sequence), as many items, and
+    # four wave slots of six ints per item; the planner writes every entry it reports
+    bs = int(pool.block_size)
+    b0 = np.zeros_like(ctx) if tok_begin is None else beg
+    live = ctx > b0
+    positions = int(np.sum((ctx[live] - 1) // bs - b0[live] // bs + 1))
+    plan = np.empty(8 + int(ctx.shape[0]) + 26 * positions, np.int32)
+    st = lib.kvattn_decode_plan(*args, _i32p(plan), plan.size, ctypes.byref(n), ctypes.byref(ng),
+                                ctypes.byref(mp))
+    if st == _lib.E_INVAL and n.value > plan.size:  # the bound cannot be short; kept as a guard
+        plan = np.empty(n.value, np.int32)
+        st = lib.kvattn_decode_plan(*args, _i32p(plan), plan.size, ctypes.byref(n),
+                                    ctypes.byref(ng), ctypes.byref(mp))
+    check(st, "decode_plan")
+    return plan[:n.value].copy(), int(ng.value), int(mp.value)
 
 
 def decode_partial_plan(pool, q, q_dtype, num_q_heads, scale, table_dev, max_blocks, plan_dev,

@@ -68,7 +68,9 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
 
   // per sequence and block position i of its range: the token extent [lo_i, hi_i) and the
   // key (i, block id, extent); sequences with the same key hold the same tokens in the same
-  // block.  A position with an invalid id stays private (the kernel flags it).
+  // block.  A position with an invalid id stays private (the kernel flags it).  A block id's
+  // first key is found by direct lookup; a block id seen again at another position or with
+  // another extent is looked up by its whole key.
   struct Key {
     int64_t a, b;
     bool operator==(const Key& o) const { return a == o.a && b == o.b; }
@@ -76,9 +78,9 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
   struct KeyHash {
     size_t operator()(const Key& k) const { return (size_t)mix(mix(0, (uint64_t)k.a), (uint64_t)k.b); }
   };
-  std::unordered_map<Key, int32_t, KeyHash> key_index;
-  std::vector<std::vector<int32_t>> key_members;   // ascending sequences
-  std::vector<std::vector<int32_t>> pos_key(batch);  // per sequence, per position: key or -1
+  struct KeyRec {
+    int32_t i, lo, hi;
+  };
   for (int b = 0; b < batch; ++b) {
     const int beg = tok_begin ? tok_begin[b] : 0;
     const int len = ctx_lens[b];
@@ -90,28 +92,61 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
     if (span_parts > 0 && (int64_t)span_parts * P / bs >= kPlanWindow)
       return set_error(KVATTN_E_UNSUPPORTED,
                        "decode_plan: span_parts * part_tokens spans more than 127 blocks");
+  }
+  std::vector<int64_t> pos_off(batch + 1, 0);  // positions of sequence b: [pos_off[b], pos_off[b + 1])
+  for (int b = 0; b < batch; ++b) {
+    const int beg = tok_begin ? tok_begin[b] : 0;
+    const int len = ctx_lens[b];
+    pos_off[b + 1] = pos_off[b] + (beg == len ? 0 : (len - 1) / bs - beg / bs + 1);
+  }
+  std::vector<int32_t> pos_key(pos_off[batch]);  // key of each position, or -1
+  std::vector<KeyRec> key_rec;
+  std::vector<int32_t> key_count;
+  std::vector<int32_t> first_key(pool->total_blocks, -1);
+  std::unordered_map<Key, int32_t, KeyHash> key_index;
+  for (int b = 0; b < batch; ++b) {
+    const int beg = tok_begin ? tok_begin[b] : 0;
+    const int len = ctx_lens[b];
     const int32_t* row = table + (int64_t)b * max_blocks;
+    int64_t x = pos_off[b];
     if (beg == len) continue;
-    for (int i = beg / bs; i <= (len - 1) / bs; ++i) {
+    for (int i = beg / bs; i <= (len - 1) / bs; ++i, ++x) {
       const int32_t pid = row[i];
       if (pid < 0 || pid >= pool->total_blocks) {
-        pos_key[b].push_back(-1);
+        pos_key[x] = -1;
         continue;
       }
       const int lo = std::max(beg, i * bs), hi = std::min(len, (i + 1) * bs);
-      const Key k{((int64_t)i << 32) | (uint32_t)pid, ((int64_t)lo << 32) | (uint32_t)hi};
-      auto it = key_index.find(k);
-      int32_t ki;
-      if (it == key_index.end()) {
-        ki = (int32_t)key_members.size();
-        key_index.emplace(k, ki);
-        key_members.push_back({});
-      } else {
-        ki = it->second;
+      int32_t ki = first_key[pid];
+      if (ki < 0) {
+        ki = first_key[pid] = (int32_t)key_rec.size();
+        key_rec.push_back({i, lo, hi});
+        key_count.push_back(0);
+      } else if (key_rec[ki].i != i || key_rec[ki].lo != lo || key_rec[ki].hi != hi) {
+        const Key k{((int64_t)i << 32) | (uint32_t)pid, ((int64_t)lo << 32) | (uint32_t)hi};
+        auto it = key_index.find(k);
+        if (it == key_index.end()) {
+          ki = (int32_t)key_rec.size();
+          key_index.emplace(k, ki);
+          key_rec.push_back({i, lo, hi});
+          key_count.push_back(0);
+        } else {
+          ki = it->second;
+        }
       }
-      key_members[ki].push_back(b);
-      pos_key[b].push_back(ki);
+      ++key_count[ki];
+      pos_key[x] = ki;
     }
+  }
+  // each key's sequences, ascending, in one flat array
+  std::vector<int64_t> key_off(key_count.size() + 1, 0);
+  for (size_t k = 0; k < key_count.size(); ++k) key_off[k + 1] = key_off[k] + key_count[k];
+  std::vector<int32_t> key_seqs(key_off.back());
+  {
+    std::vector<int64_t> fill(key_off.begin(), key_off.end() - 1);
+    for (int b = 0; b < batch; ++b)
+      for (int64_t x = pos_off[b]; x < pos_off[b + 1]; ++x)
+        if (pos_key[x] >= 0) key_seqs[fill[pos_key[x]]++] = b;
   }
 
   // items: maximal runs of positions of a sequence with the same sharers, taken from their
@@ -126,25 +161,37 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
     const int P = part_tokens[b];
     const int span = span_parts > 0 ? span_parts : std::max(1, (kPlanWindow - 1) / (P / bs));
     const int piece_blocks = std::min<int64_t>(kPlanWindow - 1, (int64_t)span * P / bs);
-    const std::vector<int32_t>& keys = pos_key[b];
+    const int32_t* keys = pos_key.data() + pos_off[b];
+    const size_t nkeys = (size_t)(pos_off[b + 1] - pos_off[b]);
     const int i0 = beg / bs;
-    auto sharers = [&](size_t x) -> std::vector<int32_t> {
-      if (keys[x] < 0) return {b};
-      return key_members[keys[x]];
+    const int32_t alone = b;
+    // the sharers of a position (an invalid id: its own sequence alone)
+    auto sharers = [&](size_t x, const int32_t*& p) -> size_t {
+      if (keys[x] < 0) {
+        p = &alone;
+        return 1;
+      }
+      p = key_seqs.data() + key_off[keys[x]];
+      return (size_t)key_count[keys[x]];
     };
     size_t x = 0;
-    while (x < keys.size()) {
-      const std::vector<int32_t> S = sharers(x);
+    while (x < nkeys) {
+      const int32_t* S;
+      const size_t ns = sharers(x, S);
       size_t y = x + 1;
-      while (y < keys.size() && sharers(y) == S) ++y;
+      for (; y < nkeys; ++y) {
+        const int32_t* T;
+        const size_t nt = sharers(y, T);
+        if (nt != ns || !std::equal(S, S + ns, T)) break;
+      }
       if (S[0] == b) {  // the run belongs to its lowest sequence
         for (size_t c = x; c < y; c += piece_blocks) {
           const size_t e = std::min(y, c + (size_t)piece_blocks);
           const int lo = std::max(beg, (int)(i0 + c) * bs);
           const int hi = std::min(len, (int)(i0 + e) * bs);
-          for (size_t k = 0; k < S.size(); k += mpw) {
-            Item it{b, lo, hi, S.size() > 1 ? 1 : 0, {}};
-            for (size_t u = k; u < std::min(S.size(), k + (size_t)mpw); ++u) it.members.push_back(S[u]);
+          for (size_t k = 0; k < ns; k += mpw) {
+            Item it{b, lo, hi, ns > 1 ? 1 : 0, {}};
+            it.members.assign(S + k, S + std::min(ns, k + (size_t)mpw));
             items.push_back(std::move(it));
             item_work.push_back(hi - lo);
           }
