@@ -353,7 +353,10 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  *                           first member entry, mode 0 / 1 / 2},
  *   members[M][2] = {sequence, partial slot}.
  *   table        host [batch][max_blocks] int32 (the device copy's contents)
- *   plan         host int32 [plan_cap], or NULL to query the size only
+ *   plan         host int32 [plan_cap], or NULL to query the size only.  plan_len never
+ *                exceeds 8 + batch + 26 P, P the block positions of all ranges (sequence b:
+ *                (ctx_len - 1) / bs - tok_begin / bs + 1 when ctx_len > tok_begin), so a
+ *                buffer of that size needs one call
  *   plan_len     receives the plan's length in int32 entries
  *   n_groups     receives the workgroups of the plan (the grid of kvattn_decode_partial_plan)
  *   max_parts    receives the most partials any sequence gets (size o_part / lse_part for it)
