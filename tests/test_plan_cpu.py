@@ -328,6 +328,10 @@ def test_random_pools_plan_invariants(seed):
     items, members = check_plan(plan, ng, mp, table, lens, begins, parts, bs, group,
                                 span=span if span else 128)
     check_range_modes(items, members)
+    # the header's bound on a plan's length: 8 + batch + 26 P (P: block positions)
+    live = lens > begins
+    positions = int(np.sum((lens[live] - 1) // bs - begins[live] // bs + 1))
+    assert plan.size <= 8 + len(lens) + 26 * positions
     if not (table >= pool_blocks).any():
         # every distinct (position, block id, token extent) key is read once: blocks held with
         # the same extent are read once for all their holders, and a block two sequences hold
