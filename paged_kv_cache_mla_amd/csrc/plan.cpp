@@ -102,7 +102,12 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
   std::vector<int32_t> pos_key(pos_off[batch]);  // key of each position, or -1
   std::vector<KeyRec> key_rec;
   std::vector<int32_t> key_count;
-  std::vector<int32_t> first_key(pool->total_blocks, -1);
+  // a block id's first key: an array over the pool's ids where the pool is not much larger
+  // than the plan, else a hash map (the cost then follows the plan's positions, not the pool)
+  const bool direct = (int64_t)pool->total_blocks <= 16 * pos_off[batch] + 4096;
+  std::vector<int32_t> first_key(direct ? pool->total_blocks : 0, -1);
+  std::unordered_map<int32_t, int32_t> first_key_map;
+  if (!direct) first_key_map.reserve((size_t)pos_off[batch]);
   std::unordered_map<Key, int32_t, KeyHash> key_index;
   for (int b = 0; b < batch; ++b) {
     const int beg = tok_begin ? tok_begin[b] : 0;
@@ -117,9 +122,10 @@ extern "C" kvattn_status kvattn_decode_plan(const kvattn_pool* pool, int32_t bat
         continue;
       }
       const int lo = std::max(beg, i * bs), hi = std::min(len, (i + 1) * bs);
-      int32_t ki = first_key[pid];
+      int32_t* slot = direct ? &first_key[pid] : &first_key_map.emplace(pid, -1).first->second;
+      int32_t ki = *slot;
       if (ki < 0) {
-        ki = first_key[pid] = (int32_t)key_rec.size();
+        ki = *slot = (int32_t)key_rec.size();
         key_rec.push_back({i, lo, hi});
         key_count.push_back(0);
       } else if (key_rec[ki].i != i || key_rec[ki].lo != lo || key_rec[ki].hi != hi) {

@@ -349,3 +349,18 @@ def test_random_pools_plan_invariants(seed):
                 t = np.arange(begins[b], lens[b])
                 slots.update(zip(table[b][t // bs].tolist(), (t % bs).tolist()))
             assert len(slots) <= read <= len(slots) + bs * len(lens)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_does_not_depend_on_pool_size(seed):
+    """The same tables planned over a pool just large enough and over one far larger than the
+    plan (where the planner keys block ids through a hash map rather than an array over the
+    pool) give the same plan, bit for bit."""
+    rng = np.random.default_rng(8000 + seed)
+    bs, hkv, group, table, lens, begins, parts, span, pool_blocks = _random_pool_case(rng)
+    table = np.where(table >= pool_blocks, -5, table)       # no invalid ids: both pools hold all
+    plans = []
+    for nblocks in (pool_blocks, pool_blocks + 400_000):
+        pool = Pool(bs, hkv, 64, 64, "bf16", False, [(FAKE, nblocks)])
+        plans.append(decode_plan(pool, hkv * group, table, lens, begins, parts, span_parts=span))
+    assert np.array_equal(plans[0][0], plans[1][0]) and plans[0][1:] == plans[1][1:]
