@@ -393,3 +393,80 @@ def test_random_pools_plan_matches_oracle(seed):
     live = np.asarray(lens) > np.asarray(begins)
     assert float(np.max(np.abs(lse[live] - lse_ref[live]))) <= oc.lse_tol(case)
     assert np.isneginf(lse[~live]).all() and (o[~live] == 0).all()
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(256, 16, 2), (128, 32, 4)])
+def test_shared_prefix_decode_session_with_appends(d, hq, hkv):
+    """A serving loop over a pool with a shared prefix: eight sequences take the same first
+    blocks from the pool's ref-counted block table, the prefix is written once and each
+    sequence's own tokens through the append kernel, and each step appends one token to every
+    sequence, builds a new plan (the shared ranges staged: eight sharers at eight heads per KV
+    head fill four waves) and decodes; every step matches the oracle's attention over each
+    sequence's whole history."""
+    from paged_kv_cache_mla_amd import _lib
+    from paged_kv_cache_mla_amd.api import DecodeStep, Pool, append_kv
+    from synth import bf16_round_bits
+    rng = np.random.default_rng(31 + d)
+    B, bs, S, steps = 8, 16, 40, 3                     # S shared blocks (640 tokens)
+    own = [int(x) for x in rng.integers(0, 90, B)]
+    final = [S * bs + own[b] + steps for b in range(B)]
+    max_blocks = -(-max(final) // bs)
+    nblocks = S + B * (max_blocks - S) + 4
+    nel = 2 * hkv * bs * d
+    region = torch.zeros(nblocks * nel, dtype=torch.int16, device="cuda")
+    pool = Pool(bs, hkv, d, d, "bf16", False, [(region.data_ptr(), nblocks)], seed=3)
+    st, table, _ = pool.block_table(final, max_blocks, share_src=[-1] + [0] * (B - 1),
+                                    share_nblocks=[0] + [S] * (B - 1))
+    assert st == 0 and pool.shared_blocks > 0
+    table_dev = torch.from_numpy(table).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def tokens(n):
+        k = bf16_round_bits(rng.standard_normal((n, hkv, d), dtype=np.float32))
+        v = bf16_round_bits(rng.standard_normal((n, hkv, d), dtype=np.float32))
+        return k, v
+
+    def write(b, k, v, pos):
+        kd = torch.from_numpy(k[None].view(np.int16)).cuda()
+        vd = torch.from_numpy(v[None].view(np.int16)).cuda()
+        p = torch.tensor([pos], dtype=torch.int32, device="cuda")
+        append_kv(pool, kd, vd, _lib.BF16, table_dev[b:b + 1], max_blocks, p, err)
+
+    pk, pv = tokens(S * bs)                            # the prefix, written once (by sequence 0)
+    write(0, pk, pv, 0)
+    hist = []
+    for b in range(B):
+        k, v = tokens(own[b])
+        if own[b]:
+            write(b, k, v, S * bs)
+        hist.append([np.concatenate([pk, k]), np.concatenate([pv, v])])
+    scale = 1.0 / np.sqrt(float(d))
+    for step in range(steps):
+        for b in range(B):
+            k, v = tokens(1)
+            write(b, k, v, len(hist[b][0]))
+            hist[b] = [np.concatenate([hist[b][0], k]), np.concatenate([hist[b][1], v])]
+        lens = np.array([len(h[0]) for h in hist], np.int32)
+        cur = table.copy()
+        for b in range(B):
+            cur[b, -(-int(lens[b]) // bs):] = -1
+        dstep = DecodeStep(pool, cur, lens, [bs * 4] * B, hq, d)
+        assert dstep.plan is not None
+        q = bf16_round_bits(rng.standard_normal((B, hq, d), dtype=np.float32))
+        o, lse = dstep.run(torch.from_numpy(q.view(np.int16)).cuda(), _lib.BF16, scale)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0 and int(dstep.err.item()) == 0
+        o, lse = o.cpu().numpy(), lse.cpu().numpy()
+        _, _, items, _ = parse(dstep.plan, B)
+        qf = oracle.bf16_bits_to_f64(q)
+        worst = 0.0
+        for b in range(B):
+            o_ref, lse_ref = oracle.attend(qf[b], oracle.bf16_bits_to_f64(hist[b][0]),
+                                           oracle.bf16_bits_to_f64(hist[b][1]), scale)
+            e = float(np.max(np.abs(o[b] - o_ref))) / float(np.max(np.abs(o_ref)))
+            worst = max(worst, e)
+            assert e <= oc.BF16_REL_TOL, (step, b, e)
+            assert float(np.max(np.abs(lse[b] - lse_ref))) <= oc.LSE_ABS_TOL, (step, b)
+        _say(f"[session] d={d} step {step}: modes {sorted(set(items[items[:, 3] > 0, 5].tolist()))}, "
+             f"worst {worst:.2e}")
+        assert (items[:, 5] == 2).any()
