@@ -798,15 +798,16 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void gqa_decode_plan_kernel
                       plan[5] <= a.max_parts && plan[6] == a.group && plan[7] >= 1 &&
                       plan[7] * a.group <= 16;
   if (!hdr_ok) {  // every workgroup returns here (the counters are left as they are)
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
+    if (blockIdx.x == 0 && threadIdx.x == 0) flag_error(a.err, KVATTN_ERR_BAD_SEQ);
     return;
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < a.batch; i += 64 * kWavesPerGroup)
       a.nparts[i] = min(max(np[i], 0), a.max_parts);
-  if constexpr (!CLAIM) {  // grid (n_groups, Hkv): one unit per workgroup (an empty plan: none)
-    if ((int)blockIdx.x < n_groups)
-      gqa_plan_item<D, BSL, PAIRS>(a, plan, blockIdx.x, blockIdx.y, wv, lane, lds);
+  if constexpr (!CLAIM) {  // one unit per workgroup (an empty plan: none)
+    if ((int64_t)blockIdx.x < (int64_t)n_groups * a.hkv)
+      gqa_plan_item<D, BSL, PAIRS>(a, plan, (int)blockIdx.x / a.hkv, (int)blockIdx.x % a.hkv, wv,
+                                   lane, lds);
     return;
   }
   const int units = n_groups * a.hkv;
@@ -1131,9 +1132,12 @@ template <int D, int BSL>
 static hipError_t launch_plan_db(const DecodeArgs& a, const int32_t* plan, int32_t n_groups,
                                  uint32_t* work, int cus, hipStream_t st) {
   constexpr int PAIRS = D <= 128 ? 2 : 1;
-  dim3 grid((unsigned)(n_groups > 0 ? n_groups : 1), (unsigned)a.hkv);
+  // one workgroup per unit, the KV heads of a plan workgroup next to each other: the launch
+  // then dispatches the plan's order (longest wave item first) for every head, rather than
+  // the first head's whole plan before the second's
+  const int64_t units = (int64_t)n_groups * a.hkv;
+  dim3 grid((unsigned)std::max<int64_t>(1, units), 1);
   if (work) {
-    const int64_t units = (int64_t)n_groups * a.hkv;
     const int64_t resident = (int64_t)(cus > 0 ? cus : 256) * plan_groups_per_cu<D, BSL, PAIRS>();
     grid = dim3((unsigned)std::max<int64_t>(1, std::min(units, resident)), 1);
   }

@@ -440,6 +440,8 @@ kvattn_status kvattn_decode_partial_plan(const kvattn_pool* pool, const void* q,
                      "dim 64, 128 or 256 and at most 16 query heads per KV head");
   if (n_groups > 0 && pool->total_blocks == 0)
     return set_error(KVATTN_E_INVAL, "decode_partial_plan: the pool holds no blocks");
+  if ((int64_t)n_groups * L.num_kv_heads > INT32_MAX)  // one workgroup per (group, KV head)
+    return set_error(KVATTN_E_INVAL, "decode_partial_plan: n_groups x num_kv_heads above 2^31 - 1");
   DecodeArgs a{};
   a.rt = region_table(pool);
   a.q = q;
