@@ -72,11 +72,16 @@ constexpr int mfma_max_group() { return D <= 64 ? 16 : 8; }
 // output tile, so P V is accurate to ~2^-16 relative rather than bf16's 2^-9.
 // PROBE: the same loads in the same order, with no arithmetic: the in-range 16-bit elements
 // of K and V are XOR-ed into `xs` (the gather's own bandwidth ceiling, and a checksum).
-template <int D, int BSL, int PAIRS, bool NT, bool PROBE = false, int NWIN = 2>
+// QLDS: the Q^T operand lives in LDS at byte address `qlds` (D / 32 KiB, private to the wave)
+// and is read back for every tile, instead of taking D / 8 registers for the whole range: at
+// head dim 256 the ring, the accumulators and Q together would not fit the 256 registers a
+// wave has at two waves per SIMD, and the spills cost HBM traffic.
+template <int D, int BSL, int PAIRS, bool NT, bool PROBE = false, int NWIN = 2, bool QLDS = false>
 __device__ __forceinline__ void gqa_range_mfma(const DecodeArgs& a, const int32_t* trow,
                                                const uint16_t* qrow, bool qvalid, int kvh, int lo,
                                                int hi, int lane, f32x4 (&acc)[D / 16], float& m,
-                                               float& lsum, uint32_t& xs) {
+                                               float& lsum, uint32_t& xs, uint32_t qlds = 0u) {
+  typedef __attribute__((address_space(3))) u32x4 qlw32x4;
   constexpr int BS = 1 << BSL;
   constexpr int KS = D / 32;       // k-steps of the QK product (32 dims each)
   constexpr int VT = D / 16;       // 16-dim output tiles of the PV product
@@ -95,14 +100,18 @@ __device__ __forceinline__ void gqa_range_mfma(const DecodeArgs& a, const int32_
   for (int w = 0; w < NWIN; ++w) pidw[w] = trow[min(wbase + 64 * w + lane, blk_last)];
 
   // B operand of the QK product: Q^T, lane (n, g4) holds column n, dims 8*(g4+4j) .. +7.
-  bf16x8 qop[KS];
+  bf16x8 qop[QLDS ? 1 : KS];
   if constexpr (!PROBE) {
     const uint4* q4 = reinterpret_cast<const uint4*>(qrow);
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       uint4 v = q4[g4 + 4 * j];
       if (!qvalid) v = make_uint4(0u, 0u, 0u, 0u);
-      qop[j] = as_bf16x8(v);
+      if constexpr (QLDS)
+        *reinterpret_cast<qlw32x4*>((uintptr_t)(qlds + (uint32_t)((j * 64 + lane) * 16))) =
+            u32x4{v.x, v.y, v.z, v.w};
+      else
+        qop[j] = as_bf16x8(v);
     }
   }
 
@@ -171,9 +180,19 @@ __device__ __forceinline__ void gqa_range_mfma(const DecodeArgs& a, const int32_
   // bit i of the result is set when token i of the lane is inside the range
   auto scores = [&](int slot, int rel, float* sv) -> uint32_t {
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    // an opaque copy of the address, so that the compiler cannot hoist these loop-invariant
+    // reads out of the loop and back into registers
+    uint32_t qa = qlds + (uint32_t)(lane * 16);
+    if constexpr (QLDS) asm volatile("" : "+v"(qa));
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[slot][j]), qop[j], sacc, 0, 0, 0);
+    for (int j = 0; j < KS; ++j) {
+      bf16x8 qj;
+      if constexpr (QLDS)
+        qj = as_bf16x8(*reinterpret_cast<const qlw32x4*>((uintptr_t)(qa + (uint32_t)(j * 1024))));
+      else
+        qj = qop[j];
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[slot][j]), qj, sacc, 0, 0, 0);
+    }
     const int tb = ((t_lo + rel) << 4) + 4 * g4;
     uint32_t okbits = 0;
 #pragma unroll
@@ -683,7 +702,8 @@ __global__ __launch_bounds__(64 * mfma_max_group<D>()) void gqa_probe_kernel(Dec
   if (lane == 0) atomicXor(xsum + (int64_t)b * a.hkv + kvh, (xs ^ (xs >> 16)) & 0xffffu);
 }
 
-// LDS the plan kernel reserves per workgroup: two stages of gqa_range_staged.
+// LDS the plan kernel reserves per workgroup: two stages of gqa_range_staged (a quarter of it
+// holds a ring wave's Q^T at head dim 256: D / 32 KiB).
 __host__ __device__ constexpr uint32_t plan_lds_bytes(int d) { return 2u * (2 * (d / 32) + d / 16) * 1024u; }
 
 // One wave item of a plan (kvattn_decode_plan): wave `wv` of workgroup `grp` for KV head kvh.
@@ -750,15 +770,17 @@ __device__ __forceinline__ void gqa_plan_item(const DecodeArgs& a, const int32_t
   f32x4 acc[VT];
   float mx, lsum;
   uint32_t unused = 0u;
+  // At head dim 256 a ring wave keeps Q^T in its quarter of the workgroup's LDS, which only
+  // staged workgroups use otherwise.
   if (staged)
     gqa_range_staged<D, BSL, staged_ahead<D>()>(a, trow, qrow, col, __any(col), kvh, lo, hi, wv,
                                                 lane, lds, acc, mx, lsum);
   else if (item[5] == 1)  // other waves of the workgroup read the same range: keep it in L2
-    gqa_range_mfma<D, BSL, PAIRS, false, false, kPlanWindow / 64>(a, trow, qrow, col, kvh, lo, hi,
-                                                                  lane, acc, mx, lsum, unused);
+    gqa_range_mfma<D, BSL, PAIRS, false, false, kPlanWindow / 64, D == 256>(
+        a, trow, qrow, col, kvh, lo, hi, lane, acc, mx, lsum, unused, lds + wv * (D / 32) * 1024);
   else  // one wave reads the range, once, whatever its sharers: stream it
-    gqa_range_mfma<D, BSL, PAIRS, true, false, kPlanWindow / 64>(a, trow, qrow, col, kvh, lo, hi,
-                                                                 lane, acc, mx, lsum, unused);
+    gqa_range_mfma<D, BSL, PAIRS, true, false, kPlanWindow / 64, D == 256>(
+        a, trow, qrow, col, kvh, lo, hi, lane, acc, mx, lsum, unused, lds + wv * (D / 32) * 1024);
   lsum = rows_sum(lsum);
   if (col) {
     // the member and slot are read again here rather than held in registers across the loop
