@@ -378,8 +378,9 @@ int32_t kvattn_choose_group_parts(const kvattn_pool* pool, int32_t batch, int32_
  *   plan_dev     device int32 copy of the plan (all plan_len entries); n_groups its workgroups
  *   work_dev     device uint32 [2] work counters, or NULL.  NULL: one workgroup per (plan
  *                workgroup, KV head) unit, unit u = plan workgroup u / Hkv, KV head u % Hkv,
- *                launched in that order (n_groups x Hkv at most 2^31 - 1).  Given: as many workgroups as the device holds at
- *                once, each taking the next unit from the counters when it is done, so that the
+ *                launched in that order (n_groups x Hkv at most 2^31 - 1).  Given: as many
+ *                workgroups as the device holds at once, each running units in that order and
+ *                taking the next one from the counters when it is done, so that the
  *                CUs and XCDs that finish first take more (the partials do not depend on which
  *                workgroup ran a unit: the result is the same bit for bit).  The counters must
  *                be zero before the first call (e.g. zero-filled once); every call that
