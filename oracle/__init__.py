@@ -19,13 +19,25 @@ Sources (cited by tag):
   [VAMP]           "Dynamic HBM Repartitioning for Multi-Turn MoE Serving" -- §IV-C, §V-A
                    reclaimed pages joining the free-block pool.
 
-Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
-invariants, brute force at 50 digits, a library special case; the per-partition partials
-against attention over element-wise-written dense slices; the address resolution against
-the element found at each returned offset, with planted mistakes that must fail) or, for the allocator model,
-by ``tests/test_alloc_oracle.py`` (published SplitMix64 outputs, exhaustive permutation
-counts), or, for the share policy, by ``tests/test_share_policy.py`` (brute-force minimum of
-Eq. 1's step time, balance, limits, exact cost recovery, a library line fit).  None is "parity unpinned".
+Parity pins: every function here is pinned on the CPU by
+  ``tests/test_oracle_pins.py``    attention and merge (closed forms, invariants, brute force
+                                   at 50 digits, a library special case), the layout reader
+                                   against an element-wise writer, partition ranges, the
+                                   per-partition partials against attention over dense slices,
+                                   the address resolution against the element at each returned
+                                   offset (planted mistakes must fail);
+  ``tests/test_alloc_oracle.py``   the allocator model (published SplitMix64 outputs,
+                                   exhaustive permutation counts);
+  ``tests/test_share_policy.py``   the share policy (brute-force minimum of Eq. 1's step
+                                   time, balance, limits, exact cost recovery, a line fit);
+  ``tests/test_write_oracle.py``   the token writer (a loop-based statement of the layout,
+                                   round trips through the reader, untouched elements);
+  ``tests/test_sparse_oracle.py``  block selection (sub-table and masked statements along
+                                   different routes; all blocks selected gives the dense case);
+  ``tests/test_kvstore_cpu.py``    the placement-store model (token conservation, blocks
+                                   neither lost nor duplicated, copies exactly the CPU-routed
+                                   blocks).
+None is "parity unpinned".
 """
 
 from .bf16 import bf16_bits_to_f64
