@@ -319,6 +319,44 @@ def test_staged_range_with_an_invalid_id_is_flagged():
     assert holding > 0
 
 
+def test_claiming_launch_with_more_units_than_the_device_holds():
+    """Units enough that claiming workgroups run several each: eight sequences on one table row
+    (staged ranges) and sixteen private ones, 64-token pieces at head dim 256 (ring waves keep
+    Q^T in the workgroup's LDS, which a staged unit before them used for its stages).  The
+    claiming launch equals the one-unit launch bit for bit, leaves the counters at zero, and
+    sampled sequences match the oracle."""
+    from paged_kv_cache_mla_amd.session import DeviceCase
+    bs, hkv, d, hq, L = 16, 2, 256, 16, 4096
+    rng = np.random.default_rng(1051)
+    nblk = L // bs
+    pool_blocks = 17 * nblk + 6
+    ids = rng.permutation(pool_blocks).astype(np.int32)
+    table = np.concatenate([np.tile(ids[:nblk], (8, 1)),
+                            ids[nblk:17 * nblk].reshape(16, nblk)]).astype(np.int32)
+    case = _custom_case(bs, hkv, d, hq, table, [L] * 24, [0] * 24, 64, pool_blocks, 1051)
+    fixed = DeviceCase(case, plan=True, span_parts=1)
+    claim = DeviceCase(case, plan=True, span_parts=1, claim=True)
+    units = fixed.step.n_groups * hkv
+    _say(f"[claim] {units} units")
+    assert units > 2 * 256
+    _, _, items, _ = parse(fixed.step.plan, case.batch)
+    assert (items[:, 5] == 2).any() and (items[:, 5] == 0).any()
+    o_f, l_f = (t.clone() for t in fixed.run())
+    for step in range(3):
+        o_c, l_c = claim.run()
+        torch.cuda.synchronize()
+        assert torch.equal(o_c, o_f) and torch.equal(l_c, l_f), step
+        assert (claim.step.work.cpu().numpy() == 0).all(), step
+    assert int(claim.step.err.item()) == 0 and int(fixed.step.err.item()) == 0
+    o = o_f.cpu().numpy()
+    lay = oc.layout_of(case)
+    qf = oc.q_f64(case)
+    for b in (0, 5, 8, 23):
+        k, v = oracle.gather_sequence(lay, case.regions, case.region_blocks, case.table[b], 0, L)
+        o_ref, _ = oracle.attend(qf[b], k, v, case.scale)
+        assert float(np.max(np.abs(o[b] - o_ref))) / float(np.max(np.abs(o_ref))) <= oc.out_tol(case), b
+
+
 def test_plan_with_empty_sequences_and_an_empty_batch():
     """A sequence with no tokens (tok_begin = ctx_len) gets no wave item and no partial: its
     output is zero and its lse -inf, like the oracle's; the others are unaffected.  A batch
