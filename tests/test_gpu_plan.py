@@ -132,14 +132,15 @@ def _sharing_table(rng, nseq, nblk, pool_blocks, bs):
 
 
 GEOMS = [(16, 2, 256, 16), (16, 4, 128, 32), (32, 2, 64, 2), (64, 1, 128, 16), (16, 2, 128, 6),
-         (16, 1, 64, 16), (128, 2, 128, 4), (256, 2, 256, 16)]
+         (16, 1, 64, 16), (128, 2, 128, 4), (256, 2, 256, 16), (32, 1, 256, 6), (16, 4, 256, 8)]
 
 
 @pytest.mark.parametrize("bs,hkv,d,hq", GEOMS, ids=[f"bs{g[0]}-hkv{g[1]}-d{g[2]}-hq{g[3]}" for g in GEOMS])
 def test_plan_kernel_geometries_with_ragged_sharing(bs, hkv, d, hq):
     """Sharing of random prefix lengths from two stems, ragged ends and starts (one sequence
     starts inside a block), block sizes 16 .. 256, head dims 64 / 128 / 256, 1 .. 16 query
-    heads per KV head (16 .. 1 sequences per wave item)."""
+    heads per KV head (16 .. 1 sequences per wave item; at 6 heads per KV head, 4 of the 16
+    columns carry no query, also where head dim 256 keeps Q^T in LDS)."""
     rng = np.random.default_rng(bs * 7 + d + hq)
     nseq, nblk = 9, 24
     pool_blocks = 2 * nblk + nseq * nblk + 8
